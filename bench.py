@@ -1,0 +1,224 @@
+"""Benchmark of the gated delta-rule engine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline (the JSON line's ``value``): the decode state update -- B=256
+requests of one token each, H=16 q/k heads, HV=32 value heads, dk=dv=128,
+fp16 q/k/v, raw-gate arm, a 512-slot fp32 state slab updated in place at 256
+distinct slot ids -- reported as HBM GB/s of algorithmic traffic.  A step is
+one gdr_forward call over that batch.  Consecutive steps alternate between
+two disjoint sets of 256 slot ids (each a full decode batch of the same
+workload), so a step never finds the previous step's state in the 256 MB
+Infinity Cache.
+
+Also reported: prefill tokens/s on the varlen workload (8 requests of
+512..8192 tokens, H=16, HV=32, dk=dv=128, fp16, raw-gate arm, qk L2-norm,
+fp32 initial/final states) with its roofline fraction, and the fp64 CPU
+oracle timed on the host cores on the decode step (``cpu_baseline``).
+
+Per-kernel durations come from HIP events recorded on the stream the kernels
+run on (torch's current stream), around every timed launch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+METRIC = "decode state-update HBM GB/s (% peak); prefill tokens/s at dk=dv=128"
+
+
+def _t(x):
+    import torch
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def decode_bytes(B, H, HV, dk, dv, act_bytes=2):
+    """Algorithmic bytes of one decode step: each addressed state row is read
+    and written once; q, k, v, o, gate, beta, slot ids, per-head params once."""
+    state = 2 * B * HV * dv * dk * 4
+    acts = B * (2 * H * dk + 2 * HV * dv) * act_bytes + B * HV * (act_bytes + 4) + B * 4 + 2 * HV * 4
+    return state + acts, state
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["gated_delta_rule_token_amd/csrc/gdr_decode.hip",
+                  "gated_delta_rule_token_amd/csrc/gdr_device.hpp"]
+
+
+def committed_traffic(digest):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when that summary is missing or was taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_b or m_d.group(1) != digest:
+        return None
+    return float(m_b.group(1))
+
+
+def time_calls(calls, steps, warmup):
+    """Run ``calls`` round-robin: warmup untimed, then exactly ``steps`` timed
+    launches with an event pair around each.  Returns (wall_s, mean_kernel_ms)."""
+    import torch
+    for i in range(warmup):
+        calls[i % len(calls)].run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        calls[i % len(calls)].run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return wall, kms
+
+
+def bench_decode(args):
+    import torch
+    from gated_delta_rule_token_amd import api, workloads
+    case = workloads.decode_slab()
+    B, H = case["q"].shape[0], case["q"].shape[2]
+    HV, dv, dk = case["v"].shape[2], case["v"].shape[3], case["q"].shape[3]
+    ids_a = case["slot_ids"]
+    rng = workloads.rng_for(101)
+    ids_b = rng.permutation(np.setdiff1d(np.arange(case["slab"].shape[0]), ids_a)).astype(np.int32)
+    slab = _t(case["slab"])
+    common = dict(gate=_t(case["gate"]), beta=_t(case["beta"]), a_log=_t(case["a_log"]),
+                  dt_bias=_t(case["dt_bias"]), state=slab, update_rule="gated_delta",
+                  gate_activation="qwen", beta_activation="sigmoid", algo=args.decode_algo)
+    q, k, v = _t(case["q"]), _t(case["k"]), _t(case["v"])
+    calls = [api.prepare(q, k, v, slot_ids=_t(ids), **common) for ids in (ids_a, ids_b)]
+    wall, kms = time_calls(calls, args.steps, args.warmup)
+    total_b, state_b = decode_bytes(B, H, HV, dk, dv)
+    digest = source_digest(DECODE_SOURCES)
+    traffic = committed_traffic(digest)
+    achieved = total_b / (kms * 1e-3) / 1e9
+    return case, {
+        "wall_s": wall, "kernel_ms": kms, "bytes_per_step": total_b, "state_bytes": state_b,
+        "gbs_wall": total_b * args.steps / wall / 1e9, "gbs_kernel": achieved,
+        "algo": calls[0].algo, "tokens": B, "traffic": traffic, "digest": digest,
+    }
+
+
+def bench_prefill(args):
+    import torch
+    from gated_delta_rule_token_amd import api, workloads
+    case = workloads.varlen_prefill()
+    T, H, dk = case["q"].shape
+    HV, dv = case["v"].shape[1:]
+    call = api.prepare(_t(case["q"]), _t(case["k"]), _t(case["v"]), gate=_t(case["gate"]),
+                       beta=_t(case["beta"]), a_log=_t(case["a_log"]), dt_bias=_t(case["dt_bias"]),
+                       cu_seqlens=_t(case["cu_seqlens"]), initial_state=_t(case["initial_state"]),
+                       update_rule="gated_delta", gate_activation="qwen", beta_activation="sigmoid",
+                       qk_l2_norm=1, algo=args.prefill_algo)
+    steps = max(1, args.prefill_steps)
+    wall, kms = time_calls([call], steps, max(1, args.warmup // 2))
+    flops = 7.0 * dk * dv * HV * T  # decay, two dot products, rank-1 write per row element
+    tflops = flops / (kms * 1e-3) / 1e12
+    lengths = np.diff(case["cu_seqlens"]).tolist()
+    return {
+        "workload": case["name"], "lengths": lengths, "tokens": int(T), "algo": call.algo,
+        "steps": steps, "kernel_ms": kms, "tokens_per_s": T / (kms * 1e-3),
+        "tokens_per_s_wall": T * steps / wall,
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None},
+    }
+
+
+def cpu_baseline(case, total_bytes):
+    """The fp64 oracle on the same decode step (all 256 requests x 32 heads),
+    on the host cores."""
+    import oracle
+    ids = case["slot_ids"]
+    g = dict(gate=case["gate"], beta=case["beta"], a_log=case["a_log"], dt_bias=case["dt_bias"],
+             initial_state=case["slab"][ids], update_rule="gated_delta", gate_activation="qwen",
+             beta_activation="sigmoid")
+    oracle.build()
+    cores = oracle.num_threads()
+    reps, elapsed = 0, 0.0
+    while elapsed < 10.0 and reps < 20:
+        t0 = time.perf_counter()
+        oracle.forward(case["q"], case["k"], case["v"], **g)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    return {"value": total_bytes * reps / elapsed / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d run(s) of the full decode step (256 requests x 32 heads, 1 token each), "
+                      "fp64 oracle incl. input upcast, %.1f s total" % (reps, elapsed)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--decode-algo", default="auto")
+    ap.add_argument("--prefill-algo", default="auto")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the engine has no multi-GPU path in this build "
+              "(requests and heads shard with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+
+    result = {"metric": METRIC}
+    if args.only in (None, "decode"):
+        case, d = bench_decode(args)
+        pct = d["gbs_kernel"] / HBM_PEAK_GBS
+        result.update({
+            "value": d["gbs_wall"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": d["wall_s"] * 1e3 / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": case["name"], "batch": 256, "tokens_per_request": 1,
+                       "num_heads_qk": 16, "num_heads_v": 32, "dk": 128, "dv": 128,
+                       "num_slots": 512, "activations": "f16", "state": "f32",
+                       "update_rule": "gated_delta", "gate": "qwen raw gate + sigmoid beta",
+                       "kernel": d["algo"]},
+            "decode": {"kernel_ms": d["kernel_ms"], "gbs_kernel": d["gbs_kernel"],
+                       "pct_of_8tbs": 100 * pct, "tokens_per_s": d["tokens"] / (d["kernel_ms"] * 1e-3),
+                       "bytes_per_step": d["bytes_per_step"], "state_bytes_per_step": d["state_bytes"],
+                       "kernel_source_digest": d["digest"]},
+            "roofline": {"bound": "hbm", "achieved": d["gbs_kernel"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": pct, "traffic": d["traffic"]},
+        })
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
+        del case
+    if args.only in (None, "prefill"):
+        result["prefill"] = bench_prefill(args)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,324 @@
+"""Thin ctypes binding of libgdr (include/gdr.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch (as the operator contract's
+loader infers and allocates them, "com.microsoft.GatedDeltaNet" README,
+Use section), and the call goes to ``gdr_forward`` on torch's current
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback, and a missing library raises ``GDRError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdr.so")
+_lock = threading.Lock()
+_lib = None
+
+GDR_OK, GDR_E_INVALID, GDR_E_UNSUPPORTED, GDR_E_ALIAS, GDR_E_WORKSPACE, GDR_E_HIP = range(6)
+F32, F16 = 0, 1
+RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3, "gated_delta_v2": 4}
+GATES = {"none": 0, "qwen": 1}
+BETAS = {"none": 0, "sigmoid": 1}
+ALGOS = {"auto": 0, "recurrent": 1, "decode": 2, "chunked": 3}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+
+
+class GDRError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (status, message))
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("num_heads_qk", ctypes.c_int32),
+        ("num_heads_v", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("gate_dtype", ctypes.c_int32),
+        ("update_rule", ctypes.c_int32),
+        ("gate_activation", ctypes.c_int32),
+        ("beta_activation", ctypes.c_int32),
+        ("qk_l2_norm", ctypes.c_int32),
+        ("decay_per_key", ctypes.c_int32),
+        ("rank4", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
+        ("state_update_capacity", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class Tensors(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "q", "k", "v", "o", "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens",
+        "slot_ids", "initial_state", "final_state")]
+
+
+EXPORTS = ("gdr_abi_version", "gdr_status_str", "gdr_last_error", "gdr_validate",
+           "gdr_workspace_size", "gdr_select_algo", "gdr_forward", "gdr_gate")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Open libgdr.so (once).  Raises GDRError when it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise GDRError("GDR_E_HIP", "libgdr.so is not built (python -m gated_delta_rule_token_amd.build)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.gdr_abi_version.restype = ctypes.c_int
+        lib.gdr_status_str.restype = ctypes.c_char_p
+        lib.gdr_status_str.argtypes = [ctypes.c_int]
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_validate.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Tensors)]
+        lib.gdr_validate.restype = ctypes.c_int
+        lib.gdr_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gdr_workspace_size.restype = ctypes.c_int
+        lib.gdr_select_algo.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int32)]
+        lib.gdr_select_algo.restype = ctypes.c_int
+        lib.gdr_forward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Tensors), ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+        lib.gdr_forward.restype = ctypes.c_int
+        lib.gdr_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+        lib.gdr_gate.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def check(status: int):
+    if status != GDR_OK:
+        lib = load_library()
+        raise GDRError(lib.gdr_status_str(status).decode(), lib.gdr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return F32
+    if dt == torch.float16:
+        return F16
+    raise GDRError("GDR_E_INVALID", "unsupported dtype %s (float32 or float16)" % dt)
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise GDRError("GDR_E_INVALID", "%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise GDRError("GDR_E_INVALID", "%s must be on the GPU" % name)
+    if device is not None and t.device != device:
+        raise GDRError("GDR_E_INVALID", "%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise GDRError("GDR_E_INVALID", "%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise GDRError("GDR_E_INVALID", "%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
+                  cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
+                  update_rule="gated_delta", gate_activation="none", beta_activation="none",
+                  qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", batch=None):
+    """Problem descriptor from tensor shapes (no device access)."""
+    rank4 = q.dim() == 4
+    if rank4:
+        B, L, H, dk = q.shape
+        T = B * L
+    else:
+        T, H, dk = q.shape
+        if cu_seqlens is not None:
+            B, L = cu_seqlens.shape[0] - 1, 0
+        else:
+            if batch is None:
+                if initial_state is not None:
+                    batch = initial_state.shape[0]
+                elif slot_ids is not None:
+                    batch = slot_ids.shape[0]
+                else:
+                    batch = 1
+            B = int(batch)
+            L = T // B if B else 0
+    HV, dv = v.shape[-2], v.shape[-1]
+    per_key = gate is not None and gate.dim() == q.dim()
+    p = Problem(
+        total_tokens=T, batch=B, seq_len=L, num_heads_qk=H, num_heads_v=HV, head_dim_k=dk,
+        head_dim_v=dv, num_slots=0 if state is None else state.shape[0],
+        act_dtype=_dtype_code(q.dtype),
+        gate_dtype=F32 if gate is None else _dtype_code(gate.dtype),
+        update_rule=RULES[update_rule], gate_activation=GATES[gate_activation],
+        beta_activation=BETAS[beta_activation], qk_l2_norm=int(bool(qk_l2_norm)),
+        decay_per_key=int(per_key), rank4=int(rank4), chunk_size=int(chunk_size),
+        algo=ALGOS[algo], state_update_capacity=0, scale=float(scale))
+    return p
+
+
+def workspace_size(problem: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    check(load_library().gdr_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
+    return int(n.value)
+
+
+def selected_algo(problem: Problem) -> str:
+    a = ctypes.c_int32(0)
+    check(load_library().gdr_select_algo(ctypes.byref(problem), ctypes.byref(a)))
+    return ALGO_NAMES[a.value]
+
+
+def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
+            cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
+            update_rule="gated_delta", gate_activation="none", beta_activation="none",
+            qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", out=None,
+            final_state=None, workspace=None, batch=None):
+    """Run the gated delta rule on the GPU.
+
+    q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
+    decay, or the raw projection with gate_activation='qwen'): (...,HV) or
+    per key (...,HV,dk); beta: (...,HV) fp32; erase: (...,HV,dk) fp32.
+    With ``state`` (a slab (num_slots,HV,dv,dk) fp32) and ``slot_ids``, the
+    slab is updated in place and returned as the second result; otherwise a
+    final state (B,HV,dv,dk) is allocated (or ``final_state`` is filled).
+    Returns (o, final_state).
+    """
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    if gate is not None:
+        _need(gate, "gate", device=dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(erase, "erase", torch.float32, dev)
+    _need(a_log, "a_log", torch.float32, dev)
+    _need(dt_bias, "dt_bias", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(slot_ids, "slot_ids", torch.int32, dev)
+    _need(initial_state, "initial_state", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    if k.shape != q.shape:
+        raise GDRError("GDR_E_INVALID", "k must have q's shape")
+    if v.shape[:-2] != q.shape[:-2]:
+        raise GDRError("GDR_E_INVALID", "v must share q's leading axes")
+    p = build_problem(q, k, v, gate=gate, beta=beta, erase=erase, a_log=a_log, dt_bias=dt_bias,
+                      cu_seqlens=cu_seqlens, initial_state=initial_state, slot_ids=slot_ids,
+                      state=state, update_rule=update_rule, gate_activation=gate_activation,
+                      beta_activation=beta_activation, qk_l2_norm=qk_l2_norm, scale=scale,
+                      chunk_size=chunk_size, algo=algo, batch=batch)
+    HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
+    lead = tuple(q.shape[:-2])
+    if out is None:
+        out = torch.empty(lead + (HV, dv), dtype=q.dtype, device=dev)
+    else:
+        _need(out, "out", q.dtype, dev)
+    if state is not None:
+        fin = state
+    elif final_state is not None:
+        fin = _need(final_state, "final_state", torch.float32, dev)
+    else:
+        fin = torch.empty((p.batch, HV, dv, dk), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(p)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(gate), beta=_ptr(beta),
+                erase=_ptr(erase), a_log=_ptr(a_log), dt_bias=_ptr(dt_bias),
+                cu_seqlens=_ptr(cu_seqlens), slot_ids=_ptr(slot_ids),
+                initial_state=_ptr(initial_state), final_state=_ptr(fin))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    check(lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), _ptr(workspace),
+                          ws_bytes if workspace is not None else 0, stream))
+    return out, fin
+
+
+def gate(a, dt_bias, decay_scale, b=None, want_beta=False, out_decay=None, out_beta=None):
+    """Standalone gate fusion ("com.microsoft.LinearAttentionGate"):
+    decay = decay_scale * softplus(a + dt_bias), beta = sigmoid(b) if wanted.
+    The last axis of ``a`` is the head axis.  Returns (decay, beta-or-None)."""
+    lib = load_library()
+    dev = a.device
+    _need(a, "a", device=dev)
+    _need(dt_bias, "dt_bias", torch.float32, dev)
+    _need(decay_scale, "decay_scale", torch.float32, dev)
+    if b is not None:
+        _need(b, "b", a.dtype, dev)
+    heads = a.shape[-1]
+    decay = out_decay if out_decay is not None else torch.empty_like(a)
+    beta = None
+    if want_beta:
+        beta = out_beta if out_beta is not None else torch.empty_like(a)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    check(lib.gdr_gate(a.numel(), heads, _dtype_code(a.dtype), _ptr(a), _ptr(dt_bias),
+                       _ptr(decay_scale), _ptr(b), _ptr(decay), _ptr(beta), stream))
+    return decay, beta
+
+
+class Prepared:
+    """A gdr_forward call with its argument structs built once (for timing
+    loops and replay): ``run()`` only re-issues the C call on the current
+    stream.  Holds references to every tensor it points at."""
+
+    def __init__(self, q, k, v, **kw):
+        lib = load_library()
+        self._lib = lib
+        self.o, self.final_state = None, None
+        dev = q.device
+        p = build_problem(q, k, v, **{key: kw.get(key) for key in (
+            "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens", "initial_state",
+            "slot_ids", "state")}, **{key: kw[key] for key in (
+                "update_rule", "gate_activation", "beta_activation", "qk_l2_norm", "scale",
+                "chunk_size", "algo", "batch") if key in kw})
+        HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
+        out = kw.get("out")
+        if out is None:
+            out = torch.empty(tuple(q.shape[:-2]) + (HV, dv), dtype=q.dtype, device=dev)
+        fin = kw.get("state")
+        if fin is None:
+            fin = kw.get("final_state")
+        if fin is None:
+            fin = torch.empty((p.batch, HV, dv, dk), dtype=torch.float32, device=dev)
+        ws = workspace_size(p)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        self.tensors = dict(kw, q=q, k=k, v=v, out=out, fin=fin)
+        g = kw.get
+        self.t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(g("gate")),
+                         beta=_ptr(g("beta")), erase=_ptr(g("erase")), a_log=_ptr(g("a_log")),
+                         dt_bias=_ptr(g("dt_bias")), cu_seqlens=_ptr(g("cu_seqlens")),
+                         slot_ids=_ptr(g("slot_ids")), initial_state=_ptr(g("initial_state")),
+                         final_state=_ptr(fin))
+        self.p = p
+        self.ws_bytes = ws
+        self.algo = selected_algo(p)
+        self.o, self.final_state = out, fin
+        check(lib.gdr_validate(ctypes.byref(self.p), ctypes.byref(self.t)))
+
+    def run(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.o.device).cuda_stream
+        check(self._lib.gdr_forward(ctypes.byref(self.p), ctypes.byref(self.t),
+                                    _ptr(self.workspace), self.ws_bytes, stream))
+        return self.o, self.final_state
+
+
+def prepare(q, k, v, **kw) -> Prepared:
+    return Prepared(q, k, v, **kw)

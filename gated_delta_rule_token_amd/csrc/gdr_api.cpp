@@ -1,0 +1,299 @@
+// gdr_api.cpp -- the C ABI of libgdr (declared in include/gdr.h): host-side
+// argument validation, kernel selection and launch.  Nothing here touches
+// tensor memory; cu_seqlens and slot_ids stay on the device.
+#include "gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdr_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dsize(int32_t dt) { return dt == GDR_F16 ? 2 : 4; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Number of state rows (batch or slab) the final_state buffer holds.
+int64_t state_rows(const gdr_problem *p) { return p->num_slots > 0 ? p->num_slots : p->batch; }
+
+gdr_status check_problem(const gdr_problem *p)
+{
+    if (!p) return fail(GDR_E_INVALID, "problem is NULL");
+    if (p->state_update_capacity != 0)
+        return fail(GDR_E_UNSUPPORTED, "state_update_capacity must be 0 (compact capture is not implemented)");
+    if (p->act_dtype != GDR_F32 && p->act_dtype != GDR_F16)
+        return fail(GDR_E_INVALID, "act_dtype must be GDR_F32 or GDR_F16");
+    if (p->gate_dtype != GDR_F32 && p->gate_dtype != p->act_dtype)
+        return fail(GDR_E_INVALID, "gate_dtype must be GDR_F32 or the activation dtype");
+    if (p->update_rule < GDR_RULE_LINEAR || p->update_rule > GDR_RULE_GATED_DELTA_V2)
+        return fail(GDR_E_INVALID, "update_rule %d out of range", p->update_rule);
+    if (p->gate_activation != GDR_GATE_NONE && p->gate_activation != GDR_GATE_QWEN)
+        return fail(GDR_E_INVALID, "gate_activation %d out of range", p->gate_activation);
+    if (p->beta_activation != GDR_BETA_NONE && p->beta_activation != GDR_BETA_SIGMOID)
+        return fail(GDR_E_INVALID, "beta_activation %d out of range", p->beta_activation);
+    if (p->algo < GDR_ALGO_AUTO || p->algo > GDR_ALGO_CHUNKED)
+        return fail(GDR_E_INVALID, "algo %d out of range", p->algo);
+    if (p->num_heads_qk < 1 || p->num_heads_v < 1 || p->num_heads_v % p->num_heads_qk != 0)
+        return fail(GDR_E_INVALID, "num_heads_v (%d) must be a positive multiple of num_heads_qk (%d)",
+                    p->num_heads_v, p->num_heads_qk);
+    if (p->head_dim_k < 1 || p->head_dim_k > 256 || p->head_dim_v < 1 || p->head_dim_v > 256)
+        return fail(GDR_E_INVALID, "head dims must lie in [1, 256] (dk=%d, dv=%d)", p->head_dim_k, p->head_dim_v);
+    if (p->total_tokens < 0 || p->batch < 0 || p->seq_len < 0 || p->num_slots < 0 || p->chunk_size < 0)
+        return fail(GDR_E_INVALID, "negative size");
+    if (p->total_tokens > INT32_MAX) return fail(GDR_E_INVALID, "total_tokens above 2^31-1");
+    const bool decays = gdr::rule_decays(p->update_rule);
+    if (p->gate_activation == GDR_GATE_QWEN && !decays)
+        return fail(GDR_E_INVALID, "gate_activation qwen needs a decayed update_rule");
+    if (p->decay_per_key && !decays) return fail(GDR_E_INVALID, "decay_per_key needs a decayed update_rule");
+    if (p->decay_per_key && (p->gate_activation != GDR_GATE_NONE || p->gate_dtype != GDR_F32))
+        return fail(GDR_E_UNSUPPORTED, "a per-key decay must be an fp32 log decay (no gate activation)");
+    if (!std::isfinite(p->scale)) return fail(GDR_E_INVALID, "scale is not finite");
+    const int64_t blocks = (int64_t)p->batch * p->num_heads_v * 16;
+    if (blocks > INT32_MAX) return fail(GDR_E_INVALID, "batch * num_heads_v too large");
+    if (p->algo == GDR_ALGO_DECODE && (p->head_dim_k != 128 || p->head_dim_v != 128))
+        return fail(GDR_E_UNSUPPORTED, "the decode kernel needs dk = dv = 128");
+    if (p->algo == GDR_ALGO_CHUNKED)
+        return fail(GDR_E_UNSUPPORTED, "the chunked kernel is not built in this library version");
+    return GDR_OK;
+}
+
+gdr_status check_tensors(const gdr_problem *p, const gdr_tensors *t)
+{
+    const int rule = p->update_rule;
+    const bool decays = gdr::rule_decays(rule);
+    const bool has_beta = gdr::rule_has_beta(rule);
+    const bool v2 = rule == GDR_RULE_GATED_DELTA_V2;
+    const bool qwen = p->gate_activation == GDR_GATE_QWEN;
+    const int64_t T = p->total_tokens;
+
+    if (p->rank4 && t->cu_seqlens) return fail(GDR_E_INVALID, "cu_seqlens requires the rank-3 spelling");
+    if (!t->cu_seqlens) {
+        if ((int64_t)p->batch * p->seq_len != T)
+            return fail(GDR_E_INVALID, "uniform packing needs total_tokens == batch * seq_len (%lld != %d * %d)",
+                        (long long)T, p->batch, p->seq_len);
+    }
+    // Token-indexed inputs may be NULL when there are no tokens (a zero-size
+    // tensor has no storage); otherwise presence follows the update rule.
+    if (t->gate && !decays) return fail(GDR_E_INVALID, "gate given to an update_rule without decay");
+    if (t->beta && !has_beta) return fail(GDR_E_INVALID, "beta given to an update_rule without it");
+    if (t->erase && !v2) return fail(GDR_E_INVALID, "erase given to an update_rule without it");
+    if (T > 0 && decays && !t->gate) return fail(GDR_E_INVALID, "gate is required by this update_rule");
+    if (T > 0 && has_beta && !t->beta) return fail(GDR_E_INVALID, "beta is required by this update_rule");
+    if (T > 0 && v2 && !t->erase) return fail(GDR_E_INVALID, "erase is required by gated_delta_v2");
+    if ((t->a_log != nullptr) != (t->dt_bias != nullptr))
+        return fail(GDR_E_INVALID, "a_log and dt_bias must be given together");
+    if ((t->a_log != nullptr) != qwen)
+        return fail(GDR_E_INVALID, qwen ? "gate_activation qwen requires a_log and dt_bias" : "a_log/dt_bias given without gate_activation qwen");
+    if ((p->num_slots > 0) != (t->slot_ids != nullptr))
+        return fail(GDR_E_INVALID, "slot_ids must be given exactly when num_slots > 0");
+    if (p->num_slots > 0 && t->initial_state)
+        return fail(GDR_E_INVALID, "with a slot slab the state is read in place; initial_state must be NULL");
+    if (!t->final_state && state_rows(p) > 0) return fail(GDR_E_INVALID, "final_state (or the slab) is required");
+    if (T > 0 && (!t->q || !t->k || !t->v || !t->o)) return fail(GDR_E_INVALID, "q, k, v and o are required");
+    if (p->batch > 0 && !t->cu_seqlens && p->seq_len == 0 && T != 0)
+        return fail(GDR_E_INVALID, "seq_len must be set without cu_seqlens");
+
+    const void *ptrs[] = {t->q, t->k, t->v, t->o, t->gate, t->beta, t->erase, t->a_log, t->dt_bias,
+                          t->cu_seqlens, t->slot_ids, t->initial_state, t->final_state};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(GDR_E_INVALID, "every tensor pointer must be 16-byte aligned");
+
+    // aliasing: outputs must not overlap inputs or each other; final == initial is the in-place case
+    const int64_t H = p->num_heads_qk, HV = p->num_heads_v, dk = p->head_dim_k, dv = p->head_dim_v;
+    const size_t a = dsize(p->act_dtype);
+    const size_t state_bytes = (size_t)state_rows(p) * HV * dv * dk * 4;
+    auto rng = [](const char *n, const void *ptr, size_t bytes) {
+        uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+        return Range{n, lo, ptr ? lo + bytes : lo};
+    };
+    const Range out_o = rng("o", t->o, (size_t)T * HV * dv * a);
+    const Range out_s = rng("final_state", t->final_state, state_bytes);
+    const Range ins[] = {
+        rng("q", t->q, (size_t)T * H * dk * a),
+        rng("k", t->k, (size_t)T * H * dk * a),
+        rng("v", t->v, (size_t)T * HV * dv * a),
+        rng("gate", t->gate, (size_t)T * HV * (p->decay_per_key ? dk : 1) * dsize(p->gate_dtype)),
+        rng("beta", t->beta, (size_t)T * HV * 4),
+        rng("erase", t->erase, (size_t)T * HV * dk * 4),
+        rng("a_log", t->a_log, (size_t)HV * 4),
+        rng("dt_bias", t->dt_bias, (size_t)HV * 4),
+        rng("cu_seqlens", t->cu_seqlens, (size_t)(p->batch + 1) * 4),
+        rng("slot_ids", t->slot_ids, (size_t)p->batch * 4),
+        rng("initial_state", t->initial_state, (size_t)p->batch * HV * dv * dk * 4),
+    };
+    if (overlaps(out_o, out_s)) return fail(GDR_E_ALIAS, "o overlaps final_state");
+    for (const Range &r : ins) {
+        if (overlaps(out_o, r)) return fail(GDR_E_ALIAS, "o overlaps %s", r.name);
+        const bool same_state = r.name[0] == 'i' && r.lo == out_s.lo && r.hi == out_s.hi;
+        if (!same_state && overlaps(out_s, r)) return fail(GDR_E_ALIAS, "final_state overlaps %s", r.name);
+    }
+    return GDR_OK;
+}
+
+int32_t pick_algo(const gdr_problem *p)
+{
+    if (p->algo != GDR_ALGO_AUTO) return p->algo;
+    const bool d128 = p->head_dim_k == 128 && p->head_dim_v == 128;
+    // tokens per request on average; decode when requests are a handful of tokens
+    const int64_t per_req = p->batch > 0 ? (p->total_tokens + p->batch - 1) / p->batch : 0;
+    if (d128 && per_req <= 8) return GDR_ALGO_DECODE;
+    return GDR_ALGO_RECURRENT;
+}
+
+int dk_tile(int dk) { return dk <= 32 ? 32 : dk <= 64 ? 64 : dk <= 128 ? 128 : 256; }
+
+// rows per workgroup = 16 * g: enough workgroups to fill the machine while
+// amortising the per-token staging over as many rows as possible
+int rows_group(const gdr_problem *p)
+{
+    if (p->head_dim_v <= 16) return 1;
+    if (p->head_dim_v <= 32) return 2;
+    return 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_str(gdr_status s)
+{
+    switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_E_INVALID: return "GDR_E_INVALID";
+    case GDR_E_UNSUPPORTED: return "GDR_E_UNSUPPORTED";
+    case GDR_E_ALIAS: return "GDR_E_ALIAS";
+    case GDR_E_WORKSPACE: return "GDR_E_WORKSPACE";
+    case GDR_E_HIP: return "GDR_E_HIP";
+    }
+    return "GDR_E_UNKNOWN";
+}
+
+const char *gdr_last_error(void) { return g_last_error.c_str(); }
+
+gdr_status gdr_validate(const gdr_problem *problem, const gdr_tensors *tensors)
+{
+    g_last_error.clear();
+    gdr_status st = check_problem(problem);
+    if (st != GDR_OK || !tensors) return st;
+    return check_tensors(problem, tensors);
+}
+
+gdr_status gdr_workspace_size(const gdr_problem *problem, size_t *bytes)
+{
+    g_last_error.clear();
+    if (!bytes) return fail(GDR_E_INVALID, "bytes is NULL");
+    gdr_status st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    *bytes = 0;
+    return GDR_OK;
+}
+
+gdr_status gdr_select_algo(const gdr_problem *problem, int32_t *algo)
+{
+    g_last_error.clear();
+    if (!algo) return fail(GDR_E_INVALID, "algo is NULL");
+    gdr_status st = check_problem(problem);
+    if (st != GDR_OK) return st;
+    *algo = pick_algo(problem);
+    return GDR_OK;
+}
+
+gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    if (!tensors) return fail(GDR_E_INVALID, "tensors is NULL");
+    gdr_status st = gdr_validate(problem, tensors);
+    if (st != GDR_OK) return st;
+    size_t need = 0;
+    gdr_workspace_size(problem, &need);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDR_E_WORKSPACE, "workspace of %zu bytes required", need);
+    (void)workspace;
+
+    const gdr_problem &p = *problem;
+    const gdr_tensors &t = *tensors;
+    gdr::Params k{};
+    k.q = t.q;
+    k.k = t.k;
+    k.v = t.v;
+    k.o = t.o;
+    k.gate = t.gate;
+    k.beta = t.beta;
+    k.erase = t.erase;
+    k.a_log = t.a_log;
+    k.dt_bias = t.dt_bias;
+    k.cu_seqlens = t.cu_seqlens;
+    k.slot_ids = t.slot_ids;
+    k.init = t.initial_state;
+    k.state = t.final_state;
+    k.T = p.total_tokens;
+    k.B = p.batch;
+    k.L = t.cu_seqlens ? 0 : p.seq_len;
+    k.H = p.num_heads_qk;
+    k.HV = p.num_heads_v;
+    k.dk = p.head_dim_k;
+    k.dv = p.head_dim_v;
+    k.num_slots = p.num_slots;
+    k.gate_qwen = p.gate_activation == GDR_GATE_QWEN;
+    k.gate_f16 = p.gate_dtype == GDR_F16;
+    k.beta_sigmoid = p.beta_activation == GDR_BETA_SIGMOID;
+    k.qk_l2_norm = p.qk_l2_norm != 0;
+    k.scale = p.scale != 0.f ? p.scale : 1.f / std::sqrt((float)p.head_dim_k);
+    if (p.batch == 0) return GDR_OK;
+
+    const bool f16 = p.act_dtype == GDR_F16;
+    const bool pk = p.decay_per_key != 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    switch (pick_algo(problem)) {
+    case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, f16, s); break;
+    default: err = gdr::launch_recurrent(k, p.update_rule, pk, f16, dk_tile(p.head_dim_k), rows_group(problem), s); break;
+    }
+    if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
+gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a, const float *dt_bias,
+                    const float *decay_scale, const void *b, void *decay, void *beta, void *stream)
+{
+    g_last_error.clear();
+    if (count < 0 || heads < 1) return fail(GDR_E_INVALID, "count must be >= 0 and heads >= 1");
+    if (count % heads != 0) return fail(GDR_E_INVALID, "count must be a multiple of heads (last axis)");
+    if (dtype != GDR_F32 && dtype != GDR_F16) return fail(GDR_E_INVALID, "dtype must be GDR_F32 or GDR_F16");
+    if (count > 0 && (!a || !dt_bias || !decay_scale || !decay)) return fail(GDR_E_INVALID, "a, dt_bias, decay_scale and decay are required");
+    if (beta && !b) return fail(GDR_E_INVALID, "beta requested without b");
+    hipError_t err = gdr::launch_gate(count, heads, dtype == GDR_F16, a, dt_bias, decay_scale, beta ? b : nullptr,
+                                      decay, beta, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
+}  // extern "C"

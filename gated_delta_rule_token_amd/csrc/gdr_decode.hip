@@ -1,0 +1,196 @@
+// gdr_decode.hip -- decode kernel for dk = dv = 128: one workgroup streams the
+// whole 64 KiB state of one (request, value head) through registers.
+//
+// Decode is HBM-bound: each addressed state byte is read once and written
+// once per call (in place for a slot slab, CLIKA "gatedDeltaUpdate"), and all
+// other traffic is a few hundred bytes per (request, head).  So the kernel
+// is built around the state stream:
+//   * 256 threads = 4 waves; wave w owns rows [32w, 32w+32); 16 lanes hold a
+//     row (key columns l16*4 .. +3 and 64 + l16*4 .. +3), 4 rows per
+//     wave-instruction, 8 row groups per wave.  Every state access is a
+//     16-byte vector; one wave-instruction covers 4 rows x 256 contiguous
+//     bytes.
+//   * All 16 row-group loads of a lane (64 fp32 values, 16 KiB per wave) are
+//     issued before the first one is used, so each wave keeps 16 KiB of reads
+//     in flight.
+//   * The per-token prologue (q/k L2 norms, q.k, raw-gate decay, sigmoid
+//     update rate, per-key decay vectors) is computed in fp32 registers by
+//     every wave for its own use; nothing goes through memory.
+// Tokens of the request (normally one) are applied in order with the state
+// resident in registers; the recurrence and rule terms are those of the
+// "com.microsoft.GatedDeltaNet" README (Description, Attributes).
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <typename TA, int RULE, bool PK>
+__global__ __launch_bounds__(256) void k_decode128(const Params p)
+{
+    constexpr int DK = 128, C = 8, G = 8;
+    constexpr bool VD = PK || RULE == GATED_DELTA_V2;
+    constexpr bool DEC = rule_decays(RULE);
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr bool BETA = rule_has_beta(RULE);
+
+    const int HV = p.HV, H = p.H;
+    const int h = blockIdx.x % HV, b = blockIdx.x / HV;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, r4 = lane >> 4;
+    const int qh = (int)(((int64_t)h * H) / HV);
+
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, b, h, src, dst)) return;
+    int64_t s, e;
+    request_range(p, b, s, e);
+
+    // lane's first element within row group g: row (32*wave + 4*g + r4), column l16*4
+    const size_t lane_off = (size_t)(wave * 32 + r4) * DK + l16 * 4;
+    f4 S[G][2];
+    if (src) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const f4 *rp = reinterpret_cast<const f4 *>(src + lane_off + (size_t)g * 4 * DK);
+            S[g][0] = rp[0];
+            S[g][1] = rp[16];
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) S[g][0] = S[g][1] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const TA *__restrict__ q = static_cast<const TA *>(p.q);
+    const TA *__restrict__ k = static_cast<const TA *>(p.k);
+    const TA *__restrict__ v = static_cast<const TA *>(p.v);
+    TA *__restrict__ o = static_cast<TA *>(p.o);
+
+    for (int64_t t = s; t < e; ++t) {
+        const size_t th = (size_t)t * HV + h;
+        float qv[C], kv[C];
+        {
+            const TA *qp = q + ((size_t)t * H + qh) * DK + l16 * 4;
+            const TA *kp = k + ((size_t)t * H + qh) * DK + l16 * 4;
+            float lo[4], hi[4];
+            load_act<TA, 4>(qp, lo);
+            load_act<TA, 4>(qp + 64, hi);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { qv[x] = lo[x]; qv[4 + x] = hi[x]; }
+            load_act<TA, 4>(kp, lo);
+            load_act<TA, 4>(kp + 64, hi);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { kv[x] = lo[x]; kv[4 + x] = hi[x]; }
+        }
+        float vi[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) vi[g] = to_f32(v[th * DK + wave * 32 + g * 4 + r4]);
+
+        float qss = 0.f, kss = 0.f, qk = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            qss = fmaf(qv[c], qv[c], qss);
+            kss = fmaf(kv[c], kv[c], kss);
+            qk = fmaf(qv[c], kv[c], qk);
+        }
+        qk = sum16(qk);
+        float inq = 1.f, ink = 1.f;
+        if (p.qk_l2_norm) {
+            inq = 1.f / sqrtf(sum16(qss) + 1e-12f);
+            ink = 1.f / sqrtf(sum16(kss) + 1e-12f);
+        }
+        qk *= inq * ink;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            qv[c] *= inq;
+            kv[c] *= ink;
+        }
+
+        float a = 1.f, bb = 1.f;
+        if constexpr (DEC && !VD) a = expf(log_decay(p, th, h));
+        if constexpr (BETA) bb = update_rate(p, th);
+        float av[C], kb[C];
+        if constexpr (VD) {
+            float sa = 0.f;
+            if constexpr (!PK) sa = log_decay(p, th, h);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int col = (c < 4 ? 0 : 64) + l16 * 4 + (c & 3);
+                const float g = PK ? static_cast<const float *>(p.gate)[th * DK + col] : sa;
+                av[c] = expf(g);
+                float er = 1.f;
+                if constexpr (RULE == GATED_DELTA_V2) er = p.erase[th * DK + col];
+                kb[c] = er * av[c] * kv[c];
+                qv[c] *= av[c];
+            }
+        }
+
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float sv[C];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { sv[x] = S[g][0][x]; sv[4 + x] = S[g][1][x]; }
+            float r = 0.f, u = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if constexpr (RET) r = fmaf(sv[c], VD ? kb[c] : kv[c], r);
+                u = fmaf(sv[c], qv[c], u);
+            }
+            if constexpr (RET) r = sum16(r);
+            u = sum16(u);
+            if constexpr (DEC && !VD) {
+                r *= a;
+                u *= a;
+            }
+            float cc;
+            if constexpr (RULE == GATED_DELTA_V2) cc = vi[g] - r;
+            else if constexpr (BETA) cc = bb * (vi[g] - r);
+            else cc = vi[g];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if constexpr (VD) sv[c] = fmaf(av[c], sv[c], cc * kv[c]);
+                else if constexpr (DEC) sv[c] = fmaf(a, sv[c], cc * kv[c]);
+                else sv[c] = fmaf(cc, kv[c], sv[c]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { S[g][0][x] = sv[x]; S[g][1][x] = sv[4 + x]; }
+            if (l16 == 0) o[th * DK + wave * 32 + g * 4 + r4] = from_f32<TA>(p.scale * (u + qk * cc));
+        }
+    }
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        f4 *rp = reinterpret_cast<f4 *>(dst + lane_off + (size_t)g * 4 * DK);
+        rp[0] = S[g][0];
+        rp[16] = S[g][1];
+    }
+}
+
+template <typename TA, int RULE, bool PK>
+static hipError_t launch_one(const Params &p, hipStream_t stream)
+{
+    const int64_t blocks = (int64_t)p.B * p.HV;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_decode128<TA, RULE, PK>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t by_rule(const Params &p, int rule, bool pk, hipStream_t s)
+{
+    switch (rule) {
+    case LINEAR: return launch_one<TA, LINEAR, false>(p, s);
+    case DELTA: return launch_one<TA, DELTA, false>(p, s);
+    case GATED: return pk ? launch_one<TA, GATED, true>(p, s) : launch_one<TA, GATED, false>(p, s);
+    case GATED_DELTA: return pk ? launch_one<TA, GATED_DELTA, true>(p, s) : launch_one<TA, GATED_DELTA, false>(p, s);
+    default: return pk ? launch_one<TA, GATED_DELTA_V2, true>(p, s) : launch_one<TA, GATED_DELTA_V2, false>(p, s);
+    }
+}
+
+hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s)
+{
+    return f16 ? by_rule<half_t>(p, rule, per_key, s) : by_rule<float>(p, rule, per_key, s);
+}
+
+}  // namespace gdr

@@ -1,0 +1,156 @@
+// gdr_device.hpp -- device-side building blocks shared by the gated delta-rule
+// kernels (gfx950 / CDNA4, wave64).
+//
+// The recurrence (the "com.microsoft.GatedDeltaNet" README, Description) is
+// evaluated per V-major state row i (a dk-vector S_i).  Because
+//   S_i' = alpha (.) S_i + c_i k,    c_i = beta (v_i - (alpha (.) S_i) . k)
+// the new row and the read-out o_i = scale S_i' . q both follow from two dot
+// products of the OLD row with per-token vectors:
+//   r_i = S_i . (alpha (.) k),  u_i = S_i . (alpha (.) q),
+//   o_i = scale (u_i + (q . k) c_i)
+// so every kernel reads a row once, reduces two partial sums across the 16
+// lanes that hold the row, and writes it once.  (For a per-head scalar decay
+// alpha is factored out of the dot products.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+enum Rule : int { LINEAR = 0, GATED = 1, DELTA = 2, GATED_DELTA = 3, GATED_DELTA_V2 = 4 };
+
+__host__ __device__ constexpr bool rule_decays(int r) { return r == GATED || r == GATED_DELTA || r == GATED_DELTA_V2; }
+__host__ __device__ constexpr bool rule_has_beta(int r) { return r == DELTA || r == GATED_DELTA; }
+__host__ __device__ constexpr bool rule_retrieves(int r) { return r == DELTA || r == GATED_DELTA || r == GATED_DELTA_V2; }
+
+// Kernel argument block, passed by value.
+struct Params {
+    const void *q, *k, *v;
+    void *o;
+    const void *gate;
+    const float *beta, *erase, *a_log, *dt_bias;
+    const int32_t *cu_seqlens, *slot_ids;
+    const float *init;      // incoming states (B,HV,dv,dk) or nullptr (zeros); unused with slots
+    float *state;           // outgoing states, or the slab updated in place
+    int64_t T;
+    int32_t B, L, H, HV, dk, dv, num_slots;
+    int32_t gate_qwen, gate_f16, beta_sigmoid, qk_l2_norm;
+    float scale;
+};
+
+typedef _Float16 half_t;
+
+template <typename TA> __device__ __forceinline__ float to_f32(TA x) { return static_cast<float>(x); }
+template <typename TA> __device__ __forceinline__ TA from_f32(float x) { return static_cast<TA>(x); }
+
+// ---------------------------------------------------------------- lane reductions
+// DPP moves within a 16-lane row.  Every step adds a bitwise-identical pair in
+// both partner lanes (fp addition commutes), so after the four steps all 16
+// lanes hold the same sum, which keeps redundant per-row work consistent.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float sum16(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+    x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+    x += dpp_mov<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
+    return x;
+}
+
+// ---------------------------------------------------------------- gate math (fp32)
+// softplus(x) = log(1 + e^x), evaluated without overflow on either side.
+__device__ __forceinline__ float softplus_f32(float x)
+{
+    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf(-x)); }
+
+// Log decay g for token t, head h (scalar gate): README Attributes
+// gate_activation; the raw-gate arm reads the projection in fp16 or fp32.
+__device__ __forceinline__ float log_decay(const Params &p, size_t idx, int h)
+{
+    float x = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[idx])
+                         : static_cast<const float *>(p.gate)[idx];
+    if (p.gate_qwen) x = -expf(p.a_log[h]) * softplus_f32(x + p.dt_bias[h]);
+    return x;
+}
+
+__device__ __forceinline__ float update_rate(const Params &p, size_t idx)
+{
+    float b = p.beta[idx];
+    return p.beta_sigmoid ? sigmoid_f32(b) : b;
+}
+
+// ---------------------------------------------------------------- addressing
+// Request b's token range: README Inputs cu_seqlens (clamped to [0,T]; a
+// decreasing entry gives an empty request) or uniform packing.
+__device__ __forceinline__ void request_range(const Params &p, int b, int64_t &s, int64_t &e)
+{
+    if (p.cu_seqlens) {
+        int64_t a = p.cu_seqlens[b], z = p.cu_seqlens[b + 1];
+        a = a < 0 ? 0 : (a > p.T ? p.T : a);
+        z = z < 0 ? 0 : (z > p.T ? p.T : z);
+        s = a;
+        e = z > a ? z : a;
+    } else {
+        s = (int64_t)b * p.L;
+        e = s + p.L;
+    }
+}
+
+// Base element offsets of request b / head h's incoming and outgoing state.
+// Returns false when the request is skipped (slot id out of range).
+__device__ __forceinline__ bool state_ptrs(const Params &p, int b, int h, const float *&src, float *&dst)
+{
+    const size_t head = (size_t)p.dv * p.dk;
+    if (p.num_slots > 0) {
+        const int32_t slot = p.slot_ids[b];
+        if (slot < 0 || slot >= p.num_slots) return false;
+        dst = p.state + ((size_t)slot * p.HV + h) * head;
+        src = dst;
+    } else {
+        dst = p.state + ((size_t)b * p.HV + h) * head;
+        src = p.init ? p.init + ((size_t)b * p.HV + h) * head : nullptr;
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------- vector loads
+template <typename TA, int N>
+__device__ __forceinline__ void load_act(const TA *__restrict__ ptr, float (&out)[N])
+{
+    if constexpr (sizeof(TA) == 2 && N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(ptr + i);
+            const half_t *h = reinterpret_cast<const half_t *>(&w);
+            out[i] = to_f32(h[0]); out[i + 1] = to_f32(h[1]);
+            out[i + 2] = to_f32(h[2]); out[i + 3] = to_f32(h[3]);
+        }
+    } else if constexpr (sizeof(TA) == 4 && N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 w = *reinterpret_cast<const float4 *>(ptr + i);
+            out[i] = w.x; out[i + 1] = w.y; out[i + 2] = w.z; out[i + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = to_f32(ptr[i]);
+    }
+}
+
+template <typename TA, int N>
+__device__ __forceinline__ void load_act_masked(const TA *__restrict__ ptr, int valid, float (&out)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = i < valid ? to_f32(ptr[i]) : 0.f;
+}
+
+}  // namespace gdr

@@ -1,0 +1,22 @@
+// gdr_launch.hpp -- host-side launchers of the gated delta-rule kernels
+// (internal to libgdr; the public surface is include/gdr.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdr_device.hpp"
+
+namespace gdr {
+
+// Recurrent kernel: dkt in {32, 64, 128, 256} (>= dk), g in {1, 2, 4}
+// (rows per workgroup = 16 * g).
+hipError_t launch_recurrent(const Params &p, int rule, bool per_key, bool f16, int dkt, int g, hipStream_t s);
+
+// Decode kernel, dk = dv = 128 only.
+hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s);
+
+// Standalone gate fusion.
+hipError_t launch_gate(int64_t count, int heads, bool f16, const void *a, const float *dt_bias,
+                       const float *decay_scale, const void *b, void *decay, void *beta, hipStream_t s);
+
+}  // namespace gdr

@@ -1,0 +1,173 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/gdr.h declares, and rejects invalid arguments before touching the
+GPU (gdr_validate / gdr_workspace_size / gdr_select_algo make no HIP call and
+read no tensor memory, so fake, aligned pointer values are enough here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_token_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "gdr.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.library_path()):
+        from gated_delta_rule_token_amd import build
+        build.build()
+    return api.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(api.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.gdr_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["GDR_OK", "GDR_E_INVALID", "GDR_E_UNSUPPORTED", "GDR_E_ALIAS",
+                                 "GDR_E_WORKSPACE", "GDR_E_HIP"]):
+        assert lib.gdr_status_str(code).decode() == name
+
+
+# fake device addresses: distinct, 1 MiB apart, 256-byte aligned; never dereferenced
+_BASE = 0x7F0000000000
+
+
+def _fake(i):
+    return _BASE + i * (1 << 28)
+
+
+def _good(**over):
+    T, B, H, HV, D = 16, 2, 2, 4, 32
+    p = api.Problem(total_tokens=T, batch=B, seq_len=0, num_heads_qk=H, num_heads_v=HV,
+                    head_dim_k=D, head_dim_v=D, num_slots=0, act_dtype=api.F32,
+                    gate_dtype=api.F32, update_rule=api.RULES["gated_delta"],
+                    gate_activation=api.GATES["qwen"], beta_activation=api.BETAS["sigmoid"],
+                    qk_l2_norm=1, decay_per_key=0, rank4=0, chunk_size=64, algo=0,
+                    state_update_capacity=0, scale=0.0)
+    t = api.Tensors(q=_fake(1), k=_fake(2), v=_fake(3), o=_fake(4), gate=_fake(5), beta=_fake(6),
+                    erase=None, a_log=_fake(7), dt_bias=_fake(8), cu_seqlens=_fake(9),
+                    slot_ids=None, initial_state=None, final_state=_fake(10))
+    for key, val in over.items():
+        if hasattr(p, key) and key not in ("q", "k", "v", "o"):
+            setattr(p, key, val)
+        else:
+            setattr(t, key, val)
+    return p, t
+
+
+def _validate(lib, p, t):
+    return lib.gdr_validate(ctypes.byref(p), ctypes.byref(t) if t is not None else None)
+
+
+def test_good_problem_validates(lib):
+    p, t = _good()
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+
+
+BAD = [
+    ("capacity", dict(state_update_capacity=4), api.GDR_E_UNSUPPORTED),
+    ("act_dtype", dict(act_dtype=7), api.GDR_E_INVALID),
+    ("rule", dict(update_rule=9), api.GDR_E_INVALID),
+    ("gate_act", dict(gate_activation=5), api.GDR_E_INVALID),
+    ("beta_act", dict(beta_activation=5), api.GDR_E_INVALID),
+    ("algo", dict(algo=11), api.GDR_E_INVALID),
+    ("hv_not_multiple", dict(num_heads_v=3), api.GDR_E_INVALID),
+    ("dk_too_big", dict(head_dim_k=257), api.GDR_E_INVALID),
+    ("dv_zero", dict(head_dim_v=0), api.GDR_E_INVALID),
+    ("rank4_with_cu", dict(rank4=1, seq_len=8), api.GDR_E_INVALID),
+    ("missing_gate", dict(gate=None), api.GDR_E_INVALID),
+    ("missing_beta", dict(beta=None), api.GDR_E_INVALID),
+    ("a_log_without_dt_bias", dict(dt_bias=None), api.GDR_E_INVALID),
+    ("qwen_without_params", dict(a_log=None, dt_bias=None), api.GDR_E_INVALID),
+    ("params_without_qwen", dict(gate_activation=0), api.GDR_E_INVALID),
+    ("erase_for_v1", dict(erase=_fake(11)), api.GDR_E_INVALID),
+    ("slots_without_ids", dict(num_slots=8), api.GDR_E_INVALID),
+    ("ids_without_slots", dict(slot_ids=_fake(12)), api.GDR_E_INVALID),
+    ("missing_final_state", dict(final_state=None), api.GDR_E_INVALID),
+    ("missing_q", dict(q=None), api.GDR_E_INVALID),
+    ("misaligned", dict(v=_fake(3) + 4), api.GDR_E_INVALID),
+    ("o_aliases_q", dict(o=_fake(1)), api.GDR_E_ALIAS),
+    ("state_aliases_v", dict(final_state=_fake(3) + 256), api.GDR_E_ALIAS),
+    ("per_key_qwen", dict(decay_per_key=1), api.GDR_E_UNSUPPORTED),
+    ("decode_needs_128", dict(algo=api.ALGOS["decode"]), api.GDR_E_UNSUPPORTED),
+    ("gate_dtype", dict(gate_dtype=api.F16), api.GDR_E_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,over,status", BAD, ids=[b[0] for b in BAD])
+def test_rejects(lib, name, over, status):
+    p, t = _good(**over)
+    got = _validate(lib, p, t)
+    assert got == status, (name, got, lib.gdr_last_error())
+    assert lib.gdr_last_error().decode() != ""
+
+
+def test_rule_presence_rules(lib):
+    # linear: no gate, no beta
+    p, t = _good(update_rule=api.RULES["linear"], gate_activation=0, gate=None, beta=None,
+                 a_log=None, dt_bias=None)
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+    t.beta = _fake(6)
+    assert _validate(lib, p, t) == api.GDR_E_INVALID
+    # gated_delta_v2: gate + erase, no beta
+    p, t = _good(update_rule=api.RULES["gated_delta_v2"], gate_activation=0, a_log=None,
+                 dt_bias=None, beta=None, erase=_fake(11), decay_per_key=1)
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+    t.beta = _fake(6)
+    assert _validate(lib, p, t) == api.GDR_E_INVALID
+
+
+def test_in_place_state_allowed_partial_overlap_rejected(lib):
+    p, t = _good(cu_seqlens=None, seq_len=8)
+    t.initial_state = _fake(10)
+    t.final_state = _fake(10)
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+    t.final_state = _fake(10) + 1024
+    assert _validate(lib, p, t) == api.GDR_E_ALIAS
+
+
+def test_uniform_packing_needs_consistent_sizes(lib):
+    p, t = _good(cu_seqlens=None, seq_len=7)
+    assert _validate(lib, p, t) == api.GDR_E_INVALID
+    p.seq_len = 8
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+
+
+def test_slab_forbids_initial_state(lib):
+    p, t = _good(num_slots=16, slot_ids=_fake(12))
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+    t.initial_state = _fake(13)
+    assert _validate(lib, p, t) == api.GDR_E_INVALID
+
+
+def test_workspace_and_algo_selection(lib):
+    p, _ = _good()
+    n = ctypes.c_size_t(99)
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
+    assert n.value == 0
+    assert api.selected_algo(p) == "recurrent"
+    p.head_dim_k = p.head_dim_v = 128
+    p.total_tokens, p.batch = 256, 256
+    assert api.selected_algo(p) == "decode"
+
+
+def test_gate_argument_checks(lib):
+    assert lib.gdr_gate(10, 3, 0, _fake(1), _fake(2), _fake(3), None, _fake(4), None, None) \
+        == api.GDR_E_INVALID  # 10 not a multiple of 3 heads
+    assert lib.gdr_gate(12, 3, 0, _fake(1), _fake(2), _fake(3), None, _fake(4), _fake(5), None) \
+        == api.GDR_E_INVALID  # beta without b
+    assert lib.gdr_gate(12, 3, 9, _fake(1), _fake(2), _fake(3), None, _fake(4), None, None) \
+        == api.GDR_E_INVALID  # bad dtype

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64
+oracle on the same seeded inputs.  Bar: max |gpu - ref| / max |ref| per
+output tensor <= 1e-4 for fp32 activations on the recurrent kernels, 2e-3
+for fp16 activations; addressing (slot ids, cu_seqlens, empty requests,
+state hand-off) bit-exact between equivalent GPU calls."""
+import zlib
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_token_amd import workloads
+from tests.gpu_helpers import (TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
+                               sub_case, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_token_amd import api
+    api.load_library()
+
+
+def _tol(case):
+    return TOL_F32 if case["act_dtype"] == "f32" else TOL_F16
+
+
+def _check_full(case, algo, what):
+    say("case %s algo=%s" % (case["name"], algo))
+    o, st = gpu_forward(case, algo)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, _tol(case), "%s o" % what)
+    assert_close(st, rs, _tol(case), "%s state" % what)
+    return o, st
+
+
+# ------------------------------------------------------------------ small cases
+def test_tiny_varlen_workload():
+    case = workloads.tiny_varlen()
+    o, st = _check_full(case, "recurrent", "tiny_varlen")
+    z = dict(case, initial_state=np.zeros((2, 4, 32, 32), np.float32))
+    o2, st2 = gpu_forward(z, "recurrent")
+    assert np.array_equal(o, o2) and np.array_equal(st, st2), "explicit zero state must equal absent state"
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float16], ids=["f32", "f16"])
+def test_readme_usage_shape(dtype):
+    _check_full(workloads.odd_shape(dtype=dtype), "recurrent", "odd dk=12 dv=9")
+
+
+RULES = [("linear", False), ("gated", False), ("gated", True), ("delta", False),
+         ("gated_delta", False), ("gated_delta", True), ("gated_delta_v2", False),
+         ("gated_delta_v2", True)]
+SHAPES = [("recurrent", 32, 32), ("recurrent", 128, 128), ("recurrent", 64, 48),
+          ("recurrent", 256, 100), ("decode", 128, 128)]
+
+
+@pytest.mark.parametrize("rule,per_key", RULES, ids=["%s%s" % (r, "_pk" if p else "") for r, p in RULES])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16], ids=["f32", "f16"])
+@pytest.mark.parametrize("algo,dk,dv", SHAPES, ids=["%s_%dx%d" % s for s in SHAPES])
+def test_rules_and_shapes(rule, per_key, dtype, algo, dk, dv):
+    seed = zlib.crc32(("%s/%s/%d/%d/%s" % (rule, per_key, dk, dv, algo)).encode()) % 1000
+    arms = {}
+    if rule in ("gated", "gated_delta") and not per_key and seed % 2 == 0:
+        arms["gate_activation"] = "qwen"
+    if rule in ("delta", "gated_delta") and seed % 3 != 0:
+        arms["beta_activation"] = "sigmoid"
+    # several staged token blocks, a ragged tail, a one-token and an empty request
+    lengths = [70, 1, 0, 33] if algo == "recurrent" else [1, 3, 0, 8, 1]
+    case = workloads.random_case(seed, lengths=lengths, H=2, HV=4, DK=dk, DV=dv, dtype=dtype,
+                                 update_rule=rule, per_key=per_key, qk_l2_norm=seed % 2,
+                                 unit_keys=True, **arms)
+    _check_full(case, algo, "%s %s %s" % (rule, algo, dtype.__name__))
+
+
+def test_gqa_ratio_and_scale():
+    case = workloads.random_case(7, lengths=[40, 9], H=2, HV=8, DK=128, DV=64,
+                                 update_rule="gated_delta", beta_activation="sigmoid")
+    case["scale"] = 0.37
+    _check_full(case, "recurrent", "HV/H=4 explicit scale")
+
+
+def test_decode_kernel_multi_token_requests():
+    case = workloads.random_case(11, rank4_batch=(16, 4), H=4, HV=8, DK=128, DV=128,
+                                 dtype=np.float16, update_rule="gated_delta",
+                                 gate_activation="qwen", beta_activation="sigmoid",
+                                 slots=(40,))
+    _check_full(case, "decode", "decode L=4 slab")
+
+
+# ------------------------------------------------------------------ the five workloads, full size
+def test_decode_workload_full():
+    case = workloads.decode_slab()
+    d = to_dev(case)
+    slab0 = d["slab"].clone()
+    say("case %s: decode kernel" % case["name"])
+    o, new_slab = gpu_forward(case, "auto", dev=d)
+    ids = case["slot_ids"]
+    gath = dict(case, slab=None, slot_ids=None, initial_state=case["slab"][ids])
+    ro, rs = oracle_forward(gath)
+    assert_close(o, ro, TOL_F16, "decode o")
+    assert_close(new_slab[ids], rs, TOL_F16, "decode slab rows")
+    untouched = np.setdiff1d(np.arange(case["slab"].shape[0]), ids)
+    assert np.array_equal(new_slab[untouched], case["slab"][untouched].astype(np.float64)), \
+        "untouched slots must be bit-identical"
+    # the rank-3 spelling with cu_seqlens = [0, 1, ..., B] is the same call
+    B = len(ids)
+    r3 = dict(case, q=case["q"].reshape(B, 16, 128), k=case["k"].reshape(B, 16, 128),
+              v=case["v"].reshape(B, 32, 128), gate=case["gate"].reshape(B, 32),
+              beta=case["beta"].reshape(B, 32), cu_seqlens=np.arange(B + 1, dtype=np.int32))
+    o3, slab3 = gpu_forward(r3, "auto")
+    assert np.array_equal(o3.reshape(o.shape), o) and np.array_equal(slab3, new_slab)
+    # the recurrent kernel on the same step agrees with the oracle too
+    o4, slab4 = gpu_forward(case, "recurrent")
+    assert_close(o4, ro, TOL_F16, "decode via recurrent o")
+    assert_close(slab4[ids], rs, TOL_F16, "decode via recurrent slab rows")
+    del slab0
+
+
+def _sampled(case, algo, pairs, tol, label):
+    say("case %s algo=%s (GPU full, oracle on %d sampled request-head pairs)" % (case["name"], algo, len(pairs)))
+    o, st = gpu_forward(case, algo)
+    T = o.shape[0] * (o.shape[1] if o.ndim == 4 else 1)
+    of = o.reshape(T, o.shape[-2], o.shape[-1])
+    for b, heads in pairs:
+        sc, (s, e) = sub_case(case, b, heads)
+        ro, rs = oracle_forward(sc)
+        assert_close(of[s:e][:, heads], ro, tol, "%s o req %d heads %s" % (label, b, heads))
+        assert_close(st[b][heads], rs[0], tol, "%s state req %d heads %s" % (label, b, heads))
+
+
+def test_varlen_prefill_workload_full():
+    case = workloads.varlen_prefill()
+    _sampled(case, "recurrent", [(0, [0, 31]), (3, [5]), (7, [16, 17])], TOL_F16, "varlen")
+
+
+def test_long_prefill_workload_full_recurrent():
+    case = workloads.long_prefill()
+    _sampled(case, "recurrent", [(0, [0]), (0, [11])], TOL_F16, "long")
+
+
+def test_perkey_erase_workload_full():
+    case = workloads.perkey_erase()
+    _sampled(case, "recurrent", [(0, [0, 3]), (3, [31])], TOL_F16, "perkey+erase")
+
+
+# ------------------------------------------------------------------ bit-exact addressing
+def _small(seed, **kw):
+    base = dict(H=2, HV=4, DK=128, DV=128, dtype=np.float16, update_rule="gated_delta",
+                gate_activation="qwen", beta_activation="sigmoid", qk_l2_norm=1)
+    base.update(kw)
+    return workloads.random_case(seed, **base)
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "decode"])
+def test_slots_equal_gather_scatter(algo):
+    case = _small(21, rank4_batch=(6, 5), slots=(13,))
+    o, slab = gpu_forward(case, algo)
+    ids = case["slot_ids"]
+    g = dict(case, slab=None, slot_ids=None, initial_state=case["slab"][ids])
+    o2, st2 = gpu_forward(g, algo)
+    assert np.array_equal(o, o2)
+    assert np.array_equal(slab[ids], st2)
+    rest = np.setdiff1d(np.arange(13), ids)
+    assert np.array_equal(slab[rest], case["slab"][rest].astype(np.float64))
+
+
+def test_out_of_range_slot_is_skipped():
+    case = _small(22, rank4_batch=(4, 3), slots=(9,))
+    case["slot_ids"] = np.array([2, 9, -1, 5], dtype=np.int32)
+    d = to_dev(case)
+    sentinel = torch.full((4, 3, 4, 128), 7.0, dtype=torch.float16, device="cuda")
+    o, slab = gpu_forward(case, "recurrent", dev=d, out=sentinel)
+    assert np.all(o[1] == 7.0) and np.all(o[2] == 7.0), "skipped requests write no output"
+    for s in (0, 1, 3, 4, 6, 7, 8):
+        assert np.array_equal(slab[s], case["slab"][s].astype(np.float64))
+    ro, rs = oracle_forward(case)
+    assert_close(o[[0, 3]], ro[[0, 3]], TOL_F16, "valid requests o")
+
+
+def test_packed_equals_separate_and_empty_copies():
+    case = _small(23, lengths=[37, 0, 64, 5], DV=64)
+    o, st = gpu_forward(case, "recurrent")
+    cu = case["cu_seqlens"]
+    for b in range(4):
+        s, e = int(cu[b]), int(cu[b + 1])
+        sc, _ = sub_case(case, b, [0, 1, 2, 3])
+        sc["q"], sc["k"] = case["q"][s:e], case["k"][s:e]  # keep the grouped q/k heads
+        ob, sb = gpu_forward(sc, "recurrent")
+        assert np.array_equal(o[s:e], ob), "request %d o differs when run alone" % b
+        assert np.array_equal(st[b], sb[0]), "request %d state differs when run alone" % b
+    assert np.array_equal(st[1], case["initial_state"][1].astype(np.float64)), "empty request copies its state"
+
+
+def test_clamped_cu_seqlens():
+    case = _small(24, lengths=[10, 10, 10], DV=32)
+    case["cu_seqlens"] = np.array([0, 12, 7, 1000], dtype=np.int32)
+    o, st = gpu_forward(case, "recurrent")
+    ro, rs = oracle_forward(case)
+    assert_close(st, rs, TOL_F16, "clamped cu_seqlens states")
+    assert np.array_equal(st[1], case["initial_state"][1].astype(np.float64))
+
+
+@pytest.mark.parametrize("split", [1, 31, 32, 45])
+def test_resume_split_is_bit_exact(split):
+    case = _small(25, lengths=[90], DV=64)
+    o, st = gpu_forward(case, "recurrent")
+    a = dict(case, q=case["q"][:split], k=case["k"][:split], v=case["v"][:split],
+             gate=case["gate"][:split], beta=case["beta"][:split],
+             cu_seqlens=np.array([0, split], np.int32))
+    oa, sa = gpu_forward(a, "recurrent")
+    b = dict(case, q=case["q"][split:], k=case["k"][split:], v=case["v"][split:],
+             gate=case["gate"][split:], beta=case["beta"][split:],
+             cu_seqlens=np.array([0, 90 - split], np.int32), initial_state=sa.astype(np.float32))
+    ob, sb = gpu_forward(b, "recurrent")
+    assert np.array_equal(np.concatenate([oa, ob]), o)
+    assert np.array_equal(sb, st)
+
+
+def test_deterministic():
+    case = workloads.varlen_prefill(lengths=[700, 300])
+    a = gpu_forward(case, "recurrent")
+    b = gpu_forward(case, "recurrent")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rule_reduction_gated_delta_zero_gate():
+    # fp32 activations so the comparison is not blurred by fp16 output rounding;
+    # the two paths differ only in fp32 rounding of the (exactly 1) decay
+    case = _small(26, lengths=[50], DV=32, gate_activation="none", dtype=np.float32)
+    case["gate"] = np.zeros_like(case["gate"])
+    a = gpu_forward(case, "recurrent")
+    b = gpu_forward(dict(case, gate=None, update_rule="delta"), "recurrent")
+    assert_close(a[0], b[0], 1e-5, "gated_delta(g=0) vs delta o")
+    assert_close(a[1], b[1], 1e-5, "gated_delta(g=0) vs delta state")
+
+
+# ------------------------------------------------------------------ standalone gate
+@pytest.mark.parametrize("dtype", [np.float32, np.float16], ids=["f32", "f16"])
+def test_gate_kernel(dtype):
+    from gated_delta_rule_token_amd import api
+    rng = np.random.Generator(np.random.PCG64(31))
+    a = (3 * rng.standard_normal((37, 5))).astype(dtype)
+    a[0, 0], a[1, 1] = 30.0, -30.0
+    b = rng.standard_normal((37, 5)).astype(dtype)
+    dt_bias = rng.uniform(0, 1, 5).astype(np.float32)
+    dscale = -np.exp(np.log(rng.uniform(1, 16, 5))).astype(np.float32)
+    tt = lambda x: torch.from_numpy(x).cuda()
+    decay, beta = api.gate(tt(a), tt(dt_bias), tt(dscale), b=tt(b), want_beta=True)
+    ref_decay = dscale.astype(np.float64) * np.logaddexp(0.0, a.astype(np.float64) + dt_bias)
+    ref_beta = 1.0 / (1.0 + np.exp(-b.astype(np.float64)))
+    tol = 1e-6 if dtype == np.float32 else 1e-3
+    got_d = decay.double().cpu().numpy()
+    got_b = beta.double().cpu().numpy()
+    assert np.max(np.abs(got_d - ref_decay) / np.maximum(np.abs(ref_decay), 1e-3)) < tol
+    assert np.max(np.abs(got_b - ref_beta)) < tol
