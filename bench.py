@@ -161,7 +161,7 @@ def cpu_baseline(case, total_bytes):
     oracle.build()
     cores = oracle.num_threads()
     reps, elapsed = 0, 0.0
-    while elapsed < 10.0 and reps < 20:
+    while elapsed < 10.0 and reps < 200:
         t0 = time.perf_counter()
         oracle.forward(case["q"], case["k"], case["v"], **g)
         elapsed += time.perf_counter() - t0
@@ -182,6 +182,9 @@ def main():
     ap.add_argument("--prefill-algo", default="auto")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
+                         "known-size reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the engine has no multi-GPU path in this build "
@@ -190,6 +193,13 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     result = {"metric": METRIC}
     if args.only in (None, "decode"):
