@@ -41,6 +41,13 @@ bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.h
 // Number of state rows (batch or slab) the final_state buffer holds.
 int64_t state_rows(const gdr_problem *p) { return p->num_slots > 0 ? p->num_slots : p->batch; }
 
+// Shapes the chunk-parallel kernels implement.
+bool chunked_ok(const gdr_problem *p)
+{
+    return p->head_dim_k == 128 && p->head_dim_v == 128 && p->act_dtype == GDR_F16 && !p->decay_per_key &&
+           p->update_rule != GDR_RULE_GATED_DELTA_V2;
+}
+
 gdr_status check_problem(const gdr_problem *p)
 {
     if (!p) return fail(GDR_E_INVALID, "problem is NULL");
@@ -77,8 +84,9 @@ gdr_status check_problem(const gdr_problem *p)
     if (blocks > INT32_MAX) return fail(GDR_E_INVALID, "batch * num_heads_v too large");
     if (p->algo == GDR_ALGO_DECODE && (p->head_dim_k != 128 || p->head_dim_v != 128))
         return fail(GDR_E_UNSUPPORTED, "the decode kernel needs dk = dv = 128");
-    if (p->algo == GDR_ALGO_CHUNKED)
-        return fail(GDR_E_UNSUPPORTED, "the chunked kernel is not built in this library version");
+    if (p->algo == GDR_ALGO_CHUNKED && !chunked_ok(p))
+        return fail(GDR_E_UNSUPPORTED, "the chunked kernels need dk = dv = 128, fp16 activations, a per-head "
+                                       "decay and an update rule other than gated_delta_v2");
     return GDR_OK;
 }
 
@@ -162,6 +170,8 @@ int32_t pick_algo(const gdr_problem *p)
     // tokens per request on average; decode when requests are a handful of tokens
     const int64_t per_req = p->batch > 0 ? (p->total_tokens + p->batch - 1) / p->batch : 0;
     if (d128 && per_req <= 8) return GDR_ALGO_DECODE;
+    // long requests: the chunk-parallel form when its shapes are supported
+    if (chunked_ok(p) && per_req >= 128) return GDR_ALGO_CHUNKED;
     return GDR_ALGO_RECURRENT;
 }
 
@@ -211,7 +221,9 @@ gdr_status gdr_workspace_size(const gdr_problem *problem, size_t *bytes)
     if (!bytes) return fail(GDR_E_INVALID, "bytes is NULL");
     gdr_status st = check_problem(problem);
     if (st != GDR_OK) return st;
-    *bytes = 0;
+    *bytes = pick_algo(problem) == GDR_ALGO_CHUNKED
+                 ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_v)
+                 : 0;
     return GDR_OK;
 }
 
@@ -236,7 +248,6 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     gdr_workspace_size(problem, &need);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GDR_E_WORKSPACE, "workspace of %zu bytes required", need);
-    (void)workspace;
 
     const gdr_problem &p = *problem;
     const gdr_tensors &t = *tensors;
@@ -275,6 +286,7 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     hipError_t err;
     switch (pick_algo(problem)) {
     case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, f16, s); break;
+    case GDR_ALGO_CHUNKED: err = gdr::launch_chunked(k, p.update_rule, workspace, s); break;
     default: err = gdr::launch_recurrent(k, p.update_rule, pk, f16, dk_tile(p.head_dim_k), rows_group(problem), s); break;
     }
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));

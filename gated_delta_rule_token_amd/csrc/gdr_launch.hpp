@@ -15,6 +15,11 @@ hipError_t launch_recurrent(const Params &p, int rule, bool per_key, bool f16, i
 // Decode kernel, dk = dv = 128 only.
 hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s);
 
+// Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations, scalar
+// decay); `ws` holds chunked_workspace_bytes(T, B, HV) bytes.
+size_t chunked_workspace_bytes(int64_t T, int B, int HV);
+hipError_t launch_chunked(const Params &p, int rule, void *ws, hipStream_t s);
+
 // Standalone gate fusion.
 hipError_t launch_gate(int64_t count, int heads, bool f16, const void *a, const float *dt_bias,
                        const float *decay_scale, const void *b, void *decay, void *beta, hipStream_t s);

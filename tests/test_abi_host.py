@@ -103,6 +103,7 @@ BAD = [
     ("state_aliases_v", dict(final_state=_fake(3) + 256), api.GDR_E_ALIAS),
     ("per_key_qwen", dict(decay_per_key=1), api.GDR_E_UNSUPPORTED),
     ("decode_needs_128", dict(algo=api.ALGOS["decode"]), api.GDR_E_UNSUPPORTED),
+    ("chunked_needs_128_f16", dict(algo=api.ALGOS["chunked"]), api.GDR_E_UNSUPPORTED),
     ("gate_dtype", dict(gate_dtype=api.F16), api.GDR_E_INVALID),
 ]
 
@@ -162,6 +163,14 @@ def test_workspace_and_algo_selection(lib):
     p.head_dim_k = p.head_dim_v = 128
     p.total_tokens, p.batch = 256, 256
     assert api.selected_algo(p) == "decode"
+    # long fp16 requests at dk = dv = 128 take the chunked kernels and need a workspace
+    p.total_tokens, p.batch, p.act_dtype, p.gate_dtype = 4096, 2, api.F16, api.F16
+    assert api.selected_algo(p) == "chunked"
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
+    assert n.value >= (4096 // 64) * 4 * 64 * 128 * 4
+    # per-key decay stays on the recurrent kernel
+    p.decay_per_key, p.gate_activation, p.gate_dtype = 1, 0, api.F32
+    assert api.selected_algo(p) == "recurrent"
 
 
 def test_gate_argument_checks(lib):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_token_amd import workloads
-from tests.gpu_helpers import (TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
+from tests.gpu_helpers import (TOL_CHUNKED, TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
                                sub_case, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -258,3 +258,63 @@ def test_gate_kernel(dtype):
     got_b = beta.double().cpu().numpy()
     assert np.max(np.abs(got_d - ref_decay) / np.maximum(np.abs(ref_decay), 1e-3)) < tol
     assert np.max(np.abs(got_b - ref_beta)) < tol
+
+
+# ------------------------------------------------------------------ chunked prefill
+CHUNK_RULES = ["linear", "gated", "delta", "gated_delta"]
+
+
+@pytest.mark.parametrize("rule", CHUNK_RULES)
+@pytest.mark.parametrize("arms", ["plain", "qwen_sigmoid_l2"])
+def test_chunked_rules(rule, arms):
+    kw = {}
+    if arms != "plain":
+        kw["qk_l2_norm"] = 1
+        if rule in ("gated", "gated_delta"):
+            kw["gate_activation"] = "qwen"
+        if rule in ("delta", "gated_delta"):
+            kw["beta_activation"] = "sigmoid"
+    # several chunks, a ragged tail, an exact multiple of 64, one token, an empty request
+    case = workloads.random_case(zlib.crc32(("chunk/%s/%s" % (rule, arms)).encode()) % 1000,
+                                 lengths=[200, 1, 0, 64, 130], H=2, HV=4, DK=128, DV=128,
+                                 dtype=np.float16, update_rule=rule, unit_keys=(arms == "plain"), **kw)
+    _check_full(case, "chunked", "chunked %s %s" % (rule, arms))
+
+
+def test_chunked_gqa_and_slab():
+    case = workloads.random_case(41, rank4_batch=(3, 150), H=2, HV=8, DK=128, DV=128,
+                                 dtype=np.float16, update_rule="gated_delta",
+                                 gate_activation="qwen", beta_activation="sigmoid", slots=(7,))
+    say("case chunked slab")
+    o, slab = gpu_forward(case, "chunked")
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "chunked slab o")
+    ids = case["slot_ids"]
+    assert_close(slab[ids], rs[ids], TOL_CHUNKED, "chunked slab rows")
+    rest = np.setdiff1d(np.arange(7), ids)
+    assert np.array_equal(slab[rest], case["slab"][rest].astype(np.float64))
+
+
+def test_chunked_matches_recurrent():
+    case = workloads.varlen_prefill(lengths=[700, 65, 300])
+    a = gpu_forward(case, "chunked")
+    b = gpu_forward(case, "recurrent")
+    assert_close(a[0], b[0], TOL_CHUNKED, "chunked vs recurrent o")
+    assert_close(a[1], b[1], TOL_CHUNKED, "chunked vs recurrent state")
+
+
+def test_chunked_deterministic():
+    case = workloads.varlen_prefill(lengths=[333, 129])
+    a = gpu_forward(case, "chunked")
+    b = gpu_forward(case, "chunked")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_long_prefill_workload_full_chunked():
+    case = workloads.long_prefill()
+    _sampled(case, "chunked", [(0, [0]), (0, [7]), (0, [15])], TOL_CHUNKED, "long chunked")
+
+
+def test_varlen_prefill_workload_full_chunked():
+    case = workloads.varlen_prefill()
+    _sampled(case, "chunked", [(0, [0, 31]), (2, [9]), (5, [20, 21])], TOL_CHUNKED, "varlen chunked")
