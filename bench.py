@@ -13,8 +13,9 @@ Infinity Cache.
 
 Also reported: prefill tokens/s on the varlen workload (8 requests of
 512..8192 tokens, H=16, HV=32, dk=dv=128, fp16, raw-gate arm, qk L2-norm,
-fp32 initial/final states) with its roofline fraction, and the fp64 CPU
-oracle timed on the host cores on the decode step (``cpu_baseline``).
+fp32 initial/final states) and on one 65,536-token sequence (H=HV=16), each
+with its algorithmic flop rate against the fp32 vector peak, and the fp64
+CPU oracle timed on the host cores on the decode step (``cpu_baseline``).
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 run on (torch's current stream), around every timed launch.
@@ -125,29 +126,34 @@ def bench_decode(args):
     }
 
 
-def bench_prefill(args):
+def bench_prefill(args, which):
+    """Prefill throughput on the varlen workload (8 requests, cu_seqlens, qk
+    L2-norm, raw gate, random initial states) or the long single sequence
+    (65,536 tokens, H=HV=16, log decay and update rate given directly)."""
     import torch
     from gated_delta_rule_token_amd import api, workloads
-    case = workloads.varlen_prefill()
-    T, H, dk = case["q"].shape
-    HV, dv = case["v"].shape[1:]
-    call = api.prepare(_t(case["q"]), _t(case["k"]), _t(case["v"]), gate=_t(case["gate"]),
-                       beta=_t(case["beta"]), a_log=_t(case["a_log"]), dt_bias=_t(case["dt_bias"]),
+    case = workloads.varlen_prefill() if which == "varlen" else workloads.long_prefill()
+    q, k, v = case["q"], case["k"], case["v"]
+    T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
+    dk, HV, dv = q.shape[-1], v.shape[-2], v.shape[-1]
+    call = api.prepare(_t(q), _t(k), _t(v), gate=_t(case["gate"]), beta=_t(case["beta"]),
+                       a_log=_t(case["a_log"]), dt_bias=_t(case["dt_bias"]),
                        cu_seqlens=_t(case["cu_seqlens"]), initial_state=_t(case["initial_state"]),
-                       update_rule="gated_delta", gate_activation="qwen", beta_activation="sigmoid",
-                       qk_l2_norm=1, algo=args.prefill_algo)
+                       update_rule=case["update_rule"], gate_activation=case["gate_activation"],
+                       beta_activation=case["beta_activation"], qk_l2_norm=case["qk_l2_norm"],
+                       algo=args.prefill_algo)
     steps = max(1, args.prefill_steps)
     wall, kms = time_calls([call], steps, max(1, args.warmup // 2))
-    flops = 7.0 * dk * dv * HV * T  # decay, two dot products, rank-1 write per row element
+    flops = 7.0 * dk * dv * HV * T  # decay, two dot products, rank-1 write per state element
     tflops = flops / (kms * 1e-3) / 1e12
-    lengths = np.diff(case["cu_seqlens"]).tolist()
-    return {
-        "workload": case["name"], "lengths": lengths, "tokens": int(T), "algo": call.algo,
-        "steps": steps, "kernel_ms": kms, "tokens_per_s": T / (kms * 1e-3),
-        "tokens_per_s_wall": T * steps / wall,
-        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None},
+    out = {
+        "workload": case["name"], "tokens": int(T), "algo": call.algo, "steps": steps,
+        "ms_per_call": kms, "tokens_per_s": T / (kms * 1e-3), "tokens_per_s_wall": T * steps / wall,
+        "algorithmic_tflops": tflops, "frac_of_fp32_vector_peak": tflops / FP32_VECTOR_PEAK_TFLOPS,
     }
+    if case["cu_seqlens"] is not None:
+        out["lengths"] = np.diff(case["cu_seqlens"]).tolist()
+    return out
 
 
 def cpu_baseline(case, total_bytes):
@@ -180,7 +186,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--decode-algo", default="auto")
     ap.add_argument("--prefill-algo", default="auto")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "varlen", "long"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
@@ -225,8 +231,10 @@ def main():
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
         del case
-    if args.only in (None, "prefill"):
-        result["prefill"] = bench_prefill(args)
+    if args.only in (None, "prefill", "varlen"):
+        result["prefill"] = bench_prefill(args, "varlen")
+    if args.only in (None, "prefill", "long"):
+        result["prefill_long"] = bench_prefill(args, "long")
     print(json.dumps(result), flush=True)
 
 

@@ -23,7 +23,8 @@
 //                  products are exact up to fp32 accumulation), the unit
 //                  lower-triangular solve for [W | U] by fp32 forward
 //                  substitution (one column per thread), and the per-token
-//                  scalars.  W and P are stored as fp16 (hi, lo) pairs.
+//                  scalars.  W and P are stored as fp16 (hi, lo) pairs, and
+//                  the chunk's K transposed (dk x 64) for the scan.
 //   k_chunk_scan   one workgroup per (request, head, 32 state rows), chunks
 //                  in order; the state tile lives in MFMA accumulators.  Each
 //                  chunk: D = U - W S^T, O = gq (Q S^T) + P D,
@@ -39,6 +40,7 @@
 namespace gdr {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;          // chunk length
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 template <int RULE>
 __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_t *__restrict__ off,
                                                    half_t *__restrict__ ws_w, half_t *__restrict__ ws_p,
-                                                   float *__restrict__ ws_u, float *__restrict__ ws_s)
+                                                   float *__restrict__ ws_u, float *__restrict__ ws_s,
+                                                   half_t *__restrict__ ws_kt)
 {
     constexpr bool DEC = rule_decays(RULE);
     constexpr bool RET = rule_retrieves(RULE);
@@ -158,7 +161,21 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
         *reinterpret_cast<h8 *>(&sQ[r][c8]) = qq;
         *reinterpret_cast<h8 *>(&sV[r][c8]) = vv;
     }
-    __syncthreads();
+    lds_barrier();
+
+    // ---- K^T of the chunk (dk rows, 64 tokens each) for the scan's state update;
+    // thread = (key column, half of the tokens), lanes read one LDS row each step
+    {
+        const int c = tid & (D128 - 1), th = tid >> 7;
+        h8 col[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) col[g][x] = sK[32 * th + 8 * g + x][c];
+        h8 *dstk = reinterpret_cast<h8 *>(ws_kt + ch * D128 * CH + (size_t)c * CH + 32 * th);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dstk[g] = col[g];
+    }
 
     // ---- per-token scalars: log decay, update rate, inverse norms
     if (tid < CH) {
@@ -184,7 +201,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
         sIk[t] = ik;
         sIq[t] = iq;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         float acc = 0.f;
         for (int t = 0; t < CH; ++t) {
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
             sG[t] = acc;  // inclusive cumulative log decay inside the chunk
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < CH) sRw[tid] = sBeta[tid] * expf(sG[tid]) * sIk[tid];  // row scale of K in the W right-hand side
 
     // ---- Q K^T -> P (hi, lo) and K K^T -> A, tiles of 16 x 16 (wave = token block)
@@ -223,7 +240,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- [W | U] = (I + A)^-1 [diag(beta gamma / |k|) K | diag(beta) V]; column per thread
     if constexpr (RET) {
@@ -274,17 +291,20 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
                                                    const half_t *__restrict__ ws_w,
                                                    const half_t *__restrict__ ws_p,
                                                    const float *__restrict__ ws_u,
-                                                   const float *__restrict__ ws_s)
+                                                   const float *__restrict__ ws_s,
+                                                   const half_t *__restrict__ ws_kt)
 {
     constexpr bool RET = rule_retrieves(RULE);
-    constexpr int LS = D128 + 4;   // fp32 state row in LDS
-    constexpr int LDD = TR + 4;    // fp32 delta row
-    constexpr int LKT = CH + 8;    // fp16 transposed-K row
+    constexpr int LS = D128 + 8;   // fp16 state row (272 B)
+    constexpr int LDT = CH + 8;    // fp16 row of the transposed delta (144 B)
 
-    __shared__ __align__(16) float sS[TR][LS];
-    __shared__ __align__(16) float sD[CH][LDD];
-    __shared__ __align__(16) half_t sKt[D128][LKT];
-    __shared__ float sSc[2 * CH + 4];
+    // Operands are split into fp16 (hi, lo) once, by the lane that owns the
+    // value, and stored as planes; every MFMA fragment is then one 16-byte
+    // LDS read.  Row strides of 68 and 36 dwords put the 16 lanes of a
+    // 16-byte access phase on 16 distinct 4-bank groups.
+    __shared__ __align__(16) half_t sS[2][TR][LS];    // state tile, hi / lo
+    __shared__ __align__(16) half_t sDt[4][TR][LDT];  // D^T hi / lo, (kd D)^T hi / lo
+    __shared__ float sSc[256];
 
     const int HV = p.HV, H = p.H;
     // XCD-aware order: blocks i, i+8, i+16, i+24 (one XCD) are the 4 tiles of one head
@@ -319,71 +339,122 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
             Sacc[j][i] = src ? src[(size_t)r * D128 + c] : 0.f;
         }
 
-    for (int j = 0; j < nch; ++j) {
-        const size_t ch = (size_t)(c0 + j) * HV + h;
-        const int64_t t0 = rs + (int64_t)j * CH;
-        const int n = (int)((re - t0) < CH ? (re - t0) : CH);
-        __syncthreads();
-        // ---- A: state tile -> LDS; K^T of the chunk -> LDS; scalars
+    // Operands of one chunk, loaded one chunk ahead so their global-memory
+    // latency hides behind the previous chunk's matrix work.  Rows past the
+    // end of the request read as zero.
+    const int tb = wave;          // token block of this wave in steps B and D
+    const int tr = 16 * tb + lr;  // A-operand row (token) of this lane
+    struct Ops {
+        h8 kt[2][4];              // K^T fragments of the state update: token steps x dk tiles
+        h8 wh[4], wl[4], aq[4];   // W (hi, lo) and Q rows, four k-steps of 32
+        h8 ph[2], pl[2];          // P (hi, lo) rows, two k-steps of 32
+        float u[2][4];            // U at this lane's D-layout positions
+        float kd[4];              // kd of this lane's four D-layout tokens
+        float sc;                 // one per-chunk scalar (threads < 129)
+        int n;                    // valid tokens in the chunk
+        int64_t t0;
+    };
+    // Every load below is unconditional (a branch around a load makes the
+    // compiler wait for it on the spot, which would defeat the prefetch).
+    auto fetch = [&](int jj, Ops &f) {
+        const size_t ch = (size_t)(c0 + jj) * HV + h;
+        f.t0 = rs + (int64_t)jj * CH;
+        f.n = (int)((re - f.t0) < CH ? (re - f.t0) : CH);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                f.kt[ks][jj] = ld_h8(ws_kt + ch * D128 * CH + (size_t)(16 * (dkb0 + jj) + lr) * CH + 32 * ks + lk);
+        f.sc = ws_s[ch * SC_STRIDE + (tid < 2 * CH ? tid : 2 * CH)];
+        const half_t *wh = ws_w + (ch * 2 + 0) * CH * D128 + (size_t)tr * D128;
+        const half_t *wl = ws_w + (ch * 2 + 1) * CH * D128 + (size_t)tr * D128;
+        // rows past the request end read its last row; their outputs are never stored
+        const int tq = tr < f.n ? tr : f.n - 1;
+        const half_t *qp = q + ((size_t)(f.t0 + tq) * H + qh) * D128;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            f.aq[kk] = ld_h8(qp + 32 * kk + lk);
+            if constexpr (RET) {
+                f.wh[kk] = ld_h8(wh + 32 * kk + lk);
+                f.wl[kk] = ld_h8(wl + 32 * kk + lk);
+            }
+        }
+        const half_t *ph = ws_p + (ch * 2 + 0) * CH * CH + (size_t)tr * CH;
+        const half_t *pl = ws_p + (ch * 2 + 1) * CH * CH + (size_t)tr * CH;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f.ph[ks] = ld_h8(ph + 32 * ks + lk);
+            f.pl[ks] = ld_h8(pl + 32 * ks + lk);
+        }
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f.u[vb][i] = ws_u[ch * CH * D128 + (size_t)(16 * tb + 4 * lq + i) * D128 + row0 + 16 * vb + lr];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.kd[i] = ws_s[ch * SC_STRIDE + CH + 16 * tb + 4 * lq + i];
+    };
+
+    // one chunk: consumes `cur`, prefetches chunk j + 1 into `nxt`
+    auto step = [&](int j, const Ops &cur, Ops &nxt) {
+        const int64_t t0 = cur.t0;
+        const int n = cur.n;
+        lds_barrier();
+        // ---- A: state tile -> LDS (hi, lo); scalars
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = Sacc[jj][i];
-        for (int idx = tid; idx < CH * 16; idx += 256) {
-            const int r = idx >> 4, c8 = (idx & 15) * 8;
-            h8 kk = {};
-            if (r < n) kk = ld_h8(k + ((size_t)(t0 + r) * H + qh) * D128 + c8);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) sKt[c8 + x][r] = kk[x];
-        }
-        if (tid < 2 * CH + 1) sSc[tid] = ws_s[ch * SC_STRIDE + tid];
-        __syncthreads();
+            for (int i = 0; i < 4; ++i) {
+                const float x = Sacc[jj][i];
+                const half_t hi = (half_t)x;
+                sS[0][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = hi;
+                sS[1][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = (half_t)(x - (float)hi);
+            }
+        sSc[tid] = cur.sc;  // entries past 2 * CH repeat gamma_C and are not read
+        // next chunk's operands (the last chunk re-reads itself: every lane
+        // issues the same loads on every iteration)
+        fetch(j + 1 < nch ? j + 1 : j, nxt);
+        lds_barrier();
 
-        // ---- B: D = U - W S^T and Opre = Q S^T for token block tb = wave, dv blocks 0, 1
-        const int tb = wave;
+        // ---- B: D = U - W S^T and Opre = Q S^T for token block tb, dv blocks 0, 1
         f4v accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f4v accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        {
-            const int tr = 16 * tb + lr;  // A-operand row (token)
-            const bool tv = tr < n;
-            const half_t *wh = ws_w + (ch * 2 + 0) * CH * D128 + (size_t)tr * D128;
-            const half_t *wl = ws_w + (ch * 2 + 1) * CH * D128 + (size_t)tr * D128;
-            const half_t *qp = q + ((size_t)(t0 + tr) * H + qh) * D128;
 #pragma unroll
-            for (int kk = 0; kk < D128; kk += 32) {
-                h8 aq = {};
-                if (tv) aq = ld_h8(qp + kk + lk);
-                h8 awh = {}, awl = {};
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb) {
+                const h8 shi = ld_h8(&sS[0][16 * vb + lr][32 * kk + lk]);
+                const h8 slo = ld_h8(&sS[1][16 * vb + lr][32 * kk + lk]);
                 if constexpr (RET) {
-                    awh = ld_h8(wh + kk + lk);
-                    awl = ld_h8(wl + kk + lk);
+                    accD[vb] = mfma16(cur.wh[kk], shi, accD[vb]);
+                    accD[vb] = mfma16(cur.wh[kk], slo, accD[vb]);
+                    accD[vb] = mfma16(cur.wl[kk], shi, accD[vb]);
                 }
-#pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    float sv[8];
-                    const float *sp = &sS[16 * vb + lr][kk + lk];
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) sv[x] = sp[x];
-                    h8 shi, slo;
-                    split8(sv, shi, slo);
-                    if constexpr (RET) {
-                        accD[vb] = mfma16(awh, shi, accD[vb]);
-                        accD[vb] = mfma16(awh, slo, accD[vb]);
-                        accD[vb] = mfma16(awl, shi, accD[vb]);
-                    }
-                    accO[vb] = mfma16(aq, shi, accO[vb]);
-                    accO[vb] = mfma16(aq, slo, accO[vb]);
-                }
+                accO[vb] = mfma16(cur.aq[kk], shi, accO[vb]);
+                accO[vb] = mfma16(cur.aq[kk], slo, accO[vb]);
             }
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * lq + i, c = 16 * vb + lr;
-                    sD[t][c] = ws_u[ch * CH * D128 + (size_t)t * D128 + row0 + c] - accD[vb][i];
-                }
         }
-        __syncthreads();
+        // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
+        // tokens per lane -> one 8-byte write per plane of D^T
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+            h4 dh, dl, sh, sl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = cur.u[vb][i] - accD[vb][i];
+                const float ds = cur.kd[i] * d;
+                dh[i] = (half_t)d;
+                dl[i] = (half_t)(d - (float)dh[i]);
+                sh[i] = (half_t)ds;
+                sl[i] = (half_t)(ds - (float)sh[i]);
+            }
+            const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
+            *reinterpret_cast<h4 *>(&sDt[0][r][c]) = dh;
+            *reinterpret_cast<h4 *>(&sDt[1][r][c]) = dl;
+            *reinterpret_cast<h4 *>(&sDt[2][r][c]) = sh;
+            *reinterpret_cast<h4 *>(&sDt[3][r][c]) = sl;
+        }
+        lds_barrier();
 
         // ---- D: O = gq (Q S^T) + P D for token block tb, dv blocks 0, 1
         {
@@ -392,23 +463,17 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
             for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) accP[vb][i] = sSc[16 * tb + 4 * lq + i] * accO[vb][i];
-            const int tr = 16 * tb + lr;
-            const half_t *ph = ws_p + (ch * 2 + 0) * CH * CH + (size_t)tr * CH;
-            const half_t *pl = ws_p + (ch * 2 + 1) * CH * CH + (size_t)tr * CH;
+            // P is lower triangular; the block above the diagonal holds zeros
+            // and is multiplied anyway so that every prefetched fragment is used
 #pragma unroll
-            for (int ks = 0; ks < CH; ks += 32) {
-                if (ks > 16 * tb + 15) break;  // P is lower triangular
-                const h8 aph = ld_h8(ph + ks + lk), apl = ld_h8(pl + ks + lk);
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int vb = 0; vb < 2; ++vb) {
-                    float dv[8];
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) dv[x] = sD[ks + lk + x][16 * vb + lr];
-                    h8 dhi, dlo;
-                    split8(dv, dhi, dlo);
-                    accP[vb] = mfma16(aph, dhi, accP[vb]);
-                    accP[vb] = mfma16(aph, dlo, accP[vb]);
-                    accP[vb] = mfma16(apl, dhi, accP[vb]);
+                    const h8 dhi = ld_h8(&sDt[0][16 * vb + lr][32 * ks + lk]);
+                    const h8 dlo = ld_h8(&sDt[1][16 * vb + lr][32 * ks + lk]);
+                    accP[vb] = mfma16(cur.ph[ks], dhi, accP[vb]);
+                    accP[vb] = mfma16(cur.ph[ks], dlo, accP[vb]);
+                    accP[vb] = mfma16(cur.pl[ks], dhi, accP[vb]);
                 }
             }
 #pragma unroll
@@ -428,23 +493,24 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Sacc[jj][i] *= gC;
 #pragma unroll
-            for (int ks = 0; ks < CH; ks += 32) {
-                float dv[8];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    const int t = ks + lk + x;
-                    dv[x] = sSc[CH + t] * sD[t][16 * dvb + lr];
-                }
-                h8 dhi, dlo;
-                split8(dv, dhi, dlo);
+            for (int ks = 0; ks < 2; ++ks) {
+                const h8 dhi = ld_h8(&sDt[2][16 * dvb + lr][32 * ks + lk]);
+                const h8 dlo = ld_h8(&sDt[3][16 * dvb + lr][32 * ks + lk]);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const h8 bk = ld_h8(&sKt[16 * (dkb0 + jj) + lr][ks + lk]);
-                    Sacc[jj] = mfma16(dhi, bk, Sacc[jj]);
-                    Sacc[jj] = mfma16(dlo, bk, Sacc[jj]);
+                    Sacc[jj] = mfma16(dhi, cur.kt[ks][jj], Sacc[jj]);
+                    Sacc[jj] = mfma16(dlo, cur.kt[ks][jj], Sacc[jj]);
                 }
             }
         }
+    };
+
+    // two operand sets used in turn, so no register copy waits on a prefetch
+    Ops opa, opb;
+    if (nch > 0) fetch(0, opa);
+    for (int j = 0; j < nch; j += 2) {
+        step(j, opa, opb);
+        if (j + 1 < nch) step(j + 1, opb, opa);
     }
 
 #pragma unroll
@@ -460,7 +526,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
 size_t chunked_workspace_bytes(int64_t T, int B, int HV)
 {
     const int64_t maxch = (T + CH - 1) / CH + B;
-    const size_t per = (size_t)2 * CH * D128 * 2 + (size_t)2 * CH * CH * 2 + (size_t)CH * D128 * 4 + SC_STRIDE * 4;
+    const size_t per = (size_t)2 * CH * D128 * 2 + (size_t)2 * CH * CH * 2 + (size_t)CH * D128 * 4 + SC_STRIDE * 4 +
+                       (size_t)D128 * CH * 2;
     const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
     return table + (size_t)maxch * HV * per;
 }
@@ -477,15 +544,16 @@ static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
     half_t *ws_p = ws_w + nch * 2 * CH * D128;
     float *ws_u = reinterpret_cast<float *>(ws_p + nch * 2 * CH * CH);
     float *ws_s = ws_u + nch * CH * D128;
+    half_t *ws_kt = reinterpret_cast<half_t *>(ws_s + nch * SC_STRIDE);
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
     if (maxch * p.HV > 0)
         hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)(maxch * p.HV)), dim3(256), 0, s, p, off, ws_w, ws_p,
-                           ws_u, ws_s);
+                           ws_u, ws_s, ws_kt);
     const int64_t nbh = (int64_t)p.B * p.HV;
     const int64_t blocks = (nbh + 7) / 8 * 8 * NTILE;
     if (blocks > 0)
         hipLaunchKernelGGL((k_chunk_scan<RULE>), dim3((unsigned)blocks), dim3(256), 0, s, p, off, ws_w, ws_p, ws_u,
-                           ws_s);
+                           ws_s, ws_kt);
     return hipGetLastError();
 }
 

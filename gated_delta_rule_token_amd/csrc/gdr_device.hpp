@@ -63,6 +63,18 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 
+// ---------------------------------------------------------------- barriers
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, which makes every wave wait for its outstanding global loads
+// (vmcnt 0) -- including loads issued early on purpose to prefetch the next
+// block.  Kernels whose waves exchange data through LDS only use this one.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- gate math (fp32)
 // softplus(x) = log(1 + e^x), evaluated without overflow on either side.
 __device__ __forceinline__ float softplus_f32(float x)
