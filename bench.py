@@ -13,7 +13,8 @@ Infinity Cache.
 
 Also reported: prefill tokens/s on the varlen workload (8 requests of
 512..8192 tokens, H=16, HV=32, dk=dv=128, fp16, raw-gate arm, qk L2-norm,
-fp32 initial/final states) and on one 65,536-token sequence (H=HV=16), each
+fp32 initial/final states), on one 65,536-token sequence (H=HV=16), and on
+the per-key-decay / erase-gate workload (4 x 4096 tokens, H=8, HV=32), each
 with its algorithmic flop rate against the fp32 vector peak, and the fp64
 CPU oracle timed on the host cores on the decode step (``cpu_baseline``).
 
@@ -132,11 +133,13 @@ def bench_prefill(args, which):
     (65,536 tokens, H=HV=16, log decay and update rate given directly)."""
     import torch
     from gated_delta_rule_token_amd import api, workloads
-    case = workloads.varlen_prefill() if which == "varlen" else workloads.long_prefill()
+    case = {"varlen": workloads.varlen_prefill, "long": workloads.long_prefill,
+            "perkey": workloads.perkey_erase}[which]()
     q, k, v = case["q"], case["k"], case["v"]
     T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
     dk, HV, dv = q.shape[-1], v.shape[-2], v.shape[-1]
     call = api.prepare(_t(q), _t(k), _t(v), gate=_t(case["gate"]), beta=_t(case["beta"]),
+                       erase=_t(case["erase"]),
                        a_log=_t(case["a_log"]), dt_bias=_t(case["dt_bias"]),
                        cu_seqlens=_t(case["cu_seqlens"]), initial_state=_t(case["initial_state"]),
                        update_rule=case["update_rule"], gate_activation=case["gate_activation"],
@@ -186,7 +189,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--decode-algo", default="auto")
     ap.add_argument("--prefill-algo", default="auto")
-    ap.add_argument("--only", choices=["decode", "prefill", "varlen", "long"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "varlen", "long", "perkey"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
@@ -235,6 +238,8 @@ def main():
         result["prefill"] = bench_prefill(args, "varlen")
     if args.only in (None, "prefill", "long"):
         result["prefill_long"] = bench_prefill(args, "long")
+    if args.only in (None, "prefill", "perkey"):
+        result["prefill_perkey_erase"] = bench_prefill(args, "perkey")
     print(json.dumps(result), flush=True)
 
 

@@ -27,8 +27,8 @@
 //                  the chunk's K transposed (dk x 64) for the scan.
 //   k_chunk_scan   one workgroup per (request, head, 32 state rows), chunks
 //                  in order; the state tile lives in MFMA accumulators.  Each
-//                  chunk: D = U - W S^T, O = gq (Q S^T) + P D,
-//                  S <- gamma_C S + (kd D)^T K.  Every fp32 operand is split
+//                  chunk: D = U - W S^T, S <- gamma_C S + (kd D)^T K on four
+//                  "chain" waves, O = gq (Q S^T) + P D on four "output" waves.  Every fp32 operand is split
 //                  into fp16 hi + lo and multiplied as hi*hi + hi*lo + lo*hi
 //                  (fp16 operands need no split), which keeps the products at
 //                  about fp32 accuracy on the f16 matrix cores.  The four
@@ -124,10 +124,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
     constexpr int LD = D128 + 8;  // padded fp16 row (bank spread)
     constexpr int LA = CH + 4;    // 16-byte rows: the solve reads A rows as float4 broadcasts
 
+    static_assert(LD * sizeof(half_t) == LA * sizeof(float), "Q rows and A rows share one LDS footprint");
     __shared__ __align__(16) half_t sK[CH][LD];
-    __shared__ __align__(16) half_t sQ[CH][LD];
     __shared__ __align__(16) half_t sV[CH][LD];
-    __shared__ float sA[CH][LA];
+    // Q is dead once Q K^T is formed; the fp32 matrix A reuses its rows
+    // (same 272-byte row stride), which keeps three workgroups per CU.
+    __shared__ __align__(16) char sQA[CH * LD * sizeof(half_t)];
+    half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sQA);
+    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sQA);
     __shared__ float sG[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
 
     const int HV = p.HV, H = p.H;
@@ -147,19 +151,43 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
     const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
     const half_t *__restrict__ v = static_cast<const half_t *>(p.v);
 
-    // ---- chunk rows of K, Q (head qh) and V (head h) -> LDS, zero past the end
-    for (int idx = tid; idx < CH * 16; idx += 256) {
-        const int r = idx >> 4, c8 = (idx & 15) * 8;
-        h8 kk = {}, qq = {}, vv = {};
+    // ---- chunk rows of K, Q (head qh) and V (head h): issue the loads first,
+    // compute the gates while they are in flight, then park them in LDS
+    h8 ldk[4], ldq[4], ldv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        ldk[i] = ldq[i] = ldv[i] = h8{};
         if (r < n) {
             const size_t tq = ((size_t)(t0 + r) * H + qh) * D128 + c8;
-            kk = ld_h8(k + tq);
-            qq = ld_h8(q + tq);
-            vv = ld_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
+            ldk[i] = ld_h8(k + tq);
+            ldq[i] = ld_h8(q + tq);
+            ldv[i] = ld_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
         }
-        *reinterpret_cast<h8 *>(&sK[r][c8]) = kk;
-        *reinterpret_cast<h8 *>(&sQ[r][c8]) = qq;
-        *reinterpret_cast<h8 *>(&sV[r][c8]) = vv;
+    }
+    // ---- per-token log decay (cumulated over the chunk by a 64-lane scan) and update rate
+    if (tid < CH) {
+        const int t = tid;
+        float g = 0.f, bt = 0.f;
+        if (t < n) {
+            const size_t th = (size_t)(t0 + t) * HV + h;
+            if constexpr (DEC) g = log_decay(p, th, h);
+            bt = BETA ? update_rate(p, th) : 1.f;
+        }
+#pragma unroll
+        for (int o = 1; o < CH; o <<= 1) {
+            const float y = __shfl_up(g, o, CH);
+            if (t >= o) g += y;
+        }
+        sG[t] = g;  // inclusive cumulative log decay inside the chunk
+        sBeta[t] = bt;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<h8 *>(&sK[r][c8]) = ldk[i];
+        *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
+        *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
     }
     lds_barrier();
 
@@ -177,66 +205,69 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
         for (int g = 0; g < 4; ++g) dstk[g] = col[g];
     }
 
-    // ---- per-token scalars: log decay, update rate, inverse norms
-    if (tid < CH) {
-        const int t = tid;
-        float g = 0.f, bt = 0.f, ik = 1.f, iq = 1.f;
-        if (t < n) {
-            const size_t th = (size_t)(t0 + t) * HV + h;
-            if constexpr (DEC) g = log_decay(p, th, h);
-            bt = BETA ? update_rate(p, th) : 1.f;
-            if (p.qk_l2_norm) {
-                float ss = 0.f, sq = 0.f;
-                for (int c = 0; c < D128; ++c) {
-                    const float a = (float)sK[t][c], qv = (float)sQ[t][c];
-                    ss = fmaf(a, a, ss);
-                    sq = fmaf(qv, qv, sq);
+    // ---- inverse L2 norms of the chunk's q and k rows: 4 threads per row
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float ss = 0.f, sq = 0.f;
+        if (p.qk_l2_norm) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const h8 kk = ld_h8(&sK[t][32 * part + 8 * g]);
+                const h8 qq = ld_h8(&sQ[t][32 * part + 8 * g]);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    ss = fmaf((float)kk[x], (float)kk[x], ss);
+                    sq = fmaf((float)qq[x], (float)qq[x], sq);
                 }
-                ik = 1.f / sqrtf(ss + 1e-12f);
-                iq = 1.f / sqrtf(sq + 1e-12f);
             }
+            ss += dpp_mov<0xB1>(ss);  // sum over the 4 lanes of the row
+            ss += dpp_mov<0x4E>(ss);
+            sq += dpp_mov<0xB1>(sq);
+            sq += dpp_mov<0x4E>(sq);
         }
-        sG[t] = g;
-        sBeta[t] = bt;
-        sIk[t] = ik;
-        sIq[t] = iq;
-    }
-    lds_barrier();
-    if (tid == 0) {
-        float acc = 0.f;
-        for (int t = 0; t < CH; ++t) {
-            acc += sG[t];
-            sG[t] = acc;  // inclusive cumulative log decay inside the chunk
+        if (part == 0) {
+            const bool on = p.qk_l2_norm && t < n;
+            sIk[t] = on ? 1.f / sqrtf(ss + 1e-12f) : 1.f;
+            sIq[t] = on ? 1.f / sqrtf(sq + 1e-12f) : 1.f;
         }
     }
     lds_barrier();
     if (tid < CH) sRw[tid] = sBeta[tid] * expf(sG[tid]) * sIk[tid];  // row scale of K in the W right-hand side
 
-    // ---- Q K^T -> P (hi, lo) and K K^T -> A, tiles of 16 x 16 (wave = token block)
+    // ---- Q K^T -> P (hi, lo) and K K^T -> A, tiles of 16 x 16 (wave = token block).
+    // Wave tb reads only Q rows of its block and writes only A rows of its
+    // block, so once all its products are formed it may overwrite them.
     const float scale = p.scale;
     {
         const int tb = wave;
         const int lr = lane & 15, lk = (lane >> 4) * 8;
+        f4v accq[4], acck[4];
+#pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
-            f4v accq = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+            accq[sb] = acck[sb] = f4v{0.f, 0.f, 0.f, 0.f};
             if (sb <= tb) {
 #pragma unroll
                 for (int kk = 0; kk < D128; kk += 32) {
                     const h8 bk = ld_h8(&sK[16 * sb + lr][kk + lk]);
-                    accq = mfma16(ld_h8(&sQ[16 * tb + lr][kk + lk]), bk, accq);
-                    if constexpr (RET) acck = mfma16(ld_h8(&sK[16 * tb + lr][kk + lk]), bk, acck);
+                    accq[sb] = mfma16(ld_h8(&sQ[16 * tb + lr][kk + lk]), bk, accq[sb]);
+                    if constexpr (RET) acck[sb] = mfma16(ld_h8(&sK[16 * tb + lr][kk + lk]), bk, acck[sb]);
                 }
             }
+        }
+        // all of this wave's LDS reads of Q must land before its A rows overwrite them
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
             const int s = 16 * sb + lr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * tb + (lane >> 4) * 4 + i;
                 const float dg = (s <= t) ? expf(sG[t] - sG[s]) : 0.f;
-                const float pv = scale * sIq[t] * sIk[s] * dg * accq[i];
+                const float pv = scale * sIq[t] * sIk[s] * dg * accq[sb][i];
                 const half_t hi = (half_t)pv;
                 ws_p[(ch * 2 + 0) * CH * CH + t * CH + s] = hi;
                 ws_p[(ch * 2 + 1) * CH * CH + t * CH + s] = (half_t)(pv - (float)hi);
-                if constexpr (RET) sA[t][s] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[i] : 0.f;
+                if constexpr (RET) sA[t][s] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
             }
         }
     }
@@ -250,10 +281,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
         float x[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
-            float r = wcol ? sRw[t] * (float)sK[t][cc] : sBeta[t] * (float)sV[t][cc];
+            // four independent partial sums keep the FMA pipeline busy
+            float r[4] = {wcol ? sRw[t] * (float)sK[t][cc] : sBeta[t] * (float)sV[t][cc], 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < t; ++s) r = fmaf(-sA[t][s], x[s], r);
-            x[t] = r;
+            for (int s = 0; s < t; ++s) r[s & 3] = fmaf(-sA[t][s], x[s], r[s & 3]);
+            x[t] = (r[0] + r[1]) + (r[2] + r[3]);
         }
         if (wcol) {
 #pragma unroll
@@ -286,13 +318,23 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
 }
 
 // ------------------------------------------------------------------ phase 2
+// 512 threads.  Waves 0-3 carry the state chain of a 32-row tile; waves 4-7
+// compute the outputs from the chain's LDS copies of S and D, so the output
+// work stays off the serial path.  Per chunk j (LDS buffer j & 1):
+//   chain:  A  S (hi, lo) -> sS[b]          | output: -
+//           == barrier 1 ==
+//           B  D = U - W S^T -> sDt[b], and (kd D) -> sDs   | O1 Opre = Q S^T
+//           == barrier 2 ==
+//           E  S <- gamma_C S + (kd D)^T K  | O2 O = gq Opre + P D, store
+// S and D are double-buffered, so a buffer is rewritten only after every
+// output wave has passed the barrier that follows its last read.
+// (no __restrict__ on the operands: loads through restrict pointers may be
+// moved across the prefetch fences below, which would put two prefetches in
+// flight and exhaust the registers)
 template <int RULE>
-__global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_t *__restrict__ off,
-                                                   const half_t *__restrict__ ws_w,
-                                                   const half_t *__restrict__ ws_p,
-                                                   const float *__restrict__ ws_u,
-                                                   const float *__restrict__ ws_s,
-                                                   const half_t *__restrict__ ws_kt)
+__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const half_t *ws_w,
+                                                   const half_t *ws_p, const float *ws_u, const float *ws_s,
+                                                   const half_t *ws_kt)
 {
     constexpr bool RET = rule_retrieves(RULE);
     constexpr int LS = D128 + 8;   // fp16 state row (272 B)
@@ -302,9 +344,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
     // value, and stored as planes; every MFMA fragment is then one 16-byte
     // LDS read.  Row strides of 68 and 36 dwords put the 16 lanes of a
     // 16-byte access phase on 16 distinct 4-bank groups.
-    __shared__ __align__(16) half_t sS[2][TR][LS];    // state tile, hi / lo
-    __shared__ __align__(16) half_t sDt[4][TR][LDT];  // D^T hi / lo, (kd D)^T hi / lo
-    __shared__ float sSc[256];
+    __shared__ __align__(16) half_t sS[2][2][TR][LS];    // [buffer][hi, lo] state tile
+    __shared__ __align__(16) half_t sDt[2][2][TR][LDT];  // [buffer][hi, lo] D^T
+    __shared__ __align__(16) half_t sDs[2][TR][LDT];     // [hi, lo] (kd D)^T, chain only
 
     const int HV = p.HV, H = p.H;
     // XCD-aware order: blocks i, i+8, i+16, i+24 (one XCD) are the 4 tiles of one head
@@ -323,203 +365,217 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const Params p, const int32_
     int64_t rs, re;
     request_range(p, b, rs, re);
     const int c0 = off[b], nch = off[b + 1] - off[b];
-
-    const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
-    const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
-    half_t *__restrict__ o = static_cast<half_t *>(p.o);
-
-    // state tile in accumulator layout: wave owns dv block (wave >> 1), dk blocks 4*(wave & 1) + j
-    const int dvb = wave >> 1, dkb0 = 4 * (wave & 1);
-    f4v Sacc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
-            Sacc[j][i] = src ? src[(size_t)r * D128 + c] : 0.f;
-        }
-
-    // Operands of one chunk, loaded one chunk ahead so their global-memory
-    // latency hides behind the previous chunk's matrix work.  Rows past the
-    // end of the request read as zero.
-    const int tb = wave;          // token block of this wave in steps B and D
+    const int tb = wave & 3;      // token block of this wave in steps B, O1, O2
     const int tr = 16 * tb + lr;  // A-operand row (token) of this lane
-    struct Ops {
-        h8 kt[2][4];              // K^T fragments of the state update: token steps x dk tiles
-        h8 wh[4], wl[4], aq[4];   // W (hi, lo) and Q rows, four k-steps of 32
-        h8 ph[2], pl[2];          // P (hi, lo) rows, two k-steps of 32
-        float u[2][4];            // U at this lane's D-layout positions
-        float kd[4];              // kd of this lane's four D-layout tokens
-        float sc;                 // one per-chunk scalar (threads < 129)
-        int n;                    // valid tokens in the chunk
-        int64_t t0;
-    };
-    // Every load below is unconditional (a branch around a load makes the
-    // compiler wait for it on the spot, which would defeat the prefetch).
-    auto fetch = [&](int jj, Ops &f) {
-        const size_t ch = (size_t)(c0 + jj) * HV + h;
-        f.t0 = rs + (int64_t)jj * CH;
-        f.n = (int)((re - f.t0) < CH ? (re - f.t0) : CH);
+
+    if (wave < 4) {
+        // ================================================================ chain
+        const int dvb = wave >> 1, dkb0 = 4 * (wave & 1);
+        f4v Sacc[4];  // state tile, accumulator layout: rows 16 dvb + 4 lq + i, cols 16 (dkb0 + j) + lr
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
+                Sacc[j][i] = src ? src[(size_t)r * D128 + c] : 0.f;
+            }
+        struct Ops {
+            h8 wh[4], wl[4];  // W (hi, lo) rows of token block tb, four k-steps of 32
+            h8 kt[2][4];      // K^T fragments: token steps x this wave's dk tiles
+            float u[2][4];    // U at this lane's D-layout positions
+            float kd[4];      // kd of this lane's four D-layout tokens
+            float gc;         // gamma_C
+        };
+        // every load unconditional: a branch around a load makes the compiler
+        // wait for it on the spot, which would defeat the prefetch
+        auto fetch = [&](int jj, Ops &f) {
+            const size_t ch = (size_t)(c0 + jj) * HV + h;
+            if constexpr (RET) {
+                const half_t *wh = ws_w + (ch * 2 + 0) * CH * D128 + (size_t)tr * D128;
+                const half_t *wl = ws_w + (ch * 2 + 1) * CH * D128 + (size_t)tr * D128;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    f.wh[kk] = ld_h8(wh + 32 * kk + lk);
+                    f.wl[kk] = ld_h8(wl + 32 * kk + lk);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int jj2 = 0; jj2 < 4; ++jj2)
+                    f.kt[ks][jj2] = ld_h8(ws_kt + ch * D128 * CH + (size_t)(16 * (dkb0 + jj2) + lr) * CH + 32 * ks + lk);
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f.u[vb][i] = ws_u[ch * CH * D128 + (size_t)(16 * tb + 4 * lq + i) * D128 + row0 + 16 * vb + lr];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.kd[i] = ws_s[ch * SC_STRIDE + CH + 16 * tb + 4 * lq + i];
+            f.gc = ws_s[ch * SC_STRIDE + 2 * CH];
+        };
+        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+            const int bf = j & 1;
+            // ---- A: state tile -> LDS (hi, lo)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                f.kt[ks][jj] = ld_h8(ws_kt + ch * D128 * CH + (size_t)(16 * (dkb0 + jj) + lr) * CH + 32 * ks + lk);
-        f.sc = ws_s[ch * SC_STRIDE + (tid < 2 * CH ? tid : 2 * CH)];
-        const half_t *wh = ws_w + (ch * 2 + 0) * CH * D128 + (size_t)tr * D128;
-        const half_t *wl = ws_w + (ch * 2 + 1) * CH * D128 + (size_t)tr * D128;
-        // rows past the request end read its last row; their outputs are never stored
-        const int tq = tr < f.n ? tr : f.n - 1;
-        const half_t *qp = q + ((size_t)(f.t0 + tq) * H + qh) * D128;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            f.aq[kk] = ld_h8(qp + 32 * kk + lk);
-            if constexpr (RET) {
-                f.wh[kk] = ld_h8(wh + 32 * kk + lk);
-                f.wl[kk] = ld_h8(wl + 32 * kk + lk);
-            }
-        }
-        const half_t *ph = ws_p + (ch * 2 + 0) * CH * CH + (size_t)tr * CH;
-        const half_t *pl = ws_p + (ch * 2 + 1) * CH * CH + (size_t)tr * CH;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            f.ph[ks] = ld_h8(ph + 32 * ks + lk);
-            f.pl[ks] = ld_h8(pl + 32 * ks + lk);
-        }
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                f.u[vb][i] = ws_u[ch * CH * D128 + (size_t)(16 * tb + 4 * lq + i) * D128 + row0 + 16 * vb + lr];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f.kd[i] = ws_s[ch * SC_STRIDE + CH + 16 * tb + 4 * lq + i];
-    };
-
-    // one chunk: consumes `cur`, prefetches chunk j + 1 into `nxt`
-    auto step = [&](int j, const Ops &cur, Ops &nxt) {
-        const int64_t t0 = cur.t0;
-        const int n = cur.n;
-        lds_barrier();
-        // ---- A: state tile -> LDS (hi, lo); scalars
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = Sacc[jj][i];
-                const half_t hi = (half_t)x;
-                sS[0][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = hi;
-                sS[1][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = (half_t)(x - (float)hi);
-            }
-        sSc[tid] = cur.sc;  // entries past 2 * CH repeat gamma_C and are not read
-        // next chunk's operands (the last chunk re-reads itself: every lane
-        // issues the same loads on every iteration)
-        fetch(j + 1 < nch ? j + 1 : j, nxt);
-        lds_barrier();
-
-        // ---- B: D = U - W S^T and Opre = Q S^T for token block tb, dv blocks 0, 1
-        f4v accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        f4v accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb) {
-                const h8 shi = ld_h8(&sS[0][16 * vb + lr][32 * kk + lk]);
-                const h8 slo = ld_h8(&sS[1][16 * vb + lr][32 * kk + lk]);
-                if constexpr (RET) {
-                    accD[vb] = mfma16(cur.wh[kk], shi, accD[vb]);
-                    accD[vb] = mfma16(cur.wh[kk], slo, accD[vb]);
-                    accD[vb] = mfma16(cur.wl[kk], shi, accD[vb]);
-                }
-                accO[vb] = mfma16(cur.aq[kk], shi, accO[vb]);
-                accO[vb] = mfma16(cur.aq[kk], slo, accO[vb]);
-            }
-        }
-        // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
-        // tokens per lane -> one 8-byte write per plane of D^T
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-            h4 dh, dl, sh, sl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float d = cur.u[vb][i] - accD[vb][i];
-                const float ds = cur.kd[i] * d;
-                dh[i] = (half_t)d;
-                dl[i] = (half_t)(d - (float)dh[i]);
-                sh[i] = (half_t)ds;
-                sl[i] = (half_t)(ds - (float)sh[i]);
-            }
-            const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
-            *reinterpret_cast<h4 *>(&sDt[0][r][c]) = dh;
-            *reinterpret_cast<h4 *>(&sDt[1][r][c]) = dl;
-            *reinterpret_cast<h4 *>(&sDt[2][r][c]) = sh;
-            *reinterpret_cast<h4 *>(&sDt[3][r][c]) = sl;
-        }
-        lds_barrier();
-
-        // ---- D: O = gq (Q S^T) + P D for token block tb, dv blocks 0, 1
-        {
-            f4v accP[2];
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accP[vb][i] = sSc[16 * tb + 4 * lq + i] * accO[vb][i];
-            // P is lower triangular; the block above the diagonal holds zeros
-            // and is multiplied anyway so that every prefetched fragment is used
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    const h8 dhi = ld_h8(&sDt[0][16 * vb + lr][32 * ks + lk]);
-                    const h8 dlo = ld_h8(&sDt[1][16 * vb + lr][32 * ks + lk]);
-                    accP[vb] = mfma16(cur.ph[ks], dhi, accP[vb]);
-                    accP[vb] = mfma16(cur.ph[ks], dlo, accP[vb]);
-                    accP[vb] = mfma16(cur.pl[ks], dhi, accP[vb]);
-                }
-            }
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * lq + i;
-                    if (t < n) o[((size_t)(t0 + t) * HV + h) * D128 + row0 + 16 * vb + lr] = (half_t)accP[vb][i];
+                    const float x = Sacc[jj][i];
+                    const half_t hi = (half_t)x;
+                    sS[bf][0][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = hi;
+                    sS[bf][1][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = (half_t)(x - (float)hi);
                 }
-        }
-
-        // ---- E: S <- gamma_C S + (kd D)^T K for the wave's 4 state tiles
-        {
-            const float gC = sSc[2 * CH];
+            fetch(j + 1 < nch ? j + 1 : j, nxt);  // the last chunk re-reads itself
+            // keep the prefetch where it is: neither the optimiser nor the
+            // scheduler may move the loads past this point in either direction
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // 1
+            // ---- B: D = U - W S^T for token block tb, state-row blocks 0, 1
+            f4v accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            if constexpr (RET) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int vb = 0; vb < 2; ++vb) {
+                        const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
+                        const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                        accD[vb] = mfma16(cur.wh[kk], shi, accD[vb]);
+                        accD[vb] = mfma16(cur.wh[kk], slo, accD[vb]);
+                        accD[vb] = mfma16(cur.wl[kk], shi, accD[vb]);
+                    }
+            }
+            // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
+            // tokens per lane -> one 8-byte write per plane
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb) {
+                h4 dh, dl, sh, sl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d = cur.u[vb][i] - accD[vb][i];
+                    const float ds = cur.kd[i] * d;
+                    dh[i] = (half_t)d;
+                    dl[i] = (half_t)(d - (float)dh[i]);
+                    sh[i] = (half_t)ds;
+                    sl[i] = (half_t)(ds - (float)sh[i]);
+                }
+                const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
+                *reinterpret_cast<h4 *>(&sDt[bf][0][r][c]) = dh;
+                *reinterpret_cast<h4 *>(&sDt[bf][1][r][c]) = dl;
+                *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
+                *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
+            }
+            lds_barrier();  // 2
+            // ---- E: S <- gamma_C S + (kd D)^T K for the wave's 4 state tiles
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Sacc[jj][i] *= gC;
+                for (int i = 0; i < 4; ++i) Sacc[jj][i] *= cur.gc;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const h8 dhi = ld_h8(&sDt[2][16 * dvb + lr][32 * ks + lk]);
-                const h8 dlo = ld_h8(&sDt[3][16 * dvb + lr][32 * ks + lk]);
+                const h8 dhi = ld_h8(&sDs[0][16 * dvb + lr][32 * ks + lk]);
+                const h8 dlo = ld_h8(&sDs[1][16 * dvb + lr][32 * ks + lk]);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     Sacc[jj] = mfma16(dhi, cur.kt[ks][jj], Sacc[jj]);
                     Sacc[jj] = mfma16(dlo, cur.kt[ks][jj], Sacc[jj]);
                 }
             }
+        };
+        // two operand sets used in turn, so no register copy waits on a prefetch
+        Ops opa, opb;
+        if (nch > 0) fetch(0, opa);
+        for (int j = 0; j < nch; j += 2) {
+            step(j, opa, opb);
+            if (j + 1 < nch) step(j + 1, opb, opa);
         }
-    };
-
-    // two operand sets used in turn, so no register copy waits on a prefetch
-    Ops opa, opb;
-    if (nch > 0) fetch(0, opa);
-    for (int j = 0; j < nch; j += 2) {
-        step(j, opa, opb);
-        if (j + 1 < nch) step(j + 1, opb, opa);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
+                dst[(size_t)r * D128 + c] = Sacc[j][i];
+            }
+    } else {
+        // ================================================================ outputs
+        const half_t *q = static_cast<const half_t *>(p.q);
+        half_t *o = static_cast<half_t *>(p.o);
+        struct Ops {
+            h8 aq[4];          // Q rows of token block tb, four k-steps of 32
+            h8 ph[2], pl[2];   // P (hi, lo) rows, two k-steps of 32
+            float gq[4];       // gq of this lane's four D-layout tokens
+            int n;             // valid tokens in the chunk
+            int64_t t0;
+        };
+        auto fetch = [&](int jj, Ops &f) {
+            const size_t ch = (size_t)(c0 + jj) * HV + h;
+            f.t0 = rs + (int64_t)jj * CH;
+            f.n = (int)((re - f.t0) < CH ? (re - f.t0) : CH);
+            // rows past the request end read its last row; their outputs are not stored
+            const int tq = tr < f.n ? tr : f.n - 1;
+            const half_t *qp = q + ((size_t)(f.t0 + tq) * H + qh) * D128;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.aq[kk] = ld_h8(qp + 32 * kk + lk);
+            const half_t *ph = ws_p + (ch * 2 + 0) * CH * CH + (size_t)tr * CH;
+            const half_t *pl = ws_p + (ch * 2 + 1) * CH * CH + (size_t)tr * CH;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f.ph[ks] = ld_h8(ph + 32 * ks + lk);
+                f.pl[ks] = ld_h8(pl + 32 * ks + lk);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.gq[i] = ws_s[ch * SC_STRIDE + 16 * tb + 4 * lq + i];
+        };
+        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+            const int bf = j & 1;
+            fetch(j + 1 < nch ? j + 1 : j, nxt);
+            asm volatile("" ::: "memory");  // pin the prefetch (see the chain role)
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // 1
+            // ---- O1: Opre = Q S^T for token block tb, state-row blocks 0, 1
+            f4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
+                    const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                    acc[vb] = mfma16(cur.aq[kk], shi, acc[vb]);
+                    acc[vb] = mfma16(cur.aq[kk], slo, acc[vb]);
+                }
+            lds_barrier();  // 2
+            // ---- O2: O = gq Opre + P D; P is lower triangular (zeros above the
+            // diagonal are multiplied anyway so every prefetched fragment is used)
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[vb][i] *= cur.gq[i];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][32 * ks + lk]);
+                    const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][32 * ks + lk]);
+                    acc[vb] = mfma16(cur.ph[ks], dhi, acc[vb]);
+                    acc[vb] = mfma16(cur.ph[ks], dlo, acc[vb]);
+                    acc[vb] = mfma16(cur.pl[ks], dhi, acc[vb]);
+                }
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * lq + i;
+                    if (t < cur.n)
+                        o[((size_t)(cur.t0 + t) * HV + h) * D128 + row0 + 16 * vb + lr] = (half_t)acc[vb][i];
+                }
+        };
+        Ops opa, opb;
+        if (nch > 0) fetch(0, opa);
+        for (int j = 0; j < nch; j += 2) {
+            step(j, opa, opb);
+            if (j + 1 < nch) step(j + 1, opb, opa);
+        }
     }
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
-            dst[(size_t)r * D128 + c] = Sacc[j][i];
-        }
 }
 
 // ------------------------------------------------------------------ host side
@@ -552,7 +608,7 @@ static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
     const int64_t nbh = (int64_t)p.B * p.HV;
     const int64_t blocks = (nbh + 7) / 8 * 8 * NTILE;
     if (blocks > 0)
-        hipLaunchKernelGGL((k_chunk_scan<RULE>), dim3((unsigned)blocks), dim3(256), 0, s, p, off, ws_w, ws_p, ws_u,
+        hipLaunchKernelGGL((k_chunk_scan<RULE>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, ws_w, ws_p, ws_u,
                            ws_s, ws_kt);
     return hipGetLastError();
 }
