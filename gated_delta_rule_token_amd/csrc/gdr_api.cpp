@@ -177,13 +177,13 @@ int32_t pick_algo(const gdr_problem *p)
 
 int dk_tile(int dk) { return dk <= 32 ? 32 : dk <= 64 ? 64 : dk <= 128 ? 128 : 256; }
 
-// rows per workgroup = 16 * g: enough workgroups to fill the machine while
-// amortising the per-token staging over as many rows as possible
+// rows per workgroup = 16 * g.  Measured on MI355X (dv = 128): g = 2 beats
+// g = 4 (more workgroups per CU to hide the token loop's latency) and g = 1
+// (per-token staging amortised over too few rows) on both the varlen and the
+// per-key workloads.
 int rows_group(const gdr_problem *p)
 {
-    if (p->head_dim_v <= 16) return 1;
-    if (p->head_dim_v <= 32) return 2;
-    return 4;
+    return p->head_dim_v <= 16 ? 1 : 2;
 }
 
 }  // namespace

@@ -295,15 +295,19 @@ __global__ __launch_bounds__(256) void k_chunk_prep(const Params p, const int32_
                 ws_w[(ch * 2 + 1) * CH * D128 + t * D128 + cc] = (half_t)(x[t] - (float)hi);
             }
         } else {
+            // U^T: state row cc, 64 tokens, written as 16-byte vectors
+            f4v *ut = reinterpret_cast<f4v *>(ws_u + ch * CH * D128 + (size_t)cc * CH);
 #pragma unroll
-            for (int t = 0; t < CH; ++t) ws_u[ch * CH * D128 + t * D128 + cc] = x[t];
+            for (int t = 0; t < CH; t += 4) ut[t / 4] = f4v{x[t], x[t + 1], x[t + 2], x[t + 3]};
         }
     } else {
-        // no retrieval: D = V
-        for (int idx = tid; idx < CH * D128; idx += 256) {
-            const int t = idx / D128, c = idx % D128;
-            ws_u[ch * CH * D128 + idx] = (float)sV[t][c];
-        }
+        // no retrieval: D = V, stored transposed like U
+        const int c = tid & (D128 - 1), half = tid >> 7;
+        f4v *ut = reinterpret_cast<f4v *>(ws_u + ch * CH * D128 + (size_t)c * CH + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 32; t += 4)
+            ut[t / 4] = f4v{(float)sV[32 * half + t][c], (float)sV[32 * half + t + 1][c], (float)sV[32 * half + t + 2][c],
+                            (float)sV[32 * half + t + 3][c]};
     }
 
     // ---- per-token scalars for the scan
@@ -370,20 +374,26 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 
     if (wave < 4) {
         // ================================================================ chain
-        const int dvb = wave >> 1, dkb0 = 4 * (wave & 1);
-        f4v Sacc[4];  // state tile, accumulator layout: rows 16 dvb + 4 lq + i, cols 16 (dkb0 + j) + lr
+        // the wave owns key-column tiles 2 wave and 2 wave + 1 of both 16-row
+        // blocks: Sacc[2 vb + jj] holds rows 16 vb + 4 lq + i, columns
+        // 16 (2 wave + jj) + lr (accumulator layout); distinct waves need
+        // distinct K^T fragments
+        const int dkb0 = 2 * wave;
+        f4v Sacc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
-                Sacc[j][i] = src ? src[(size_t)r * D128 + c] : 0.f;
-            }
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = row0 + 16 * vb + 4 * lq + i, c = 16 * (dkb0 + jj) + lr;
+                    Sacc[2 * vb + jj][i] = src ? src[(size_t)r * D128 + c] : 0.f;
+                }
         struct Ops {
             h8 wh[4], wl[4];  // W (hi, lo) rows of token block tb, four k-steps of 32
-            h8 kt[2][4];      // K^T fragments: token steps x this wave's dk tiles
-            float u[2][4];    // U at this lane's D-layout positions
-            float kd[4];      // kd of this lane's four D-layout tokens
+            h8 kt[2][2];      // K^T fragments: token steps x this wave's two dk tiles
+            f4v u[2];         // U at this lane's D-layout positions (four tokens each)
+            f4v kd;           // kd of this lane's four D-layout tokens
             float gc;         // gamma_C
         };
         // every load unconditional: a branch around a load makes the compiler
@@ -402,48 +412,55 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int jj2 = 0; jj2 < 4; ++jj2)
+                for (int jj2 = 0; jj2 < 2; ++jj2)
                     f.kt[ks][jj2] = ld_h8(ws_kt + ch * D128 * CH + (size_t)(16 * (dkb0 + jj2) + lr) * CH + 32 * ks + lk);
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    f.u[vb][i] = ws_u[ch * CH * D128 + (size_t)(16 * tb + 4 * lq + i) * D128 + row0 + 16 * vb + lr];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) f.kd[i] = ws_s[ch * SC_STRIDE + CH + 16 * tb + 4 * lq + i];
+                f.u[vb] = *reinterpret_cast<const f4v *>(ws_u + ch * CH * D128 + (size_t)(row0 + 16 * vb + lr) * CH +
+                                                          16 * tb + 4 * lq);
+            f.kd = *reinterpret_cast<const f4v *>(ws_s + ch * SC_STRIDE + CH + 16 * tb + 4 * lq);
             f.gc = ws_s[ch * SC_STRIDE + 2 * CH];
         };
         auto step = [&](int j, const Ops &cur, Ops &nxt) {
             const int bf = j & 1;
             // ---- A: state tile -> LDS (hi, lo)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
+            for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = Sacc[jj][i];
-                    const half_t hi = (half_t)x;
-                    sS[bf][0][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = hi;
-                    sS[bf][1][16 * dvb + 4 * lq + i][16 * (dkb0 + jj) + lr] = (half_t)(x - (float)hi);
-                }
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = Sacc[2 * vb + jj][i];
+                        const half_t hi = (half_t)x;
+                        sS[bf][0][16 * vb + 4 * lq + i][16 * (dkb0 + jj) + lr] = hi;
+                        sS[bf][1][16 * vb + 4 * lq + i][16 * (dkb0 + jj) + lr] = (half_t)(x - (float)hi);
+                    }
             fetch(j + 1 < nch ? j + 1 : j, nxt);  // the last chunk re-reads itself
             // keep the prefetch where it is: neither the optimiser nor the
             // scheduler may move the loads past this point in either direction
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();  // 1
-            // ---- B: D = U - W S^T for token block tb, state-row blocks 0, 1
-            f4v accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            if constexpr (RET) {
+            // ---- B: D = U - W S^T for token block tb, state-row blocks 0, 1.
+            // The three split products accumulate separately: six independent
+            // MFMA chains of four instead of two chains of twelve.
+            f4v accD[2];
+            {
+                f4v a3[2][3] = {};
+                if constexpr (RET) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                    for (int vb = 0; vb < 2; ++vb) {
-                        const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
-                        const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
-                        accD[vb] = mfma16(cur.wh[kk], shi, accD[vb]);
-                        accD[vb] = mfma16(cur.wh[kk], slo, accD[vb]);
-                        accD[vb] = mfma16(cur.wl[kk], shi, accD[vb]);
-                    }
+                        for (int vb = 0; vb < 2; ++vb) {
+                            const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
+                            const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                            a3[vb][0] = mfma16(cur.wh[kk], shi, a3[vb][0]);
+                            a3[vb][1] = mfma16(cur.wh[kk], slo, a3[vb][1]);
+                            a3[vb][2] = mfma16(cur.wl[kk], shi, a3[vb][2]);
+                        }
+                }
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) accD[vb] = a3[vb][0] + (a3[vb][1] + a3[vb][2]);
             }
             // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
             // tokens per lane -> one 8-byte write per plane
@@ -471,15 +488,22 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Sacc[jj][i] *= cur.gc;
+            {
+                f4v lo4[4] = {};  // lo products in their own chains
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const h8 dhi = ld_h8(&sDs[0][16 * dvb + lr][32 * ks + lk]);
-                const h8 dlo = ld_h8(&sDs[1][16 * dvb + lr][32 * ks + lk]);
+                for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    Sacc[jj] = mfma16(dhi, cur.kt[ks][jj], Sacc[jj]);
-                    Sacc[jj] = mfma16(dlo, cur.kt[ks][jj], Sacc[jj]);
-                }
+                    for (int vb = 0; vb < 2; ++vb) {
+                        const h8 dhi = ld_h8(&sDs[0][16 * vb + lr][32 * ks + lk]);
+                        const h8 dlo = ld_h8(&sDs[1][16 * vb + lr][32 * ks + lk]);
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            Sacc[2 * vb + jj] = mfma16(dhi, cur.kt[ks][jj], Sacc[2 * vb + jj]);
+                            lo4[2 * vb + jj] = mfma16(dlo, cur.kt[ks][jj], lo4[2 * vb + jj]);
+                        }
+                    }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) Sacc[jj] += lo4[jj];
             }
         };
         // two operand sets used in turn, so no register copy waits on a prefetch
@@ -490,12 +514,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             if (j + 1 < nch) step(j + 1, opb, opa);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = row0 + 16 * dvb + 4 * lq + i, c = 16 * (dkb0 + j) + lr;
-                dst[(size_t)r * D128 + c] = Sacc[j][i];
-            }
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = row0 + 16 * vb + 4 * lq + i, c = 16 * (dkb0 + jj) + lr;
+                    dst[(size_t)r * D128 + c] = Sacc[2 * vb + jj][i];
+                }
     } else {
         // ================================================================ outputs
         const half_t *q = static_cast<const half_t *>(p.q);
@@ -503,7 +529,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         struct Ops {
             h8 aq[4];          // Q rows of token block tb, four k-steps of 32
             h8 ph[2], pl[2];   // P (hi, lo) rows, two k-steps of 32
-            float gq[4];       // gq of this lane's four D-layout tokens
+            f4v gq;            // gq of this lane's four D-layout tokens
             int n;             // valid tokens in the chunk
             int64_t t0;
         };
@@ -523,8 +549,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 f.ph[ks] = ld_h8(ph + 32 * ks + lk);
                 f.pl[ks] = ld_h8(pl + 32 * ks + lk);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) f.gq[i] = ws_s[ch * SC_STRIDE + 16 * tb + 4 * lq + i];
+            f.gq = *reinterpret_cast<const f4v *>(ws_s + ch * SC_STRIDE + 16 * tb + 4 * lq);
         };
         auto step = [&](int j, const Ops &cur, Ops &nxt) {
             const int bf = j & 1;
@@ -533,7 +558,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();  // 1
             // ---- O1: Opre = Q S^T for token block tb, state-row blocks 0, 1
-            f4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f4v acc[2], acl[2] = {};
+            acc[0] = acc[1] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -541,7 +567,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
                     const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
                     acc[vb] = mfma16(cur.aq[kk], shi, acc[vb]);
-                    acc[vb] = mfma16(cur.aq[kk], slo, acc[vb]);
+                    acl[vb] = mfma16(cur.aq[kk], slo, acl[vb]);
                 }
             lds_barrier();  // 2
             // ---- O2: O = gq Opre + P D; P is lower triangular (zeros above the
@@ -549,17 +575,22 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[vb][i] *= cur.gq[i];
+                for (int i = 0; i < 4; ++i) acc[vb][i] = cur.gq[i] * (acc[vb][i] + acl[vb][i]);
+            {
+                f4v p3[2][2] = {};  // the two lo products in their own chains
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+                for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][32 * ks + lk]);
-                    const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][32 * ks + lk]);
-                    acc[vb] = mfma16(cur.ph[ks], dhi, acc[vb]);
-                    acc[vb] = mfma16(cur.ph[ks], dlo, acc[vb]);
-                    acc[vb] = mfma16(cur.pl[ks], dhi, acc[vb]);
-                }
+                    for (int vb = 0; vb < 2; ++vb) {
+                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][32 * ks + lk]);
+                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][32 * ks + lk]);
+                        acc[vb] = mfma16(cur.ph[ks], dhi, acc[vb]);
+                        p3[vb][0] = mfma16(cur.ph[ks], dlo, p3[vb][0]);
+                        p3[vb][1] = mfma16(cur.pl[ks], dhi, p3[vb][1]);
+                    }
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) acc[vb] += p3[vb][0] + p3[vb][1];
+            }
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
