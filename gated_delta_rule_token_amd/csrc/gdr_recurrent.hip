@@ -17,7 +17,8 @@
 //   form the gate / update rate / per-key vectors in fp32 (the fused
 //   prologue), and park everything in LDS; then each wave runs the serial
 //   token loop on its rows from LDS, writing o into an LDS tile that is
-//   stored coalesced after the block.
+//   stored coalesced at the start of the next block.  A block's raw inputs
+//   are loaded into registers while the previous block runs its loop.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
     __shared__ __align__(16) float s_q[NB][DKT];   // normalised q (times alpha on the VD path)
     __shared__ __align__(16) float s_kb[VD ? NB : 1][DKT];  // erase * alpha * k
     __shared__ __align__(16) float s_a[VD ? NB : 1][DKT];   // alpha per key column
-    __shared__ float s_sc[NB][4];                  // alpha (scalar), beta, q.k
+    __shared__ float s_sc[NB][4];                  // alpha (scalar), beta, q.k, raw gate
     __shared__ float s_v[NB][ROWS];
     __shared__ float s_o[NB][ROWS];
 
@@ -82,29 +83,81 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
             }
     }
 
-    for (int64_t t0 = s; t0 < e; t0 += NB) {
-        const int nb = (int)((e - t0) < NB ? (e - t0) : NB);
-        __syncthreads();
-
-        // ---- A: q/k of the block, L2 norms, q.k, per-key decay vectors
-        for (int task = tid; task < NB * 16; task += NT) {
-            const int tau = task >> 4, c16 = task & 15;
-            const int col0 = c16 * C;
-            const int64_t t = t0 + tau;
-            float qv[C], kv[C];
-            if (tau < nb) {
-                const TA *qp = q + ((size_t)t * H + qh) * dk + col0;
-                const TA *kp = k + ((size_t)t * H + qh) * dk + col0;
-                if (fullk) {
-                    load_act<TA, C>(qp, qv);
-                    load_act<TA, C>(kp, kv);
-                } else {
-                    load_act_masked<TA, C>(qp, dk - col0, qv);
-                    load_act_masked<TA, C>(kp, dk - col0, kv);
-                }
-            } else {
+    // The inputs of a token block are loaded into registers one block ahead
+    // (while the previous block runs its token loop) and turned into the LDS
+    // operands afterwards, so global-memory latency overlaps the serial loop.
+    // Every load is unconditional: token and column indices are clamped into
+    // the request / row, and the staging step zeroes what lies outside.
+    constexpr int NTA = NB * 16 / NT;                 // (token, 16-lane column chunk) tasks per thread
+    constexpr int NTC = (NB * ROWS + NT - 1) / NT;    // value-channel tasks per thread
+    // raw chunks as vector types, so each is one (or two) 16-byte loads into
+    // consecutive registers
+    typedef TA AV __attribute__((ext_vector_type(C), aligned(sizeof(TA) * C < 16 ? sizeof(TA) * C : 16)));
+    typedef float FV __attribute__((ext_vector_type(C), aligned(4 * C < 16 ? 4 * C : 16)));
+    struct Raw {
+        AV q[NTA], k[NTA];
+        FV dec[VD && PK ? NTA : 1];            // per-key log decay
+        FV er[RULE == GATED_DELTA_V2 ? NTA : 1];  // erase gate
+        TA v[NTC];
+        float g, bt;  // raw per-token gate and update rate (tid < NB)
+    };
+    const int64_t tlast = e - 1;
+    auto tok = [&](int64_t t) { return t < tlast ? t : tlast; };
+    auto load_raw = [&](int64_t tb0, Raw &r) {
 #pragma unroll
-                for (int c = 0; c < C; ++c) qv[c] = kv[c] = 0.f;
+        for (int i = 0; i < NTA; ++i) {
+            const int task = tid + NT * i, tau = task >> 4, col0 = (task & 15) * C;
+            const int64_t t = tok(tb0 + tau);
+            const TA *qp = q + ((size_t)t * H + qh) * dk;
+            const TA *kp = k + ((size_t)t * H + qh) * dk;
+            const size_t th = (size_t)t * HV + h;
+            if (fullk) {
+                // whole chunks: vector loads (rows and chunks are 16-byte aligned)
+                r.q[i] = *reinterpret_cast<const AV *>(qp + col0);
+                r.k[i] = *reinterpret_cast<const AV *>(kp + col0);
+                if constexpr (VD && PK) r.dec[i] = *reinterpret_cast<const FV *>(static_cast<const float *>(p.gate) + th * dk + col0);
+                if constexpr (RULE == GATED_DELTA_V2) r.er[i] = *reinterpret_cast<const FV *>(p.erase + th * dk + col0);
+            } else {
+                // partial key rows: element loads with the column clamped into the row
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const int col = col0 + c < dk ? col0 + c : dk - 1;
+                    r.q[i][c] = qp[col];
+                    r.k[i][c] = kp[col];
+                    if constexpr (VD && PK) r.dec[i][c] = static_cast<const float *>(p.gate)[th * dk + col];
+                    if constexpr (RULE == GATED_DELTA_V2) r.er[i][c] = p.erase[th * dk + col];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTC; ++i) {
+            const int task = tid + NT * i, tau = task / ROWS, rr = task % ROWS;
+            const int row = row0 + rr < dv ? row0 + rr : dv - 1;
+            r.v[i] = v[((size_t)tok(tb0 + (tau < NB ? tau : NB - 1)) * HV + h) * dv + row];
+        }
+        // every thread reads a token's scalars (threads past NB re-read the
+        // block's last one), so no load sits behind a divergent branch
+        r.g = 0.f;
+        r.bt = 1.f;
+        {
+            const size_t th = (size_t)tok(tb0 + (tid < NB ? tid : NB - 1)) * HV + h;
+            if constexpr (DEC && (!VD || !PK)) r.g = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[th])
+                                                                 : static_cast<const float *>(p.gate)[th];
+            if constexpr (BETA) r.bt = p.beta[th];
+        }
+    };
+    // LDS operands of the block starting at tb0 (nb valid tokens) from its raw inputs
+    auto stage = [&](int nb, const Raw &r) {
+#pragma unroll
+        for (int i = 0; i < NTA; ++i) {
+            const int task = tid + NT * i, tau = task >> 4, col0 = (task & 15) * C;
+            const bool live = tau < nb;
+            float qv[C], kv[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const bool in = live && col0 + c < dk;
+                qv[c] = in ? to_f32((TA)r.q[i][c]) : 0.f;
+                kv[c] = in ? to_f32((TA)r.k[i][c]) : 0.f;
             }
             float qss = 0.f, kss = 0.f, qk = 0.f;
 #pragma unroll
@@ -124,15 +177,19 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 kv[c] *= ink;
             }
             if constexpr (VD) {
+                // per-key decay: the per-key log decay, or the token's scalar one
+                // broadcast over the keys
+                float gs = 0.f;
+                if constexpr (!PK) gs = p.gate_qwen ? -expf(p.a_log[h]) * softplus_f32(s_sc[tau][3] + p.dt_bias[h])
+                                                    : s_sc[tau][3];
                 float av[C], kb[C];
-                const size_t th = (size_t)t * HV + h;
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const int col = col0 + c;
+                    const bool in = live && col0 + c < dk;
                     float a = 1.f, er = 1.f;
-                    if (tau < nb && col < dk) {
-                        a = expf(PK ? static_cast<const float *>(p.gate)[th * dk + col] : log_decay(p, th, h));
-                        if constexpr (RULE == GATED_DELTA_V2) er = p.erase[th * dk + col];
+                    if (in) {
+                        a = expf(PK ? r.dec[i][c] : gs);
+                        if constexpr (RULE == GATED_DELTA_V2) er = r.er[i][c];
                     }
                     av[c] = a;
                     kb[c] = er * a * kv[c];
@@ -149,28 +206,47 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 s_k[tau][col0 + c] = kv[c];
                 s_q[tau][col0 + c] = qv[c];
             }
-            if (c16 == 0) s_sc[tau][2] = qk * inq * ink;
+            if ((task & 15) == 0) s_sc[tau][2] = qk * inq * ink;
         }
+#pragma unroll
+        for (int i = 0; i < NTC; ++i) {
+            const int task = tid + NT * i, tau = task / ROWS, rr = task % ROWS;
+            if (task < NB * ROWS) s_v[tau][rr] = (tau < nb && row0 + rr < dv) ? to_f32(r.v[i]) : 0.f;
+        }
+    };
 
-        // ---- B: per-token scalar gate and update rate (fp32)
+    const int nblk = (int)((e - s + NB - 1) / NB);
+    Raw ra, rb;
+    if (nblk > 0) load_raw(s, ra);
+    // one block: its scalars and operands, then the token loop; the o tile of
+    // the previous block is stored at the start (after the barrier that
+    // follows its loop)
+    auto block = [&](int n, const Raw &cur, Raw &nxt) {
+        const int64_t t0 = s + (int64_t)n * NB;
+        const int nb = (int)((e - t0) < NB ? (e - t0) : NB);
+        __syncthreads();  // the previous block's loop is done with LDS
+        if (n > 0) {
+            const int64_t tp = t0 - NB;
+            for (int task = tid; task < NB * ROWS; task += NT) {
+                const int tau = task / ROWS, rr = task % ROWS, row = row0 + rr;
+                if (row < dv) o[((size_t)(tp + tau) * HV + h) * dv + row] = from_f32<TA>(s_o[tau][rr]);
+            }
+        }
+        // per-token scalar gate (the raw value parked in column 3 for the
+        // per-key staging of a scalar decay) and update rate
         if (tid < NB) {
-            float a = 1.f, bb = 1.f;
+            float a = 1.f, bb = 1.f, graw = cur.g;
             if (tid < nb) {
-                const size_t th = (size_t)(t0 + tid) * HV + h;
-                if constexpr (DEC && !VD) a = expf(log_decay(p, th, h));
-                if constexpr (BETA) bb = update_rate(p, th);
+                if constexpr (DEC && !VD) a = expf(p.gate_qwen ? -expf(p.a_log[h]) * softplus_f32(graw + p.dt_bias[h]) : graw);
+                if constexpr (BETA) bb = p.beta_sigmoid ? sigmoid_f32(cur.bt) : cur.bt;
             }
             s_sc[tid][0] = a;
             s_sc[tid][1] = bb;
+            s_sc[tid][3] = graw;
         }
-
-        // ---- C: value channels of this tile
-        for (int task = tid; task < NB * ROWS; task += NT) {
-            const int tau = task / ROWS, rr = task % ROWS, row = row0 + rr;
-            float val = 0.f;
-            if (tau < nb && row < dv) val = to_f32(v[((size_t)(t0 + tau) * HV + h) * dv + row]);
-            s_v[tau][rr] = val;
-        }
+        if constexpr (VD && !PK) __syncthreads();  // the raw scalar gate feeds the staging below
+        stage(nb, cur);
+        if (n + 1 < nblk) load_raw(t0 + NB, nxt);
         __syncthreads();
 
         // ---- serial token loop on the register-resident rows
@@ -218,12 +294,19 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 if (l16 == 0) s_o[tau][rl] = p.scale * (u + qk * cc);
             }
         }
+    };
+    for (int n = 0; n < nblk; n += 2) {
+        block(n, ra, rb);
+        if (n + 1 < nblk) block(n + 1, rb, ra);
+    }
+    // ---- o tile of the last block
+    if (nblk > 0) {
         __syncthreads();
-
-        // ---- o tile of the block -> global (act dtype, round to nearest even)
+        const int64_t tp = s + (int64_t)(nblk - 1) * NB;
+        const int nb = (int)(e - tp);
         for (int task = tid; task < NB * ROWS; task += NT) {
             const int tau = task / ROWS, rr = task % ROWS, row = row0 + rr;
-            if (tau < nb && row < dv) o[((size_t)(t0 + tau) * HV + h) * dv + row] = from_f32<TA>(s_o[tau][rr]);
+            if (tau < nb && row < dv) o[((size_t)(tp + tau) * HV + h) * dv + row] = from_f32<TA>(s_o[tau][rr]);
         }
     }
 
