@@ -382,6 +382,27 @@ def pin_chunked_equivalence(fwd):
             o_c, s_c = forward_chunked(q, k, v, chunk_size=c, **kw)
             _close(o_c, o_ref, 1e-10, "chunked %s C=%d o" % (rule, c))
             _close(s_c, s_ref, 1e-10, "chunked %s C=%d state" % (rule, c))
+    # per-key-channel decay (Ascend Formula) and the key-axis erase gate of
+    # Gated DeltaNet-2, with the raw-gate arm on a per-key gate as well
+    gk = -r.uniform(0, 2, (T, HV, DK))
+    erase = r.uniform(0, 1, (T, HV, DK))
+    raw = r.standard_normal((T, HV, DK))
+    a_log, dt_bias = np.log(r.uniform(1, 16, HV)), r.uniform(0, 1, HV)
+    cases = [
+        ("gated_delta per-key", dict(update_rule="gated_delta", gate=gk, beta=beta)),
+        ("gated per-key", dict(update_rule="gated", gate=gk)),
+        ("gated_delta_v2 per-key", dict(update_rule="gated_delta_v2", gate=gk, erase=erase)),
+        ("gated_delta_v2 per-head", dict(update_rule="gated_delta_v2", gate=g, erase=erase)),
+        ("gated_delta per-key qwen", dict(update_rule="gated_delta", gate=raw, beta=beta,
+                                          gate_activation="qwen", a_log=a_log, dt_bias=dt_bias)),
+    ]
+    for name, kw in cases:
+        kw.update(initial_state=S0, cu_seqlens=cu)
+        o_ref, s_ref = fwd(q, k, v, **kw)
+        for c in (1, 3, 16, 64):
+            o_c, s_c = forward_chunked(q, k, v, chunk_size=c, **kw)
+            _close(o_c, o_ref, 1e-10, "chunked %s C=%d o" % (name, c))
+            _close(s_c, s_ref, 1e-10, "chunked %s C=%d state" % (name, c))
 
 
 def pin_kmajor_cross(fwd):
