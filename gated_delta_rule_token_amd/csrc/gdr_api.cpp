@@ -41,11 +41,16 @@ bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.h
 // Number of state rows (batch or slab) the final_state buffer holds.
 int64_t state_rows(const gdr_problem *p) { return p->num_slots > 0 ? p->num_slots : p->batch; }
 
-// Shapes the chunk-parallel kernels implement.
+// Shapes the chunk-parallel kernels implement (every rule; a per-key decay
+// and the erase gate take the per-key form).
+bool chunked_per_key(const gdr_problem *p)
+{
+    return p->decay_per_key != 0 || p->update_rule == GDR_RULE_GATED_DELTA_V2;
+}
+
 bool chunked_ok(const gdr_problem *p)
 {
-    return p->head_dim_k == 128 && p->head_dim_v == 128 && p->act_dtype == GDR_F16 && !p->decay_per_key &&
-           p->update_rule != GDR_RULE_GATED_DELTA_V2;
+    return p->head_dim_k == 128 && p->head_dim_v == 128 && p->act_dtype == GDR_F16;
 }
 
 gdr_status check_problem(const gdr_problem *p)
@@ -85,8 +90,7 @@ gdr_status check_problem(const gdr_problem *p)
     if (p->algo == GDR_ALGO_DECODE && (p->head_dim_k != 128 || p->head_dim_v != 128))
         return fail(GDR_E_UNSUPPORTED, "the decode kernel needs dk = dv = 128");
     if (p->algo == GDR_ALGO_CHUNKED && !chunked_ok(p))
-        return fail(GDR_E_UNSUPPORTED, "the chunked kernels need dk = dv = 128, fp16 activations, a per-head "
-                                       "decay and an update rule other than gated_delta_v2");
+        return fail(GDR_E_UNSUPPORTED, "the chunked kernels need dk = dv = 128 and fp16 activations");
     return GDR_OK;
 }
 
@@ -222,7 +226,8 @@ gdr_status gdr_workspace_size(const gdr_problem *problem, size_t *bytes)
     gdr_status st = check_problem(problem);
     if (st != GDR_OK) return st;
     *bytes = pick_algo(problem) == GDR_ALGO_CHUNKED
-                 ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_v)
+                 ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_v,
+                                                               chunked_per_key(problem))
                  : 0;
     return GDR_OK;
 }
@@ -286,7 +291,7 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     hipError_t err;
     switch (pick_algo(problem)) {
     case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, f16, s); break;
-    case GDR_ALGO_CHUNKED: err = gdr::launch_chunked(k, p.update_rule, workspace, s); break;
+    case GDR_ALGO_CHUNKED: err = gdr::launch_chunked(k, p.update_rule, pk, workspace, s); break;
     default: err = gdr::launch_recurrent(k, p.update_rule, pk, f16, dk_tile(p.head_dim_k), rows_group(problem), s); break;
     }
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));

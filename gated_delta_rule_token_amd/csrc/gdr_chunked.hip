@@ -53,20 +53,30 @@ constexpr int D128 = 128;       // dk = dv
 // Workspace record of one (chunk, head).  Every operand of the scan is stored
 // in MFMA fragment order: 1 KB blocks holding the 16 bytes lane l (= 16 lq + lr)
 // of a wave loads at l * 16, so each wave-wide load reads 1 KB of consecutive
-// bytes (eight whole cache lines).
-//   R_W   W (hi, lo) fp16, block (tb * 4 + kk) * 2 + plane: token 16 tb + lr, keys 32 kk + 8 lq .. +7
-//   R_KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
-//   R_U   U fp32,          block tb * 8 + rt:              tokens 16 tb + 4 lq .. +3, row 16 rt + lr
-//   R_Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
-//   R_P   P (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr, tokens 32 ks + 8 lq .. +7
-//   R_SC  fp32 scalars: kd[64], gq[64], gamma_C
-constexpr uint32_t R_W = 0;
-constexpr uint32_t R_KT = R_W + 32 * 1024;
-constexpr uint32_t R_U = R_KT + 16 * 1024;
-constexpr uint32_t R_Q = R_U + 32 * 1024;
-constexpr uint32_t R_P = R_Q + 16 * 1024;
-constexpr uint32_t R_SC = R_P + 16 * 1024;
-constexpr uint32_t WS_REC = R_SC + 1024;
+// bytes (eight whole cache lines).  Per-head decay (PK = false):
+//   W   W (hi, lo) fp16, block (tb * 4 + kk) * 2 + plane: token 16 tb + lr, keys 32 kk + 8 lq .. +7
+//   KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
+//   U   U fp32,          block tb * 8 + rt:              tokens 16 tb + 4 lq .. +3, row 16 rt + lr
+//   Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
+//   P   P (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr, tokens 32 ks + 8 lq .. +7
+//   SC  fp32 scalars: kd[64], gq[64], gamma_C
+// Decay per key channel (PK = true): the per-token weights kd and gq become
+// per-element factors, so two operands carry fp32 values and get two planes:
+//   KT  Kd^T (hi, lo),   block (mt * 2 + ks) * 2 + plane,  Kd = kn o exp(G_C - G)
+//   Q   Qg (hi, lo),     block (tb * 4 + kk) * 2 + plane,  Qg = scale qn o exp(G)
+//   SC  fp32 gamma_C of each of the 128 key channels
+template <bool PK>
+struct Rec {
+    static constexpr uint32_t W = 0;
+    static constexpr uint32_t KT = W + 32 * 1024;
+    static constexpr uint32_t U = KT + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t Q = U + 32 * 1024;
+    static constexpr uint32_t P = Q + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t SC = P + 16 * 1024;
+    static constexpr uint32_t SIZE = SC + 1024;
+};
+constexpr uint32_t R_W = Rec<false>::W, R_KT = Rec<false>::KT, R_U = Rec<false>::U, R_Q = Rec<false>::Q,
+                   R_P = Rec<false>::P, R_SC = Rec<false>::SC, WS_REC = Rec<false>::SIZE;
 
 __device__ __forceinline__ f4v mfma16(h8 a, h8 b, f4v c)
 {
@@ -86,11 +96,11 @@ __device__ __forceinline__ void split8(const float (&x)[8], h8 &hi, h8 &lo)
 
 __device__ __forceinline__ h8 ld_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
 
-// Raw buffer resource over one workspace record (the record's bytes only:
-// an offset past it reads zero instead of faulting).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *rec)
+// Raw buffer resource over one workspace record of `bytes` bytes (an offset
+// past it reads zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *rec, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rec), 0, (int)WS_REC, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rec), 0, (int)bytes, 0x00020000);
 }
 
 template <typename T>
@@ -371,6 +381,386 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
     }
 }
 
+// ------------------------------------------------------------------ phase 1, per-key decay
+// Decay per key channel (Ascend "aclnnRecurrentGatedDeltaRule", Formula) and
+// the key-axis erase gate of Gated DeltaNet-2 (ONNX issue "Spec gap ...
+// Gated DeltaNet-2", "The GDN-2 recurrence").  With G[t][j] the cumulative
+// log decay of key channel j up to token t inside the chunk, kn = k / |k|,
+// qn = q / |q| (or the raw vectors without qk_l2_norm), and the retrieval key
+// l_t = beta_t kn_t (delta rules) or b_t o kn_t (erase gate), unrolling the
+// recurrence over the chunk gives
+//   A_ts = sum_j l_tj kn_sj exp(G_tj - G_sj)  (s < t),   P_ts = scale sum_j qn_tj kn_sj exp(G_tj - G_sj)  (s <= t)
+//   W = (I + A)^-1 (l o e^G),   U = (I + A)^-1 diag(w) V   (w = beta, or 1 for the erase gate)
+//   Qg = scale qn o e^G,   Kd = kn o e^(G_C - G),   gamma_C = e^(G_C)
+// and the scan's chunk step D = U - W S^T, O = Qg S^T + P D,
+// S^T <- Diag(gamma_C) S^T + Kd^T D.
+//
+// A and P are 16 x 16 blocks (s block sb <= t block tb) of fp32 matrix-core
+// products over the key channels.  Each block splits its decay at the last
+// token e = 16 sb + 15 of block sb: exp(G_t - G_s) = exp(G_t - G_e) exp(G_e - G_s).
+// For decaying channels the second factor is <= 1, and so is the first off
+// the diagonal; on the diagonal the first is >= 1 and bounded by the decay
+// inside the block.  A diagonal block whose decay can exceed DIAG_NATS in
+// some channel (and, with growing channels, every block of the chunk) is
+// summed term by term instead, so no factor leaves the fp32 range.
+//
+// 256 threads, two workgroups per CU.  LDS: K and Q rows (fp16) and G (fp32);
+// after the Gram products A takes Q's rows and V takes K's, and after the
+// solve the W (hi, lo) rows take Q's and G's.
+constexpr float DIAG_NATS = 80.f;
+
+template <int RULE, bool PKG>
+__global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const int32_t *__restrict__ off,
+                                                          char *__restrict__ ws)
+{
+    using RC = Rec<true>;
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr bool BETA = rule_has_beta(RULE);
+    constexpr bool V2 = RULE == GATED_DELTA_V2;
+    constexpr int LD = D128 + 8;   // padded fp16 row
+    constexpr int LF = D128 + 4;   // padded fp32 row
+    constexpr int LA = CH + 4;
+    constexpr int SLOT = CH * LD * 2;
+    static_assert(CH * LA * 4 == SLOT, "A rows fill Q's slot");
+    static_assert(2 * SLOT <= SLOT + CH * LF * 4, "W planes fit over Q and G");
+
+    __shared__ __align__(16) char sm[2 * SLOT + CH * LF * 4];
+    half_t(*sK)[LD] = reinterpret_cast<half_t(*)[LD]>(sm);            // K rows; V rows after the Gram
+    half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + SLOT);     // Q rows
+    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + SLOT);       // A after the Gram
+    float(*sG)[LF] = reinterpret_cast<float(*)[LF]>(sm + 2 * SLOT);   // G (cumulative log decay)
+    half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm + SLOT);  // W (hi, lo) after the solve
+    __shared__ float sIk[CH], sIq[CH], sWt[CH];
+    __shared__ float sTot[2][D128], sPos[2][D128];
+    __shared__ int sFlag;
+
+    const int HV = p.HV, H = p.H;
+    const int64_t ci = blockIdx.x / HV;
+    const int h = blockIdx.x % HV;
+    if (ci >= off[p.B]) return;
+    const int b = chunk_request(off, p.B, ci);
+    int64_t rs, re;
+    request_range(p, b, rs, re);
+    const int64_t t0 = rs + (ci - off[b]) * CH;
+    const int n = (int)((re - t0) < CH ? (re - t0) : CH);
+    const int qh = (int)(((int64_t)h * H) / HV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int col = tid & (D128 - 1);
+    char *rec = ws + ((size_t)ci * HV + h) * RC::SIZE;
+    const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
+    const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
+    const half_t *__restrict__ v = static_cast<const half_t *>(p.v);
+    const float scale = p.scale;
+    // erase gate row of chunk token t (rows past the end read the last token's)
+    auto erase_row = [&](int t) { return p.erase + ((size_t)(t0 + (t < n ? t : n - 1)) * HV + h) * D128; };
+
+    // ---- load phase: K, Q, V rows (fp16), log decay rows (fp32); the W-column
+    // threads also fetch their erase-gate column for the solve's right-hand side
+    h8 ldk[4], ldq[4], ldv[4];
+    f4v ldg[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        ldk[i] = ldq[i] = ldv[i] = h8{};
+        if (r < n) {
+            const size_t tq = ((size_t)(t0 + r) * H + qh) * D128 + c8;
+            ldk[i] = ld_h8(k + tq);
+            ldq[i] = ld_h8(q + tq);
+            ldv[i] = ld_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+        ldg[i] = f4v{0.f, 0.f, 0.f, 0.f};
+        if (r < n) {
+            const size_t th = (size_t)(t0 + r) * HV + h;
+            if constexpr (PKG) {
+                ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
+            } else {
+                const float g = log_decay(p, th, h);
+                ldg[i] = f4v{g, g, g, g};
+            }
+        }
+    }
+    float ev[CH];  // erase gate column of a W-column thread
+    if constexpr (V2) {
+        if (tid < D128) {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) ev[t] = erase_row(t)[col];
+        }
+    }
+    if (tid < CH) {
+        const int t = tid;
+        float w = 0.f;
+        if (t < n) w = BETA ? update_rate(p, (size_t)(t0 + t) * HV + h) : 1.f;
+        sWt[t] = w;
+    }
+    if (tid == 0) sFlag = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<h8 *>(&sK[r][c8]) = ldk[i];
+        *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+        *reinterpret_cast<f4v *>(&sG[r][c4]) = ldg[i];
+    }
+    lds_barrier();
+
+    // ---- cumulative log decay: thread (key col, half hf) scans tokens
+    // 32 hf .. 32 hf + 31 (bands 2 hf, 2 hf + 1), then adds the first half's total.
+    // Guard sums: the decay inside each band (past its first token) bounds the
+    // diagonal split factor; the total growth of the chunk bounds every other.
+    {
+        const int hf = tid >> 7;
+        float run = 0.f, pos = 0.f, neg[2] = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const int t = 32 * hf + r;
+            const float g = sG[t][col];
+            run += g;
+            sG[t][col] = run;
+            pos += fmaxf(g, 0.f);
+            if (r & 15) neg[r >> 4] += fmaxf(-g, 0.f);
+        }
+        sTot[hf][col] = run;
+        sPos[hf][col] = pos;
+        int big = 0;
+        if (neg[0] > DIAG_NATS) big |= 1 << (2 * hf);
+        if (neg[1] > DIAG_NATS) big |= 1 << (2 * hf + 1);
+        if (big) atomicOr(&sFlag, big);
+    }
+    // ---- inverse L2 norms of the chunk's q and k rows: 4 threads per row
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float ss = 0.f, sq = 0.f;
+        if (p.qk_l2_norm) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const h8 kk = ld_h8(&sK[t][32 * part + 8 * g]);
+                const h8 qq = ld_h8(&sQ[t][32 * part + 8 * g]);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    ss = fmaf((float)kk[x], (float)kk[x], ss);
+                    sq = fmaf((float)qq[x], (float)qq[x], sq);
+                }
+            }
+            ss += dpp_mov<0xB1>(ss);  // sum over the 4 lanes of the row
+            ss += dpp_mov<0x4E>(ss);
+            sq += dpp_mov<0xB1>(sq);
+            sq += dpp_mov<0x4E>(sq);
+        }
+        if (part == 0) {
+            const bool on = p.qk_l2_norm && t < n;
+            sIk[t] = on ? 1.f / sqrtf(ss + 1e-12f) : 1.f;
+            sIq[t] = on ? 1.f / sqrtf(sq + 1e-12f) : 1.f;
+        }
+    }
+    lds_barrier();
+    if (tid >= D128) {
+        const float add = sTot[0][col];
+#pragma unroll
+        for (int r = 32; r < CH; ++r) sG[r][col] += add;
+    } else if (sPos[0][col] + sPos[1][col] > DIAG_NATS) {
+        atomicOr(&sFlag, 16);
+    }
+    lds_barrier();
+
+    // ---- operands built from G: Kd^T and Qg fragments (4 + 4 per thread), gamma_C
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // Kd^T: key j, tokens 32 ks + 8 l4 .. +7
+        const int f = tid + 256 * i, j = f & (D128 - 1), grp = f >> 7, ks = grp >> 2, l4 = grp & 3;
+        const float gc = sG[CH - 1][j];
+        float x8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int u = 32 * ks + 8 * l4 + x;
+            x8[x] = (float)sK[u][j] * sIk[u] * expf(gc - sG[u][j]);
+        }
+        h8 hi, lo;
+        split8(x8, hi, lo);
+        char *dst = rec + RC::KT + ((uint32_t)(((j >> 4) * 2 + ks) * 2) * 64 + l4 * 16 + (j & 15)) * 16;
+        *reinterpret_cast<h8 *>(dst) = hi;
+        *reinterpret_cast<h8 *>(dst + 1024) = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // Qg: token 16 tb + lr, keys 32 kk + 8 lq .. +7
+        const int f = tid + 256 * i, blk = f >> 6, fl = f & 63;
+        const int t = 16 * (blk >> 2) + (fl & 15), key = 32 * (blk & 3) + 8 * (fl >> 4);
+        const h8 qq = ld_h8(&sQ[t][key]);
+        float x8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * expf(sG[t][key + x]);
+        h8 hi, lo;
+        split8(x8, hi, lo);
+        char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
+        *reinterpret_cast<h8 *>(dst) = hi;
+        *reinterpret_cast<h8 *>(dst + 1024) = lo;
+    }
+    if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = expf(sG[CH - 1][tid]);
+
+    // ---- A and P, 16 x 16 blocks (sb <= tb) on the fp32 matrix cores; wave w
+    // takes pairs w, w + 4, w + 8.  Lane (lr, lq) sums key channels 32 lq .. 32 lq + 31,
+    // and the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr] without the
+    // per-token factors (applied below).
+    constexpr int8_t PTB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int8_t PSB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    const int flags = sFlag;
+    f4v resA[3], resP[3];
+#pragma unroll
+    for (int slot = 0; slot < 3; ++slot) {
+        const int pi = wave + 4 * slot;
+        resA[slot] = resP[slot] = f4v{0.f, 0.f, 0.f, 0.f};
+        if (pi < 10) {
+            const int tb = PTB[pi], sb = PSB[pi], e = 16 * sb + 15;
+            const int t = 16 * tb + lr, sr = 16 * sb + lr;
+            const float *er = V2 ? erase_row(t) : nullptr;
+            if ((flags & 16) || (tb == sb && ((flags >> tb) & 1))) {
+                // strong decay inside the block (or growth): every term with its own exponential
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * sb + 4 * lq + i;
+                    float a = 0.f, pq = 0.f;
+                    if (s <= t) {
+                        for (int j = 0; j < D128; ++j) {
+                            const float kx = (float)sK[s][j] * expf(sG[t][j] - sG[s][j]);
+                            if constexpr (RET) a = fmaf((V2 ? er[j] : 1.f) * (float)sK[t][j], kx, a);
+                            pq = fmaf((float)sQ[t][j], kx, pq);
+                        }
+                    }
+                    resA[slot][i] = a;
+                    resP[slot][i] = pq;
+                }
+            } else {
+                f4v eb[8];
+                if constexpr (V2) {
+#pragma unroll
+                    for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
+                }
+                f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < 8; ++kq) {
+                    const int key = 32 * lq + 4 * kq;
+                    const f4v gt = *reinterpret_cast<const f4v *>(&sG[t][key]);
+                    const f4v ge = *reinterpret_cast<const f4v *>(&sG[e][key]);
+                    const f4v gs = *reinterpret_cast<const f4v *>(&sG[sr][key]);
+                    const h4 kt = *reinterpret_cast<const h4 *>(&sK[t][key]);
+                    const h4 ks = *reinterpret_cast<const h4 *>(&sK[sr][key]);
+                    const h4 qt = *reinterpret_cast<const h4 *>(&sQ[t][key]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float exa = expf(gt[x] - ge[x]);
+                        const float right = (float)ks[x] * expf(ge[x] - gs[x]);
+                        if constexpr (RET)
+                            accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (V2 ? eb[kq][x] : 1.f) * (float)kt[x] * exa, accA, 0, 0, 0);
+                        accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (float)qt[x] * exa, accP, 0, 0, 0);
+                    }
+                }
+                resA[slot] = accA;
+                resP[slot] = accP;
+            }
+        }
+    }
+    // ---- right-hand side of W for key column col (threads 0-127)
+    float x[CH];
+    if (tid < D128) {
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const float lt = (V2 ? ev[t] : sWt[t]) * sIk[t] * (float)sK[t][col];
+            x[t] = RET ? lt * expf(sG[t][col]) : 0.f;
+        }
+    }
+    lds_barrier();  // K and Q are dead: V takes K's rows, A takes Q's
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<h8 *>(&sK[r][c8]) = ldv[i];
+    }
+#pragma unroll
+    for (int slot = 0; slot < 3; ++slot) {
+        const int pi = wave + 4 * slot;
+        if (pi < 10) {
+            const int tb = PTB[pi], sb = PSB[pi];
+            const int t = 16 * tb + lr, s0 = 16 * sb + 4 * lq;
+            const float at = (V2 ? 1.f : sWt[t]) * sIk[t], pt = scale * sIq[t];
+            f4v pv, av;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = s0 + i;
+                pv[i] = s <= t ? pt * sIk[s] * resP[slot][i] : 0.f;
+                av[i] = s < t ? at * sIk[s] * resA[slot][i] : 0.f;
+            }
+            h4 hi, lo;
+            split4(pv, hi, lo);
+            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = hi;
+            *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
+        }
+    }
+#pragma unroll
+    for (int zi = 0; zi < 2; ++zi) {
+        // the P blocks above the diagonal are zero (the scan multiplies them anyway)
+        constexpr int8_t ZTB[6] = {0, 0, 0, 1, 1, 2};
+        constexpr int8_t ZSB[6] = {1, 2, 3, 2, 3, 3};
+        const int z = wave + 4 * zi;
+        if (z < 6) {
+            const int tb = ZTB[z], sb = ZSB[z], s0 = 16 * sb + 4 * lq;
+            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = h4{};
+            *reinterpret_cast<h4 *>(rec + po + 1024) = h4{};
+        }
+    }
+    lds_barrier();
+
+    // ---- [W | U] = (I + A)^-1 [l o e^G | diag(w) V]; one column per thread
+    const bool wcol = tid < D128;
+    if (!wcol) {
+#pragma unroll
+        for (int t = 0; t < CH; ++t) x[t] = (RET ? sWt[t] : 1.f) * (float)sK[t][col];
+    }
+    if constexpr (RET) {
+#pragma unroll
+        for (int t = 1; t < CH; ++t) {
+            float r[4] = {x[t], 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < t; ++s) r[s & 3] = fmaf(-sA[t][s], x[s], r[s & 3]);
+            x[t] = (r[0] + r[1]) + (r[2] + r[3]);
+        }
+    }
+    if (!wcol) {
+#pragma unroll
+        for (int qd = 0; qd < CH / 4; ++qd)
+            *reinterpret_cast<f4v *>(rec + RC::U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) =
+                f4v{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+    }
+    if constexpr (RET) {
+        lds_barrier();  // A and G are dead: W (hi, lo) rows take their place
+        if (wcol) {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                const half_t hi = (half_t)x[t];
+                sW[0][t][col] = hi;
+                sW[1][t][col] = (half_t)(x[t] - (float)hi);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
+            const int tb = blk >> 3, kk = (blk >> 1) & 3, pl = blk & 1;
+            *reinterpret_cast<h8 *>(rec + RC::W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][32 * kk + 8 * (fl >> 4)]);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ phase 2
 // 512 threads.  Waves 0-3 carry the state chain of a 32-row tile, kept
 // transposed (key rows, state-row columns) in MFMA accumulators; waves 4-7
@@ -389,9 +779,14 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
 // are loaded during chunk j into the second of two register sets; every load
 // is unconditional, since a branch around a load makes the compiler wait for
 // it on the spot.
-template <int RULE, int NVB>
+// With a decay per key channel (PK) the state decays by a vector gamma_C, and
+// Kd^T and Qg carry fp32 values split into (hi, lo) planes, so stage E and O1
+// take three products each; stage E then reads D^T directly (no kd D copy).
+template <int RULE, int NVB, bool PK>
 __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws)
 {
+    using RC = Rec<PK>;
+    constexpr int NPL = PK ? 2 : 1;       // fp16 planes of the K^T and q operands
     constexpr bool RET = rule_retrieves(RULE);
     constexpr int TR = 16 * NVB;          // state rows of this workgroup
     constexpr int NTILE = D128 / TR;      // workgroups per head
@@ -402,7 +797,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     // phase on 16 distinct 4-bank groups.
     __shared__ __align__(16) half_t sS[2][2][TR][LS];    // [buffer][hi, lo][row][key]
     __shared__ __align__(16) half_t sDt[2][2][TR][LDT];  // [buffer][hi, lo][row][token] D^T
-    __shared__ __align__(16) half_t sDs[2][TR][LDT];     // [hi, lo][row][token] (kd D)^T, chain only
+    __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][LDT];  // [hi, lo][row][token] (kd D)^T, chain only
     __shared__ __align__(16) half_t sO[4][16][TR + 8];   // per output wave: [token][row] staging for the store
 
     const int HV = p.HV;
@@ -435,18 +830,20 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 Sc[a][rt] = src ? *reinterpret_cast<const f4v *>(src + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq)
                                 : f4v{0.f, 0.f, 0.f, 0.f};
         struct Ops {
-            h8 wh[4], wl[4];  // W (hi, lo) of token block tb, four k-steps of 32
-            h8 kt[2][2];      // K^T fragments: key tiles 2 wave + a, token steps ks
-            f4v u[NVB];       // U at this lane's D positions, one per row block
-            f4v kd;           // kd of this lane's four D tokens
-            float gc;         // gamma_C
+            h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
+            h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
+            f4v u[NVB];         // U at this lane's D positions, one per row block
+            f4v kd;             // per head: kd of this lane's four D tokens
+            float gc;           // per head: gamma_C
+            f4v gk[2];          // per key: gamma_C of keys 16 (2 wave + a) + 4 lq .. +3
         };
-        const uint32_t offW = R_W + (uint32_t)tb * 8 * 1024 + l16;
-        const uint32_t offK = R_KT + (uint32_t)(2 * wave) * 2 * 1024 + l16;
-        const uint32_t offU = R_U + (uint32_t)(tb * 8 + NVB * tile) * 1024 + l16;
-        const uint32_t offKd = R_SC + (uint32_t)(16 * tb + 4 * lq) * 4;
+        const uint32_t offW = RC::W + (uint32_t)tb * 8 * 1024 + l16;
+        const uint32_t offK = RC::KT + (uint32_t)(2 * wave) * 2 * NPL * 1024 + l16;
+        const uint32_t offU = RC::U + (uint32_t)(tb * 8 + NVB * tile) * 1024 + l16;
+        const uint32_t offKd = RC::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
+        const uint32_t offGk = RC::SC + (uint32_t)(32 * wave + 4 * lq) * 4;
         auto fetch = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * WS_REC);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
             if constexpr (RET) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -457,11 +854,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = ld_b128<h8>(r, offK + (2 * a + ks) * 1024);
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int pl = 0; pl < NPL; ++pl) f.kt[a][ks][pl] = ld_b128<h8>(r, offK + ((2 * a + ks) * NPL + pl) * 1024);
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) f.u[vb] = ld_b128<f4v>(r, offU + vb * 1024);
-            f.kd = ld_b128<f4v>(r, offKd);
-            f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, R_SC + 2 * CH * 4, 0, 0));
+            if constexpr (PK) {
+                f.gk[0] = ld_b128<f4v>(r, offGk);
+                f.gk[1] = ld_b128<f4v>(r, offGk + 64);
+            } else {
+                f.kd = ld_b128<f4v>(r, offKd);
+                f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, RC::SC + 2 * CH * 4, 0, 0));
+            }
         };
         auto step = [&](int j, const Ops &cur, Ops &nxt) {
             const int bf = j & 1;
@@ -507,42 +911,50 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             // tokens per lane -> one 8-byte write per plane
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
-                f4v d, ds;
+                f4v d;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    d[i] = cur.u[vb][i] - accD[vb][i];
-                    ds[i] = cur.kd[i] * d[i];
-                }
-                h4 dh, dl, sh, sl;
+                for (int i = 0; i < 4; ++i) d[i] = cur.u[vb][i] - accD[vb][i];
+                h4 dh, dl;
                 split4(d, dh, dl);
-                split4(ds, sh, sl);
                 const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
                 *reinterpret_cast<h4 *>(&sDt[bf][0][r][c]) = dh;
                 *reinterpret_cast<h4 *>(&sDt[bf][1][r][c]) = dl;
-                *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
-                *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
+                if constexpr (!PK) {
+                    f4v ds;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ds[i] = cur.kd[i] * d[i];
+                    h4 sh, sl;
+                    split4(ds, sh, sl);
+                    *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
+                    *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
+                }
             }
             lds_barrier();  // 2
             // ---- E: S^T <- gamma_C S^T + K^T (kd D) for key tiles 2 wave + a, row blocks rt
+            // (per key: S^T <- Diag(gamma_C) S^T + Kd^T D)
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= cur.gc;
+                for (int rt = 0; rt < NVB; ++rt) {
+                    if constexpr (PK) Sc[a][rt] *= cur.gk[a];
+                    else Sc[a][rt] *= cur.gc;
+                }
             {
                 // with two row blocks the lo products get their own chains
-                constexpr bool SEPL = NVB < 4;
+                constexpr bool SEPL = NVB < 4 || PK;
                 f4v lo4[2][NVB] = {};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int rt = 0; rt < NVB; ++rt) {
-                        const h8 dhi = ld_h8(&sDs[0][16 * rt + lr][32 * ks + lk]);
-                        const h8 dlo = ld_h8(&sDs[1][16 * rt + lr][32 * ks + lk]);
+                        const h8 dhi = PK ? ld_h8(&sDt[bf][0][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[0][16 * rt + lr][32 * ks + lk]);
+                        const h8 dlo = PK ? ld_h8(&sDt[bf][1][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[1][16 * rt + lr][32 * ks + lk]);
 #pragma unroll
                         for (int a = 0; a < 2; ++a) {
-                            Sc[a][rt] = mfma16(cur.kt[a][ks], dhi, Sc[a][rt]);
-                            if constexpr (SEPL) lo4[a][rt] = mfma16(cur.kt[a][ks], dlo, lo4[a][rt]);
-                            else Sc[a][rt] = mfma16(cur.kt[a][ks], dlo, Sc[a][rt]);
+                            Sc[a][rt] = mfma16(cur.kt[a][ks][0], dhi, Sc[a][rt]);
+                            if constexpr (SEPL) lo4[a][rt] = mfma16(cur.kt[a][ks][0], dlo, lo4[a][rt]);
+                            else Sc[a][rt] = mfma16(cur.kt[a][ks][0], dlo, Sc[a][rt]);
+                            if constexpr (PK) lo4[a][rt] = mfma16(cur.kt[a][ks][NPL - 1], dhi, lo4[a][rt]);
                         }
                     }
 #pragma unroll
@@ -568,11 +980,11 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         // ================================================================ outputs
         half_t *o = static_cast<half_t *>(p.o);
         struct Ops {
-            h8 q[4];          // q rows of token block tb, four k-steps of 32
+            h8 q[4][NPL];     // q rows (per key: Qg hi, lo) of token block tb, four k-steps of 32
             h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
-            float gq;         // gq of this lane's token
+            float gq;         // per head: gq of this lane's token
         };
-        const uint32_t offQ = R_Q + (uint32_t)tb * 4 * 1024 + l16;
+        const uint32_t offQ = RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16;
         // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
         const int tok_bytes = HV * D128 * 2;
         // after the LDS transpose each lane stores 16 bytes: token 16 tb + (lane >> 2),
@@ -580,18 +992,20 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         static_assert(TR == 32, "the output transpose assumes 32-row tiles");
         const int st_tok = lane >> 2, st_q = lane & 3;
         const uint32_t offO = (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q);
-        const uint32_t offP = R_P + (uint32_t)tb * 4 * 1024 + l16;
-        const uint32_t offG = R_SC + (uint32_t)(CH + 16 * tb + lr) * 4;
+        const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
+        const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         auto fetch = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * WS_REC);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.q[kk] = ld_b128<h8>(r, offQ + kk * 1024);
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 f.ph[ks] = ld_b128<h8>(r, offP + ks * 2048);
                 f.pl[ks] = ld_b128<h8>(r, offP + ks * 2048 + 1024);
             }
-            f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
+            if constexpr (!PK) f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
         };
         // Store the output tile of chunk jo, staged in sO, as one 16-byte write per
         // lane.  The store is unconditional: the resource spans the chunk's
@@ -623,14 +1037,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 for (int vb = 0; vb < NVB; ++vb) {
                     const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
                     const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
-                    acc[vb] = mfma16(shi, cur.q[kk], acc[vb]);
-                    acl[vb] = mfma16(slo, cur.q[kk], acl[vb]);
+                    acc[vb] = mfma16(shi, cur.q[kk][0], acc[vb]);
+                    acl[vb] = mfma16(slo, cur.q[kk][0], acl[vb]);
+                    if constexpr (PK) acl[vb] = mfma16(shi, cur.q[kk][NPL - 1], acl[vb]);
                 }
             lds_barrier();  // 2
             // ---- O2: O^T = gq O^T + D^T P^T; P is lower triangular (zeros above the
             // diagonal are multiplied anyway so every prefetched fragment is used)
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) acc[vb] = cur.gq * (acc[vb] + acl[vb]);
+            for (int vb = 0; vb < NVB; ++vb) {
+                if constexpr (PK) acc[vb] = acc[vb] + acl[vb];
+                else acc[vb] = cur.gq * (acc[vb] + acl[vb]);
+            }
             {
                 f4v p3[NVB] = {};  // the two lo products in their own chain
 #pragma unroll
@@ -678,26 +1096,28 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 
 // ------------------------------------------------------------------ host side
 
-size_t chunked_workspace_bytes(int64_t T, int B, int HV)
+size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key)
 {
     const int64_t maxch = (T + CH - 1) / CH + B;
     const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
-    return table + (size_t)maxch * HV * WS_REC;
+    return table + (size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE);
 }
 
 // Row tile of the scan: 32 rows (measured on MI355X: 64-row tiles halve the
 // per-row operand reads but lengthen each chunk step by 1.7x, which loses on
 // both the single long sequence and the batched prefill).
-template <int RULE, int NVB>
+template <int RULE, int NVB, bool PK>
 static void launch_scan(const Params &p, const int32_t *off, const char *rec, hipStream_t s)
 {
     constexpr int NTILE = D128 / (16 * NVB);
     const int64_t nbh = (int64_t)p.B * p.HV;
     const int64_t blocks = (nbh + 7) / 8 * 8 * NTILE;
-    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec);
+    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec);
 }
 
-template <int RULE>
+// PK: the per-key record and kernels; PKG: the gate itself is per key (else
+// a per-head gate broadcast over the key channels, used by the erase gate).
+template <int RULE, bool PK, bool PKG>
 static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
 {
     const int64_t maxch = (p.T + CH - 1) / CH + p.B;
@@ -706,19 +1126,26 @@ static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
     int32_t *off = reinterpret_cast<int32_t *>(base);
     char *rec = base + table;
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
-    if (maxch * p.HV > 0)
-        hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)(maxch * p.HV)), dim3(256), 0, s, p, off, rec);
-    launch_scan<RULE, 2>(p, off, rec, s);
+    if (maxch * p.HV > 0) {
+        if constexpr (PK)
+            hipLaunchKernelGGL((k_chunk_prep_pk<RULE, PKG>), dim3((unsigned)(maxch * p.HV)), dim3(256), 0, s, p, off, rec);
+        else
+            hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)(maxch * p.HV)), dim3(256), 0, s, p, off, rec);
+    }
+    launch_scan<RULE, 2, PK>(p, off, rec, s);
     return hipGetLastError();
 }
 
-hipError_t launch_chunked(const Params &p, int rule, void *ws, hipStream_t s)
+hipError_t launch_chunked(const Params &p, int rule, bool per_key, void *ws, hipStream_t s)
 {
+    if (rule == GATED_DELTA_V2)
+        return per_key ? launch_rule<GATED_DELTA_V2, true, true>(p, ws, s) : launch_rule<GATED_DELTA_V2, true, false>(p, ws, s);
+    if (per_key) return rule == GATED ? launch_rule<GATED, true, true>(p, ws, s) : launch_rule<GATED_DELTA, true, true>(p, ws, s);
     switch (rule) {
-    case LINEAR: return launch_rule<LINEAR>(p, ws, s);
-    case GATED: return launch_rule<GATED>(p, ws, s);
-    case DELTA: return launch_rule<DELTA>(p, ws, s);
-    default: return launch_rule<GATED_DELTA>(p, ws, s);
+    case LINEAR: return launch_rule<LINEAR, false, false>(p, ws, s);
+    case GATED: return launch_rule<GATED, false, false>(p, ws, s);
+    case DELTA: return launch_rule<DELTA, false, false>(p, ws, s);
+    default: return launch_rule<GATED_DELTA, false, false>(p, ws, s);
     }
 }
 

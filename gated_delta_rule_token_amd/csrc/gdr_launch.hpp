@@ -15,10 +15,11 @@ hipError_t launch_recurrent(const Params &p, int rule, bool per_key, bool f16, i
 // Decode kernel, dk = dv = 128 only.
 hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s);
 
-// Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations, scalar
-// decay); `ws` holds chunked_workspace_bytes(T, B, HV) bytes.
-size_t chunked_workspace_bytes(int64_t T, int B, int HV);
-hipError_t launch_chunked(const Params &p, int rule, void *ws, hipStream_t s);
+// Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations); the
+// per-key form (per_key) serves a decay per key channel and the erase gate.
+// `ws` holds chunked_workspace_bytes(T, B, HV, per_key) bytes.
+size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key);
+hipError_t launch_chunked(const Params &p, int rule, bool per_key, void *ws, hipStream_t s);
 
 // Standalone gate fusion.
 hipError_t launch_gate(int64_t count, int heads, bool f16, const void *a, const float *dt_bias,

@@ -168,8 +168,16 @@ def test_workspace_and_algo_selection(lib):
     assert api.selected_algo(p) == "chunked"
     assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
     assert n.value >= (4096 // 64) * 4 * 64 * 128 * 4
-    # per-key decay stays on the recurrent kernel
+    # a per-key decay takes the per-key chunked form, whose record is larger
+    n_head = n.value
     p.decay_per_key, p.gate_activation, p.gate_dtype = 1, 0, api.F32
+    assert api.selected_algo(p) == "chunked"
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
+    assert n.value > n_head
+    # short requests stay on the recurrent kernel, fp32 activations too
+    p.total_tokens = 2 * 100
+    assert api.selected_algo(p) == "recurrent"
+    p.total_tokens, p.act_dtype = 4096, api.F32
     assert api.selected_algo(p) == "recurrent"
 
 

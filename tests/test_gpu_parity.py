@@ -318,3 +318,65 @@ def test_long_prefill_workload_full_chunked():
 def test_varlen_prefill_workload_full_chunked():
     case = workloads.varlen_prefill()
     _sampled(case, "chunked", [(0, [0, 31]), (2, [9]), (5, [20, 21])], TOL_CHUNKED, "varlen chunked")
+
+
+# ------------------------------------------------------------------ chunked prefill, per-key form
+PK_RULES = [("gated_delta", True), ("gated", True), ("gated_delta_v2", True), ("gated_delta_v2", False)]
+
+
+@pytest.mark.parametrize("rule,per_key", PK_RULES, ids=["%s%s" % (r, "_pk" if p else "") for r, p in PK_RULES])
+@pytest.mark.parametrize("arms", ["plain", "sigmoid_l2"])
+def test_chunked_per_key_rules(rule, per_key, arms):
+    kw = {}
+    if arms != "plain":
+        kw["qk_l2_norm"] = 1
+        if rule == "gated_delta":
+            kw["beta_activation"] = "sigmoid"
+    case = workloads.random_case(zlib.crc32(("chunkpk/%s/%d/%s" % (rule, per_key, arms)).encode()) % 1000,
+                                 lengths=[200, 1, 0, 64, 130], H=2, HV=4, DK=128, DV=128,
+                                 dtype=np.float16, update_rule=rule, per_key=per_key,
+                                 unit_keys=(arms == "plain"), **kw)
+    _check_full(case, "chunked", "chunked per-key %s%s %s" % (rule, "_pk" if per_key else "", arms))
+
+
+@pytest.mark.parametrize("rule", ["gated_delta", "gated_delta_v2"])
+def test_chunked_per_key_strong_decay(rule):
+    """Channels that decay by 8 nats per token exceed the bound the chunk
+    prologue's block split allows inside a 16-token block, so those diagonal
+    blocks are summed term by term; the rest of the channels stay mild."""
+    case = workloads.random_case(77, lengths=[150, 64, 37], H=2, HV=4, DK=128, DV=128,
+                                 dtype=np.float16, update_rule=rule, per_key=True)
+    g = case["gate"].copy()
+    g[:, :, ::5] = -8.0
+    g[:90, 1, 3::7] = -0.001
+    case["gate"] = g
+    _check_full(case, "chunked", "chunked per-key strong decay %s" % rule)
+
+
+def test_chunked_per_key_gqa_and_slab():
+    case = workloads.random_case(43, rank4_batch=(3, 150), H=2, HV=8, DK=128, DV=128,
+                                 dtype=np.float16, update_rule="gated_delta_v2", per_key=True,
+                                 slots=(7,))
+    say("case chunked per-key slab")
+    o, slab = gpu_forward(case, "chunked")
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "chunked per-key slab o")
+    ids = case["slot_ids"]
+    assert_close(slab[ids], rs[ids], TOL_CHUNKED, "chunked per-key slab rows")
+    rest = np.setdiff1d(np.arange(7), ids)
+    assert np.array_equal(slab[rest], case["slab"][rest].astype(np.float64))
+
+
+def test_chunked_per_key_matches_recurrent_and_is_deterministic():
+    case = workloads.perkey_erase(B=2, L=700)
+    a = gpu_forward(case, "chunked")
+    b = gpu_forward(case, "recurrent")
+    assert_close(a[0], b[0], TOL_CHUNKED, "per-key chunked vs recurrent o")
+    assert_close(a[1], b[1], TOL_CHUNKED, "per-key chunked vs recurrent state")
+    c = gpu_forward(case, "chunked")
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_perkey_erase_workload_full_chunked():
+    case = workloads.perkey_erase()
+    _sampled(case, "chunked", [(0, [0, 3]), (2, [17]), (3, [31])], TOL_CHUNKED, "perkey+erase chunked")
