@@ -408,6 +408,11 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
 // after the Gram products A takes Q's rows and V takes K's, and after the
 // solve the W (hi, lo) rows take Q's and G's.
 constexpr float DIAG_NATS = 80.f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (one instruction; results below the normal
+// range flush toward zero, which only ever drops terms smaller than 1e-38)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int RULE, bool PKG>
 __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const int32_t *__restrict__ off,
@@ -428,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     half_t(*sK)[LD] = reinterpret_cast<half_t(*)[LD]>(sm);            // K rows; V rows after the Gram
     half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + SLOT);     // Q rows
     float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + SLOT);       // A after the Gram
-    float(*sG)[LF] = reinterpret_cast<float(*)[LF]>(sm + 2 * SLOT);   // G (cumulative log decay)
+    float(*sG)[LF] = reinterpret_cast<float(*)[LF]>(sm + 2 * SLOT);   // G log2(e): cumulative log2 decay
     half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm + SLOT);  // W (hi, lo) after the solve
     __shared__ float sIk[CH], sIq[CH], sWt[CH];
     __shared__ float sTot[2][D128], sPos[2][D128];
@@ -561,12 +566,15 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         }
     }
     lds_barrier();
+    // second half adds the first half's total; both convert to log2 units
     if (tid >= D128) {
         const float add = sTot[0][col];
 #pragma unroll
-        for (int r = 32; r < CH; ++r) sG[r][col] += add;
-    } else if (sPos[0][col] + sPos[1][col] > DIAG_NATS) {
-        atomicOr(&sFlag, 16);
+        for (int r = 32; r < CH; ++r) sG[r][col] = (sG[r][col] + add) * LOG2E;
+    } else {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) sG[r][col] *= LOG2E;
+        if (sPos[0][col] + sPos[1][col] > DIAG_NATS) atomicOr(&sFlag, 16);
     }
     lds_barrier();
 
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
             const int u = 32 * ks + 8 * l4 + x;
-            x8[x] = (float)sK[u][j] * sIk[u] * expf(gc - sG[u][j]);
+            x8[x] = (float)sK[u][j] * sIk[u] * ex2(gc - sG[u][j]);
         }
         h8 hi, lo;
         split8(x8, hi, lo);
@@ -596,14 +604,14 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         const h8 qq = ld_h8(&sQ[t][key]);
         float x8[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * expf(sG[t][key + x]);
+        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * ex2(sG[t][key + x]);
         h8 hi, lo;
         split8(x8, hi, lo);
         char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
         *reinterpret_cast<h8 *>(dst) = hi;
         *reinterpret_cast<h8 *>(dst + 1024) = lo;
     }
-    if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = expf(sG[CH - 1][tid]);
+    if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
 
     // ---- A and P, 16 x 16 blocks (sb <= tb) on the fp32 matrix cores; wave w
     // takes pairs w, w + 4, w + 8.  Lane (lr, lq) sums key channels 32 lq .. 32 lq + 31,
@@ -629,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                     float a = 0.f, pq = 0.f;
                     if (s <= t) {
                         for (int j = 0; j < D128; ++j) {
-                            const float kx = (float)sK[s][j] * expf(sG[t][j] - sG[s][j]);
+                            const float kx = (float)sK[s][j] * ex2(sG[t][j] - sG[s][j]);
                             if constexpr (RET) a = fmaf((V2 ? er[j] : 1.f) * (float)sK[t][j], kx, a);
                             pq = fmaf((float)sQ[t][j], kx, pq);
                         }
@@ -655,8 +663,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                     const h4 qt = *reinterpret_cast<const h4 *>(&sQ[t][key]);
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        const float exa = expf(gt[x] - ge[x]);
-                        const float right = (float)ks[x] * expf(ge[x] - gs[x]);
+                        const float exa = ex2(gt[x] - ge[x]);
+                        const float right = (float)ks[x] * ex2(ge[x] - gs[x]);
                         if constexpr (RET)
                             accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (V2 ? eb[kq][x] : 1.f) * (float)kt[x] * exa, accA, 0, 0, 0);
                         accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (float)qt[x] * exa, accP, 0, 0, 0);
@@ -673,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             const float lt = (V2 ? ev[t] : sWt[t]) * sIk[t] * (float)sK[t][col];
-            x[t] = RET ? lt * expf(sG[t][col]) : 0.f;
+            x[t] = RET ? lt * ex2(sG[t][col]) : 0.f;
         }
     }
     lds_barrier();  // K and Q are dead: V takes K's rows, A takes Q's
