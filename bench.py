@@ -46,11 +46,12 @@ def _t(x):
     return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def decode_bytes(B, H, HV, dk, dv, act_bytes=2):
-    """Algorithmic bytes of one decode step: each addressed state row is read
-    and written once; q, k, v, o, gate, beta, slot ids, per-head params once."""
+def decode_bytes(B, H, HV, dk, dv, L=1, act_bytes=2):
+    """Algorithmic bytes of one decode step of L tokens per request: each
+    addressed state row is read and written once; q, k, v, o, gate, beta of
+    every token, slot ids and per-head params once."""
     state = 2 * B * HV * dv * dk * 4
-    acts = B * (2 * H * dk + 2 * HV * dv) * act_bytes + B * HV * (act_bytes + 4) + B * 4 + 2 * HV * 4
+    acts = B * L * ((2 * H * dk + 2 * HV * dv) * act_bytes + HV * (act_bytes + 4)) + B * 4 + 2 * HV * 4
     return state + acts, state
 
 
@@ -100,10 +101,10 @@ def time_calls(calls, steps, warmup):
     return wall, kms
 
 
-def bench_decode(args):
+def bench_decode(args, L=1):
     import torch
     from gated_delta_rule_token_amd import api, workloads
-    case = workloads.decode_slab()
+    case = workloads.decode_slab(L=L)
     B, H = case["q"].shape[0], case["q"].shape[2]
     HV, dv, dk = case["v"].shape[2], case["v"].shape[3], case["q"].shape[3]
     ids_a = case["slot_ids"]
@@ -115,15 +116,15 @@ def bench_decode(args):
                   gate_activation="qwen", beta_activation="sigmoid", algo=args.decode_algo)
     q, k, v = _t(case["q"]), _t(case["k"]), _t(case["v"])
     calls = [api.prepare(q, k, v, slot_ids=_t(ids), **common) for ids in (ids_a, ids_b)]
-    wall, kms = time_calls(calls, args.steps, args.warmup)
-    total_b, state_b = decode_bytes(B, H, HV, dk, dv)
+    wall, kms = time_calls(calls, args.steps if L == 1 else max(20, args.steps // 4), args.warmup)
+    total_b, state_b = decode_bytes(B, H, HV, dk, dv, L)
     digest = source_digest(DECODE_SOURCES)
     traffic = committed_traffic(digest)
     achieved = total_b / (kms * 1e-3) / 1e9
     return case, {
         "wall_s": wall, "kernel_ms": kms, "bytes_per_step": total_b, "state_bytes": state_b,
         "gbs_wall": total_b * args.steps / wall / 1e9, "gbs_kernel": achieved,
-        "algo": calls[0].algo, "tokens": B, "traffic": traffic, "digest": digest,
+        "algo": calls[0].algo, "tokens": B * L, "traffic": traffic, "digest": digest,
     }
 
 
@@ -189,7 +190,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--decode-algo", default="auto")
     ap.add_argument("--prefill-algo", default="auto")
-    ap.add_argument("--only", choices=["decode", "prefill", "varlen", "long", "perkey"], default=None)
+    ap.add_argument("--only", choices=["decode", "mtp", "prefill", "varlen", "long", "perkey"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
@@ -233,6 +234,16 @@ def main():
         })
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
+        del case
+    if args.only in (None, "decode", "mtp"):
+        # the same step with 4 tokens per request (speculative / multi-token verify):
+        # the state crosses HBM once for all four tokens
+        case, d = bench_decode(args, L=4)
+        result["decode_mtp"] = {
+            "workload": case["name"], "tokens_per_request": 4, "kernel": d["algo"],
+            "kernel_ms": d["kernel_ms"], "tokens_per_s": d["tokens"] / (d["kernel_ms"] * 1e-3),
+            "gbs_kernel": d["gbs_kernel"], "pct_of_8tbs": 100 * d["gbs_kernel"] / HBM_PEAK_GBS,
+            "bytes_per_step": d["bytes_per_step"]}
         del case
     if args.only in (None, "prefill", "varlen"):
         result["prefill"] = bench_prefill(args, "varlen")

@@ -88,24 +88,26 @@ def tiny_varlen(seed: int = 0):
         qk_l2_norm=1, act_dtype="f32")
 
 
-def decode_slab(seed: int = 1, B=256, H=16, HV=32, D=128, num_slots=512, with_slab=True):
-    """One decode step: B requests of one token (rank-4 (B,1,...)), H=16 q/k
-    heads, HV=32 value heads, dk=dv=128, fp16 q/k/v (keys unit length), a
+def decode_slab(seed: int = 1, B=256, H=16, HV=32, D=128, num_slots=512, with_slab=True, L=1):
+    """One decode step: B requests of L tokens (rank-4 (B,L,...); L = 1 is
+    plain decode, a few tokens the speculative / multi-token verify shape), H=16
+    q/k heads, HV=32 value heads, dk=dv=128, fp16 q/k/v (keys unit length), a
     fp32 state slab of num_slots slots ~ N(0, 0.05) updated in place at B
     distinct random slot ids; raw-gate arm (fp16 a ~ N(0,1), per-head dt_bias
     ~ U(0,1), A_log = log U(1,16)), update rate sigmoid(b), b ~ N(0,1)."""
     rng = rng_for(seed)
     slot_ids = rng.choice(num_slots, size=B, replace=False).astype(np.int32)
-    q = _normal(rng, (B, 1, H, D), np.float16)
-    k = unit_rows(rng, (B, 1, H, D), np.float16)
-    v = _normal(rng, (B, 1, HV, D), np.float16)
-    a = _normal(rng, (B, 1, HV), np.float16)
+    q = _normal(rng, (B, L, H, D), np.float16)
+    k = unit_rows(rng, (B, L, H, D), np.float16)
+    v = _normal(rng, (B, L, HV, D), np.float16)
+    a = _normal(rng, (B, L, HV), np.float16)
     dt_bias = rng.uniform(0.0, 1.0, size=HV).astype(np.float32)
     a_log = _log_uniform_alog(rng, HV)
-    b = _normal(rng, (B, 1, HV))
+    b = _normal(rng, (B, L, HV))
     slab = _normal(rng, (num_slots, HV, D, D), np.float32, std=0.05) if with_slab else None
     return base(
-        name="decode_B%d_H%d_HV%d_d%d_slab%d_f16" % (B, H, HV, D, num_slots),
+        name=("decode_B%d_H%d_HV%d_d%d_slab%d_f16" % (B, H, HV, D, num_slots)) if L == 1 else
+             ("decode_B%d_L%d_H%d_HV%d_d%d_slab%d_f16" % (B, L, H, HV, D, num_slots)),
         q=q, k=k, v=v, gate=a, dt_bias=dt_bias, a_log=a_log, beta=b, slot_ids=slot_ids,
         slab=slab, update_rule="gated_delta", gate_activation="qwen",
         beta_activation="sigmoid", qk_l2_norm=0, act_dtype="f16", num_slots=num_slots)

@@ -133,6 +133,22 @@ def _sampled(case, algo, pairs, tol, label):
         assert_close(st[b][heads], rs[0], tol, "%s state req %d heads %s" % (label, b, heads))
 
 
+def test_decode_workload_four_tokens_per_request():
+    """The decode step at its full shape with 4 tokens per request (the
+    multi-token verify shape): AUTO keeps the decode kernel, which holds the
+    state rows in registers across the tokens."""
+    case = workloads.decode_slab(L=4)
+    say("case %s: decode kernel, 4 tokens per request" % case["name"])
+    o, new_slab = gpu_forward(case, "auto")
+    ids = case["slot_ids"]
+    gath = dict(case, slab=None, slot_ids=None, initial_state=case["slab"][ids])
+    ro, rs = oracle_forward(gath)
+    assert_close(o, ro, TOL_F16, "decode L=4 o")
+    assert_close(new_slab[ids], rs, TOL_F16, "decode L=4 slab rows")
+    untouched = np.setdiff1d(np.arange(case["slab"].shape[0]), ids)
+    assert np.array_equal(new_slab[untouched], case["slab"][untouched].astype(np.float64))
+
+
 def test_varlen_prefill_workload_full():
     case = workloads.varlen_prefill()
     _sampled(case, "recurrent", [(0, [0, 31]), (3, [5]), (7, [16, 17])], TOL_F16, "varlen")
