@@ -235,7 +235,7 @@ def main():
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
         del case
-    if args.only in (None, "decode", "mtp"):
+    if args.only in (None, "mtp"):
         # the same step with 4 tokens per request (speculative / multi-token verify):
         # the state crosses HBM once for all four tokens
         case, d = bench_decode(args, L=4)

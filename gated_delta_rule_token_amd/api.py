@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(_PKG, "libgdr.so")
 _lock = threading.Lock()
 _lib = None
 
+ABI_VERSION = 2  # GDR_ABI_VERSION of include/gdr.h the structs below mirror
 GDR_OK, GDR_E_INVALID, GDR_E_UNSUPPORTED, GDR_E_ALIAS, GDR_E_WORKSPACE, GDR_E_HIP = range(6)
 F32, F16 = 0, 1
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3, "gated_delta_v2": 4}
@@ -63,7 +64,7 @@ class Problem(ctypes.Structure):
 class Tensors(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "q", "k", "v", "o", "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens",
-        "slot_ids", "initial_state", "final_state")]
+        "slot_ids", "initial_state", "final_state", "gate_scale", "seq_lens")]
 
 
 EXPORTS = ("gdr_abi_version", "gdr_status_str", "gdr_last_error", "gdr_validate",
@@ -84,6 +85,9 @@ def load_library():
             raise GDRError("GDR_E_HIP", "libgdr.so is not built (python -m gated_delta_rule_token_amd.build)")
         lib = ctypes.CDLL(_LIB_PATH)
         lib.gdr_abi_version.restype = ctypes.c_int
+        if lib.gdr_abi_version() != ABI_VERSION:
+            raise GDRError("GDR_E_HIP", "libgdr.so has ABI %d, this binding expects %d (rebuild it)"
+                           % (lib.gdr_abi_version(), ABI_VERSION))
         lib.gdr_status_str.restype = ctypes.c_char_p
         lib.gdr_status_str.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
@@ -141,7 +145,8 @@ def _need(t, name, dtype=None, device=None):
 def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
                   cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
                   update_rule="gated_delta", gate_activation="none", beta_activation="none",
-                  qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", batch=None):
+                  qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", batch=None,
+                  gate_scale=None, seq_lens=None):
     """Problem descriptor from tensor shapes (no device access)."""
     rank4 = q.dim() == 4
     if rank4:
@@ -157,6 +162,8 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
                     batch = initial_state.shape[0]
                 elif slot_ids is not None:
                     batch = slot_ids.shape[0]
+                elif seq_lens is not None:
+                    batch = seq_lens.shape[0]
                 else:
                     batch = 1
             B = int(batch)
@@ -191,12 +198,16 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
             cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
             update_rule="gated_delta", gate_activation="none", beta_activation="none",
             qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", out=None,
-            final_state=None, workspace=None, batch=None):
+            final_state=None, workspace=None, batch=None, gate_scale=None, seq_lens=None):
     """Run the gated delta rule on the GPU.
 
     q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
     decay, or the raw projection with gate_activation='qwen'): (...,HV) or
     per key (...,HV,dk); beta: (...,HV) fp32; erase: (...,HV,dk) fp32.
+    Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a per-key gate, and either
+    a_log (HV,) or the folded gate_scale = -exp(a_log) (HV,).  seq_lens (B,)
+    int32 bounds each uniform-packed request to its first seq_lens[b] tokens
+    (rows past it in ``o`` are left as they are).
     With ``state`` (a slab (num_slots,HV,dv,dk) fp32) and ``slot_ids``, the
     slab is updated in place and returned as the second result; otherwise a
     final state (B,HV,dv,dk) is allocated (or ``final_state`` is filled).
@@ -213,6 +224,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     _need(erase, "erase", torch.float32, dev)
     _need(a_log, "a_log", torch.float32, dev)
     _need(dt_bias, "dt_bias", torch.float32, dev)
+    _need(gate_scale, "gate_scale", torch.float32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     _need(slot_ids, "slot_ids", torch.int32, dev)
     _need(initial_state, "initial_state", torch.float32, dev)
@@ -225,7 +238,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
                       cu_seqlens=cu_seqlens, initial_state=initial_state, slot_ids=slot_ids,
                       state=state, update_rule=update_rule, gate_activation=gate_activation,
                       beta_activation=beta_activation, qk_l2_norm=qk_l2_norm, scale=scale,
-                      chunk_size=chunk_size, algo=algo, batch=batch)
+                      chunk_size=chunk_size, algo=algo, batch=batch, gate_scale=gate_scale,
+                      seq_lens=seq_lens)
     HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
     lead = tuple(q.shape[:-2])
     if out is None:
@@ -244,7 +258,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(gate), beta=_ptr(beta),
                 erase=_ptr(erase), a_log=_ptr(a_log), dt_bias=_ptr(dt_bias),
                 cu_seqlens=_ptr(cu_seqlens), slot_ids=_ptr(slot_ids),
-                initial_state=_ptr(initial_state), final_state=_ptr(fin))
+                initial_state=_ptr(initial_state), final_state=_ptr(fin),
+                gate_scale=_ptr(gate_scale), seq_lens=_ptr(seq_lens))
     stream = torch.cuda.current_stream(dev).cuda_stream
     check(lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), _ptr(workspace),
                           ws_bytes if workspace is not None else 0, stream))
@@ -285,7 +300,7 @@ class Prepared:
         dev = q.device
         p = build_problem(q, k, v, **{key: kw.get(key) for key in (
             "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens", "initial_state",
-            "slot_ids", "state")}, **{key: kw[key] for key in (
+            "slot_ids", "state", "gate_scale", "seq_lens")}, **{key: kw[key] for key in (
                 "update_rule", "gate_activation", "beta_activation", "qk_l2_norm", "scale",
                 "chunk_size", "algo", "batch") if key in kw})
         HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
@@ -305,7 +320,8 @@ class Prepared:
                          beta=_ptr(g("beta")), erase=_ptr(g("erase")), a_log=_ptr(g("a_log")),
                          dt_bias=_ptr(g("dt_bias")), cu_seqlens=_ptr(g("cu_seqlens")),
                          slot_ids=_ptr(g("slot_ids")), initial_state=_ptr(g("initial_state")),
-                         final_state=_ptr(fin))
+                         final_state=_ptr(fin), gate_scale=_ptr(g("gate_scale")),
+                         seq_lens=_ptr(g("seq_lens")))
         self.p = p
         self.ws_bytes = ws
         self.algo = selected_algo(p)

@@ -82,8 +82,6 @@ gdr_status check_problem(const gdr_problem *p)
     if (p->gate_activation == GDR_GATE_QWEN && !decays)
         return fail(GDR_E_INVALID, "gate_activation qwen needs a decayed update_rule");
     if (p->decay_per_key && !decays) return fail(GDR_E_INVALID, "decay_per_key needs a decayed update_rule");
-    if (p->decay_per_key && (p->gate_activation != GDR_GATE_NONE || p->gate_dtype != GDR_F32))
-        return fail(GDR_E_UNSUPPORTED, "a per-key decay must be an fp32 log decay (no gate activation)");
     if (!std::isfinite(p->scale)) return fail(GDR_E_INVALID, "scale is not finite");
     const int64_t blocks = (int64_t)p->batch * p->num_heads_v * 16;
     if (blocks > INT32_MAX) return fail(GDR_E_INVALID, "batch * num_heads_v too large");
@@ -117,10 +115,13 @@ gdr_status check_tensors(const gdr_problem *p, const gdr_tensors *t)
     if (T > 0 && decays && !t->gate) return fail(GDR_E_INVALID, "gate is required by this update_rule");
     if (T > 0 && has_beta && !t->beta) return fail(GDR_E_INVALID, "beta is required by this update_rule");
     if (T > 0 && v2 && !t->erase) return fail(GDR_E_INVALID, "erase is required by gated_delta_v2");
-    if ((t->a_log != nullptr) != (t->dt_bias != nullptr))
-        return fail(GDR_E_INVALID, "a_log and dt_bias must be given together");
-    if ((t->a_log != nullptr) != qwen)
-        return fail(GDR_E_INVALID, qwen ? "gate_activation qwen requires a_log and dt_bias" : "a_log/dt_bias given without gate_activation qwen");
+    if (qwen) {
+        if (!t->dt_bias || (t->a_log != nullptr) == (t->gate_scale != nullptr))
+            return fail(GDR_E_INVALID, "gate_activation qwen requires dt_bias and exactly one of a_log, gate_scale");
+    } else if (t->a_log || t->dt_bias || t->gate_scale) {
+        return fail(GDR_E_INVALID, "a_log/gate_scale/dt_bias given without gate_activation qwen");
+    }
+    if (t->seq_lens && t->cu_seqlens) return fail(GDR_E_INVALID, "seq_lens bounds uniform packing; not with cu_seqlens");
     if ((p->num_slots > 0) != (t->slot_ids != nullptr))
         return fail(GDR_E_INVALID, "slot_ids must be given exactly when num_slots > 0");
     if (p->num_slots > 0 && t->initial_state)
@@ -131,7 +132,8 @@ gdr_status check_tensors(const gdr_problem *p, const gdr_tensors *t)
         return fail(GDR_E_INVALID, "seq_len must be set without cu_seqlens");
 
     const void *ptrs[] = {t->q, t->k, t->v, t->o, t->gate, t->beta, t->erase, t->a_log, t->dt_bias,
-                          t->cu_seqlens, t->slot_ids, t->initial_state, t->final_state};
+                          t->cu_seqlens, t->slot_ids, t->initial_state, t->final_state, t->gate_scale,
+                          t->seq_lens};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(GDR_E_INVALID, "every tensor pointer must be 16-byte aligned");
 
@@ -153,7 +155,9 @@ gdr_status check_tensors(const gdr_problem *p, const gdr_tensors *t)
         rng("beta", t->beta, (size_t)T * HV * 4),
         rng("erase", t->erase, (size_t)T * HV * dk * 4),
         rng("a_log", t->a_log, (size_t)HV * 4),
-        rng("dt_bias", t->dt_bias, (size_t)HV * 4),
+        rng("gate_scale", t->gate_scale, (size_t)HV * 4),
+        rng("dt_bias", t->dt_bias, (size_t)HV * (p->decay_per_key ? dk : 1) * 4),
+        rng("seq_lens", t->seq_lens, (size_t)p->batch * 4),
         rng("cu_seqlens", t->cu_seqlens, (size_t)(p->batch + 1) * 4),
         rng("slot_ids", t->slot_ids, (size_t)p->batch * 4),
         rng("initial_state", t->initial_state, (size_t)p->batch * HV * dv * dk * 4),
@@ -266,6 +270,8 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     k.erase = t.erase;
     k.a_log = t.a_log;
     k.dt_bias = t.dt_bias;
+    k.gate_scale = t.gate_scale;
+    k.seq_lens = t.seq_lens;
     k.cu_seqlens = t.cu_seqlens;
     k.slot_ids = t.slot_ids;
     k.init = t.initial_state;

@@ -482,7 +482,12 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         if (r < n) {
             const size_t th = (size_t)(t0 + r) * HV + h;
             if constexpr (PKG) {
-                ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
+                if (!p.gate_f16 && !p.gate_qwen) {
+                    ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) ldg[i][x] = log_decay_key(p, th, h, c4 + x);
+                }
             } else {
                 const float g = log_decay(p, th, h);
                 ldg[i] = f4v{g, g, g, g};

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 const int col = (c < 4 ? 0 : 64) + l16 * 4 + (c & 3);
-                const float g = PK ? static_cast<const float *>(p.gate)[th * DK + col] : sa;
+                const float g = PK ? log_decay_key(p, th, h, col) : sa;
                 av[c] = expf(g);
                 float er = 1.f;
                 if constexpr (RULE == GATED_DELTA_V2) er = p.erase[th * DK + col];

@@ -30,7 +30,9 @@ struct Params {
     void *o;
     const void *gate;
     const float *beta, *erase, *a_log, *dt_bias;
+    const float *gate_scale;   // folded -exp(a_log) per head, or nullptr (then a_log)
     const int32_t *cu_seqlens, *slot_ids;
+    const int32_t *seq_lens;   // valid tokens per uniform-packed request, or nullptr
     const float *init;      // incoming states (B,HV,dv,dk) or nullptr (zeros); unused with slots
     float *state;           // outgoing states, or the slab updated in place
     int64_t T;
@@ -84,14 +86,39 @@ __device__ __forceinline__ float softplus_f32(float x)
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf(-x)); }
 
+// Scale of the raw-gate arm for head h: -exp(a_log[h]) (README Attributes
+// gate_activation), or the caller's once-folded gate_scale[h] (CLIKA
+// "gatedDeltaUpdate": gate_bias and gate_scale bound together).
+__device__ __forceinline__ float gate_scale(const Params &p, int h)
+{
+    return p.gate_scale ? p.gate_scale[h] : -expf(p.a_log[h]);
+}
+
 // Log decay g for token t, head h (scalar gate): README Attributes
 // gate_activation; the raw-gate arm reads the projection in fp16 or fp32.
 __device__ __forceinline__ float log_decay(const Params &p, size_t idx, int h)
 {
     float x = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[idx])
                          : static_cast<const float *>(p.gate)[idx];
-    if (p.gate_qwen) x = -expf(p.a_log[h]) * softplus_f32(x + p.dt_bias[h]);
+    if (p.gate_qwen) x = gate_scale(p, h) * softplus_f32(x + p.dt_bias[h]);
     return x;
+}
+
+// Raw-gate arm of a per-key gate: x is key channel j of head h's projection;
+// the bias is per (head, key channel), [HV, K] beside a [B, T, HV, K] gate
+// (CLIKA "gatedDeltaUpdate").
+__device__ __forceinline__ float key_decay_from_raw(const Params &p, float x, int h, int j)
+{
+    return gate_scale(p, h) * softplus_f32(x + p.dt_bias[(size_t)h * p.dk + j]);
+}
+
+// Log decay of key channel j for token-head th (= t * HV + h) of a per-key gate.
+__device__ __forceinline__ float log_decay_key(const Params &p, size_t th, int h, int j)
+{
+    const size_t idx = th * p.dk + j;
+    float x = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[idx])
+                         : static_cast<const float *>(p.gate)[idx];
+    return p.gate_qwen ? key_decay_from_raw(p, x, h, j) : x;
 }
 
 __device__ __forceinline__ float update_rate(const Params &p, size_t idx)
@@ -102,7 +129,9 @@ __device__ __forceinline__ float update_rate(const Params &p, size_t idx)
 
 // ---------------------------------------------------------------- addressing
 // Request b's token range: README Inputs cu_seqlens (clamped to [0,T]; a
-// decreasing entry gives an empty request) or uniform packing.
+// decreasing entry gives an empty request) or uniform packing, optionally
+// bounded by seq_lens[b] clamped to [0, L] (CLIKA "gatedDeltaUpdate": seq_lens
+// bounds ragged prefill rows).
 __device__ __forceinline__ void request_range(const Params &p, int b, int64_t &s, int64_t &e)
 {
     if (p.cu_seqlens) {
@@ -113,7 +142,12 @@ __device__ __forceinline__ void request_range(const Params &p, int b, int64_t &s
         e = z > a ? z : a;
     } else {
         s = (int64_t)b * p.L;
-        e = s + p.L;
+        int64_t len = p.L;
+        if (p.seq_lens) {
+            len = p.seq_lens[b];
+            len = len < 0 ? 0 : (len > p.L ? p.L : len);
+        }
+        e = s + len;
     }
 }
 

@@ -115,7 +115,18 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 // whole chunks: vector loads (rows and chunks are 16-byte aligned)
                 r.q[i] = *reinterpret_cast<const AV *>(qp + col0);
                 r.k[i] = *reinterpret_cast<const AV *>(kp + col0);
-                if constexpr (VD && PK) r.dec[i] = *reinterpret_cast<const FV *>(static_cast<const float *>(p.gate) + th * dk + col0);
+                if constexpr (VD && PK) {
+                    // a per-key raw gate comes in the activations' dtype (fp16 gates only with fp16 activations)
+                    bool f16_gate = false;
+                    if constexpr (sizeof(TA) == 2) f16_gate = p.gate_f16 != 0;
+                    if (f16_gate) {
+                        const AV gh = *reinterpret_cast<const AV *>(static_cast<const TA *>(p.gate) + th * dk + col0);
+#pragma unroll
+                        for (int c = 0; c < C; ++c) r.dec[i][c] = to_f32((TA)gh[c]);
+                    } else {
+                        r.dec[i] = *reinterpret_cast<const FV *>(static_cast<const float *>(p.gate) + th * dk + col0);
+                    }
+                }
                 if constexpr (RULE == GATED_DELTA_V2) r.er[i] = *reinterpret_cast<const FV *>(p.erase + th * dk + col0);
             } else {
                 // partial key rows: element loads with the column clamped into the row
@@ -124,7 +135,9 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                     const int col = col0 + c < dk ? col0 + c : dk - 1;
                     r.q[i][c] = qp[col];
                     r.k[i][c] = kp[col];
-                    if constexpr (VD && PK) r.dec[i][c] = static_cast<const float *>(p.gate)[th * dk + col];
+                    if constexpr (VD && PK)
+                        r.dec[i][c] = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[th * dk + col])
+                                                 : static_cast<const float *>(p.gate)[th * dk + col];
                     if constexpr (RULE == GATED_DELTA_V2) r.er[i][c] = p.erase[th * dk + col];
                 }
             }
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 // per-key decay: the per-key log decay, or the token's scalar one
                 // broadcast over the keys
                 float gs = 0.f;
-                if constexpr (!PK) gs = p.gate_qwen ? -expf(p.a_log[h]) * softplus_f32(s_sc[tau][3] + p.dt_bias[h])
+                if constexpr (!PK) gs = p.gate_qwen ? gate_scale(p, h) * softplus_f32(s_sc[tau][3] + p.dt_bias[h])
                                                     : s_sc[tau][3];
                 float av[C], kb[C];
 #pragma unroll
@@ -188,7 +201,9 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                     const bool in = live && col0 + c < dk;
                     float a = 1.f, er = 1.f;
                     if (in) {
-                        a = expf(PK ? r.dec[i][c] : gs);
+                        float g = gs;
+                        if constexpr (PK) g = p.gate_qwen ? key_decay_from_raw(p, r.dec[i][c], h, col0 + c) : r.dec[i][c];
+                        a = expf(g);
                         if constexpr (RULE == GATED_DELTA_V2) er = r.er[i][c];
                     }
                     av[c] = a;
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
         if (tid < NB) {
             float a = 1.f, bb = 1.f, graw = cur.g;
             if (tid < nb) {
-                if constexpr (DEC && !VD) a = expf(p.gate_qwen ? -expf(p.a_log[h]) * softplus_f32(graw + p.dt_bias[h]) : graw);
+                if constexpr (DEC && !VD) a = expf(p.gate_qwen ? gate_scale(p, h) * softplus_f32(graw + p.dt_bias[h]) : graw);
                 if constexpr (BETA) bb = p.beta_sigmoid ? sigmoid_f32(cur.bt) : cur.bt;
             }
             s_sc[tid][0] = a;

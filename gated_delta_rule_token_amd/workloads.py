@@ -13,7 +13,7 @@ suite is involved; these arrays are the whole workload.
 
 Each case is a plain dict:
   q, k, v, gate, beta, erase, a_log, dt_bias, cu_seqlens, slot_ids,
-  initial_state, slab  -- numpy arrays or None
+  initial_state, slab, gate_scale, seq_lens  -- numpy arrays or None
   update_rule, gate_activation, beta_activation, qk_l2_norm, scale,
   chunk_size, act_dtype, name -- attributes
 """
@@ -24,7 +24,7 @@ import numpy as np
 ATTR_KEYS = ("update_rule", "gate_activation", "beta_activation", "qk_l2_norm", "scale",
              "chunk_size")
 ARRAY_KEYS = ("q", "k", "v", "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens",
-              "slot_ids", "initial_state", "slab")
+              "slot_ids", "initial_state", "slab", "gate_scale", "seq_lens")
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -193,10 +193,13 @@ def odd_shape(seed: int = 5, dtype=np.float32):
 def random_case(seed, *, T=None, lengths=None, H=2, HV=4, DK=32, DV=32, dtype=np.float32,
                 update_rule="gated_delta", gate_activation="none", beta_activation="none",
                 qk_l2_norm=0, per_key=False, with_initial=True, unit_keys=True,
-                rank4_batch=None, slots=None):
+                rank4_batch=None, slots=None, seq_lens=None, folded_scale=False):
     """Generic small case for parity tests.  ``lengths`` gives varlen packing
-    (cu_seqlens); ``rank4_batch`` gives a uniform (B, L) batch; ``slots``
-    = (num_slots,) addresses a slab at distinct random ids."""
+    (cu_seqlens); ``rank4_batch`` gives a uniform (B, L) batch, optionally
+    bounded per request by ``seq_lens``; ``slots`` = (num_slots,) addresses a
+    slab at distinct random ids.  The raw-gate arm draws a per-head (or, with
+    a per-key gate, per (head, key channel)) bias; ``folded_scale`` passes
+    gate_scale = -exp(A_log) instead of A_log."""
     rng = rng_for(seed)
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
@@ -224,7 +227,10 @@ def random_case(seed, *, T=None, lengths=None, H=2, HV=4, DK=32, DV=32, dtype=np
         if gate_activation == "qwen":
             case["gate"] = _normal(rng, gshape, dtype)
             case["a_log"] = _log_uniform_alog(rng, HV)
-            case["dt_bias"] = rng.uniform(0.0, 1.0, size=HV).astype(np.float32)
+            case["dt_bias"] = rng.uniform(0.0, 1.0, size=(HV, DK) if per_key else HV).astype(np.float32)
+            if folded_scale:
+                case["gate_scale"] = (-np.exp(case["a_log"].astype(np.float64))).astype(np.float32)
+                case["a_log"] = None
         else:
             case["gate"] = _neg_softplus_scaled(_normal(rng, gshape), 0.5)
     if update_rule in ("delta", "gated_delta"):
@@ -238,6 +244,8 @@ def random_case(seed, *, T=None, lengths=None, H=2, HV=4, DK=32, DV=32, dtype=np
         case["slab"] = _normal(rng, (num_slots, HV, DV, DK), np.float32, std=0.1)
     elif with_initial:
         case["initial_state"] = _normal(rng, (B, HV, DV, DK), np.float32, std=0.1)
+    if seq_lens is not None:
+        case["seq_lens"] = np.asarray(seq_lens, dtype=np.int32)
     return case
 
 

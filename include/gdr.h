@@ -31,8 +31,11 @@
  *                   when gate_activation = QWEN and gate_dtype = act dtype
  *   beta            (T, HV)      fp32
  *   erase           (T, HV, dk)  fp32 (GATED_DELTA_V2 only)
- *   a_log, dt_bias  (HV)         fp32 (gate_activation = QWEN only)
+ *   a_log           (HV)         fp32 (gate_activation = QWEN, unless gate_scale)
+ *   gate_scale      (HV)         fp32: the once-folded -exp(a_log), instead of a_log
+ *   dt_bias         (HV), or (HV, dk) beside a per-key gate; fp32 (QWEN only)
  *   cu_seqlens      (B + 1)      int32, rank-3 spelling only
+ *   seq_lens        (B)          int32, uniform packing only
  *   slot_ids        (B)          int32
  *   initial_state   (B, HV, dv, dk) fp32, or NULL for a zero state
  *   final_state     (B, HV, dv, dk) fp32; with num_slots > 0 it is instead
@@ -46,7 +49,10 @@
  * [clamp(cu[b], 0, T), clamp(cu[b+1], 0, T)) and is empty when the end is not
  * past the start (README, Inputs cu_seqlens); the clamp happens on the
  * device, the host never reads cu_seqlens or slot_ids.  Without cu_seqlens
- * the packing is uniform: request b covers [b*L, (b+1)*L), T = B * L.  An
+ * the packing is uniform: request b covers [b*L, (b+1)*L), T = B * L, or only
+ * its first clamp(seq_lens[b], 0, L) tokens when seq_lens is given (CLIKA
+ * "gatedDeltaUpdate": seq_lens bounds ragged prefill rows; the padding rows'
+ * outputs are left unwritten, like tokens outside every request).  An
  * empty request copies its incoming state to final_state (README, Outputs);
  * o rows of tokens that no request covers are left unwritten.  A slot id
  * outside [0, num_slots) skips its request entirely (nothing read or
@@ -76,7 +82,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum {
     GDR_OK = 0,
@@ -98,7 +104,10 @@ typedef enum {
 } gdr_update_rule;
 
 /* README, Attributes gate_activation: NONE takes gate as the log decay g;
- * QWEN forms g = -exp(a_log[h]) * softplus(gate + dt_bias[h]) in fp32. */
+ * QWEN forms g = -exp(a_log[h]) * softplus(gate + dt_bias[h]) in fp32, or
+ * g = gate_scale[h] * softplus(gate + dt_bias[h]) with the folded scale, and
+ * with a per-key gate dt_bias[h][j] per key channel (CLIKA "gatedDeltaUpdate",
+ * the gate_bias / gate_scale arm). */
 typedef enum { GDR_GATE_NONE = 0, GDR_GATE_QWEN = 1 } gdr_gate_activation;
 
 /* README, Attributes beta_activation: NONE takes beta as the rate; SIGMOID
@@ -143,11 +152,13 @@ typedef struct {
     const void *gate;           /* NULL unless the rule decays */
     const float *beta;          /* NULL unless the rule is DELTA or GATED_DELTA */
     const float *erase;         /* NULL unless GATED_DELTA_V2 */
-    const float *a_log, *dt_bias; /* both or neither; both iff QWEN */
+    const float *a_log, *dt_bias; /* QWEN: dt_bias and exactly one of a_log, gate_scale */
     const int32_t *cu_seqlens;  /* NULL: uniform packing */
     const int32_t *slot_ids;    /* non-NULL iff num_slots > 0 */
     const float *initial_state; /* NULL: zero state; must be NULL with slots */
     float *final_state;         /* required: final state, or the slab */
+    const float *gate_scale;    /* (HV) folded -exp(a_log), or NULL */
+    const int32_t *seq_lens;    /* (B) valid tokens per request with uniform packing, or NULL */
 } gdr_tensors;
 
 /* ABI version of the loaded library (GDR_ABI_VERSION at build time). */
@@ -160,9 +171,10 @@ const char *gdr_status_str(gdr_status status);
 const char *gdr_last_error(void);
 
 /* Host-only argument check: presence rules (README, Inputs: gate present
- * exactly for decayed rules, beta exactly for DELTA/GATED_DELTA, a_log and
- * dt_bias exactly with QWEN -- CLIKA "gatedDeltaUpdate": one without the other
- * rejects), shapes, enum ranges, cu_seqlens only with the rank-3 spelling,
+ * exactly for decayed rules, beta exactly for DELTA/GATED_DELTA; with QWEN
+ * dt_bias plus one of a_log / gate_scale, without it none of them -- CLIKA
+ * "gatedDeltaUpdate": one without the other rejects), shapes, enum ranges,
+ * cu_seqlens only with the rank-3 spelling, seq_lens only without cu_seqlens,
  * state_update_capacity == 0, aliasing.  Reads no tensor memory and makes no
  * HIP call.  `tensors` may be NULL to check the problem alone. */
 gdr_status gdr_validate(const gdr_problem *problem, const gdr_tensors *tensors);

@@ -66,6 +66,8 @@ class _Problem(ctypes.Structure):
         ("initial_state", ctypes.c_void_p),
         ("o", ctypes.c_void_p),
         ("state", ctypes.c_void_p),
+        ("gate_scale", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
     ]
 
 
@@ -143,14 +145,16 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
             cu_seqlens=None, initial_state=None, slot_ids=None, slab=None,
             update_rule="gated_delta", gate_activation="none", beta_activation="none",
             qk_l2_norm=False, scale=0.0, batch=None, erase_axis="key", o_init=None,
-            row_block=16, lib=None):
+            row_block=16, lib=None, gate_scale=None, seq_lens=None):
     """Run the fp64 recurrence.
 
     q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv).
     gate: (T,HV) or (T,HV,dk) per-key (leading axes as q); beta: (T,HV);
     erase: (T,HV,dk).  cu_seqlens: (B+1) int.  initial_state: (B,HV,dv,dk).
     slot_ids + slab: slab (num_slots,HV,dv,dk) is updated in a copy that is
-    returned as the state.  Returns (o, state) as float64 arrays; o has q's
+    returned as the state.  Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a
+    per-key gate, with a_log (HV,) or the folded gate_scale (HV,).  seq_lens
+    (B,) bounds each uniform-packed request to its first seq_lens[b] tokens.  Returns (o, state) as float64 arrays; o has q's
     leading axes with (HV, dv) trailing.  Tokens no request covers keep
     ``o_init`` (zeros by default).
     """
@@ -177,6 +181,7 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     erase = flat(erase, (HV, DK))
     cu = _i32(cu_seqlens)
     sl = _i32(slot_ids)
+    lens = _i32(seq_lens)
 
     if cu is not None:
         if rank4:
@@ -189,6 +194,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
                 batch = np.asarray(initial_state).shape[0]
             elif sl is not None:
                 batch = len(sl)
+            elif lens is not None:
+                batch = len(lens)
             else:
                 batch = 1
         B = int(batch)
@@ -210,7 +217,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     keep = [q, k, v, gate, beta, erase, cu, sl, init, o, state]
     a_log = _f64(a_log)
     dt_bias = _f64(dt_bias)
-    keep += [a_log, dt_bias]
+    gscale = _f64(gate_scale)
+    keep += [a_log, dt_bias, gscale, lens]
     p = _Problem(
         T=T, B=B, L=L, H=H, HV=HV, DK=DK, DV=DV,
         rule=RULES[update_rule],
@@ -225,7 +233,7 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
         q=_ptr(q), k=_ptr(k), v=_ptr(v), gate=_ptr(gate), beta=_ptr(beta),
         erase=_ptr(erase), a_log=_ptr(a_log), dt_bias=_ptr(dt_bias),
         cu_seqlens=_ptr(cu), slot_ids=_ptr(sl), initial_state=_ptr(init),
-        o=_ptr(o), state=_ptr(state))
+        o=_ptr(o), state=_ptr(state), gate_scale=_ptr(gscale), seq_lens=_ptr(lens))
     rc = (lib if lib is not None else _load()).gdro_forward(ctypes.byref(p))
     del keep
     if rc != 0:

@@ -44,7 +44,7 @@ def _softplus(x):
 def forward_chunked(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
                     cu_seqlens=None, initial_state=None, update_rule="gated_delta",
                     gate_activation="none", beta_activation="none", qk_l2_norm=False,
-                    scale=0.0, chunk_size=64, batch=None):
+                    scale=0.0, chunk_size=64, batch=None, gate_scale=None):
     """Rank-3 inputs (T,H,dk)/(T,HV,dv); gate (T,HV) per head or (T,HV,dk) per
     key; erase (T,HV,dk) for gated_delta_v2.  Returns (o, state) with state
     V-major (B,HV,dv,dk), like ``oracle.forward``."""
@@ -69,12 +69,15 @@ def forward_chunked(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt
         per_key = gg.size == T * HV * DK and gg.size != T * HV
         gg = gg.reshape(T, HV, DK) if per_key else gg.reshape(T, HV)
         if gate_activation == "qwen":
-            al = np.asarray(a_log, np.float64)
+            # gate_scale is the once-folded -exp(a_log); the bias is (HV, dk)
+            # beside a per-key gate (CLIKA "gatedDeltaUpdate")
+            gs = (np.asarray(gate_scale, np.float64) if gate_scale is not None
+                  else -np.exp(np.asarray(a_log, np.float64)))
             db = np.asarray(dt_bias, np.float64)
             if per_key:
-                gg = -np.exp(al)[None, :, None] * _softplus(gg + db[None, :, None])
+                gg = gs[None, :, None] * _softplus(gg + db.reshape(HV, DK)[None, :, :])
             else:
-                gg = -np.exp(al)[None, :] * _softplus(gg + db[None, :])
+                gg = gs[None, :] * _softplus(gg + db[None, :])
         g = gg if per_key else np.repeat(gg[:, :, None], DK, axis=2)
     b = np.ones((T, HV))
     if has_beta:

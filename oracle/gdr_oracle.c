@@ -37,6 +37,9 @@
  * Gates ("com.microsoft.GatedDeltaNet" README, Attributes gate_activation and
  * beta_activation; "com.microsoft.LinearAttentionGate", Description):
  *   qwen:    g = -exp(a_log[h]) * softplus(raw[t,h] + dt_bias[h])
+ *            (CLIKA "gatedDeltaUpdate": gate_scale[h], the once-folded
+ *            -exp(a_log[h]), may be bound instead of a_log; beside a per-key
+ *            gate [T, HV, K] the bias is per key channel, dt_bias[h][j])
  *   sigmoid: beta = 1 / (1 + exp(-b))
  * qk_l2_norm (README, Attributes): x <- x / sqrt(sum x^2 + 1e-12).
  *
@@ -44,7 +47,9 @@
  * [clamp(cu[b],0,T), clamp(cu[b+1],0,T)); empty when the end is not past the
  * start, in which case its incoming state is copied to final_state (README,
  * Outputs final_state).  Without cu_seqlens the packing is uniform, L tokens
- * per request.  slot_ids (CLIKA "gatedDeltaUpdate"): request b reads and
+ * per request, or only the first seq_lens[b] of them (clamped to [0, L];
+ * CLIKA "gatedDeltaUpdate": seq_lens bounds ragged prefill rows; the rest
+ * of the request's rows produce no output).  slot_ids (same page): request b reads and
  * updates slab row slot_ids[b] in place; an id outside [0, num_slots) skips
  * the request (no state or output is touched).
  *
@@ -83,6 +88,8 @@ typedef struct {
     const double *initial_state;      /* (B,HV,DV,DK) or NULL (zeros); unused with slots */
     double *o;                        /* (T,HV,DV) */
     double *state;                    /* (B,HV,DV,DK) final state, or the slab in place */
+    const double *gate_scale;         /* (HV) folded -exp(a_log), or NULL (then a_log) */
+    const int32_t *seq_lens;          /* (B) valid tokens per uniform request, or NULL */
 } gdro_problem;
 
 static double softplus(double x)
@@ -116,8 +123,14 @@ static void request_range(const gdro_problem *p, int b, int64_t *s, int64_t *e)
         *s = a;
         *e = z > a ? z : a;
     } else {
+        int64_t len = p->L;
+        if (p->seq_lens) {
+            len = p->seq_lens[b];
+            if (len < 0) len = 0;
+            if (len > p->L) len = p->L;
+        }
         *s = (int64_t)b * p->L;
-        *e = *s + p->L;
+        *e = *s + len;
     }
 }
 
@@ -163,7 +176,12 @@ static void run_block(const gdro_problem *p, int b, int h, int r0, int r1,
             for (int j = 0; j < DK; ++j) {
                 double raw = p->per_key ? p->gate[((size_t)t * HV + h) * DK + j]
                                         : p->gate[(size_t)t * HV + h];
-                double g = p->gate_qwen ? -exp(p->a_log[h]) * softplus(raw + p->dt_bias[h]) : raw;
+                double g = raw;
+                if (p->gate_qwen) {
+                    double gs = p->gate_scale ? p->gate_scale[h] : -exp(p->a_log[h]);
+                    double bias = p->per_key ? p->dt_bias[(size_t)h * DK + j] : p->dt_bias[h];
+                    g = gs * softplus(raw + bias);
+                }
                 alpha[j] = exp(g);
             }
         }
@@ -212,7 +230,7 @@ int gdro_forward(const gdro_problem *p)
     if (has_decay(p->rule) && !p->gate) return -3;
     if (has_beta(p->rule) && !p->beta) return -4;
     if (p->rule == RULE_GATED_DELTA_V2 && !p->erase) return -5;
-    if (p->gate_qwen && (!p->a_log || !p->dt_bias)) return -6;
+    if (p->gate_qwen && ((!p->a_log && !p->gate_scale) || !p->dt_bias)) return -6;
     if (p->num_slots > 0 && !p->slot_ids) return -7;
     if (p->rule < RULE_LINEAR || p->rule > RULE_GATED_DELTA_V2) return -8;
     if (!p->cu_seqlens && (int64_t)p->B * p->L != p->T) return -9;

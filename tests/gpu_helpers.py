@@ -24,7 +24,7 @@ def to_dev(case):
     import torch
     dev = {}
     for key in ("q", "k", "v", "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens",
-                "slot_ids", "initial_state", "slab"):
+                "slot_ids", "initial_state", "slab", "gate_scale", "seq_lens"):
         x = case.get(key)
         dev[key] = None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
     return dev
@@ -42,7 +42,8 @@ def gpu_forward(case, algo="auto", dev=None, **over):
               slot_ids=d["slot_ids"], state=slab, update_rule=case["update_rule"],
               gate_activation=case["gate_activation"], beta_activation=case["beta_activation"],
               qk_l2_norm=case["qk_l2_norm"], scale=case["scale"],
-              chunk_size=case.get("chunk_size", 64), algo=algo)
+              chunk_size=case.get("chunk_size", 64), algo=algo,
+              gate_scale=d.get("gate_scale"), seq_lens=d.get("seq_lens"))
     kw.update(over)
     o, st = api.forward(d["q"], d["k"], d["v"], **kw)
     torch.cuda.synchronize()
@@ -55,7 +56,7 @@ def oracle_forward(case, **over):
               initial_state=case["initial_state"], slot_ids=case["slot_ids"], slab=case["slab"],
               update_rule=case["update_rule"], gate_activation=case["gate_activation"],
               beta_activation=case["beta_activation"], qk_l2_norm=case["qk_l2_norm"],
-              scale=case["scale"])
+              scale=case["scale"], gate_scale=case.get("gate_scale"), seq_lens=case.get("seq_lens"))
     kw.update(over)
     return oracle.forward(case["q"], case["k"], case["v"], **kw)
 
@@ -70,6 +71,9 @@ def request_ranges(case):
     else:
         B = case["initial_state"].shape[0] if case["initial_state"] is not None else 1
         L = T // B
+    lens = case.get("seq_lens")
+    if lens is not None:
+        return [(b * L, b * L + int(min(max(lens[b], 0), L))) for b in range(B)]
     return [(b * L, (b + 1) * L) for b in range(B)]
 
 
@@ -96,8 +100,9 @@ def sub_case(case, b, heads):
     for key in ("gate", "beta", "erase"):
         x = tok(case[key])
         out[key] = None if x is None else np.ascontiguousarray(x[:, heads])
-    for key in ("a_log", "dt_bias"):
-        out[key] = None if case[key] is None else case[key][heads]
+    for key in ("a_log", "dt_bias", "gate_scale"):
+        out[key] = None if case.get(key) is None else case[key][heads]
+    out["seq_lens"] = None
     out["cu_seqlens"] = np.array([0, e - s], dtype=np.int32)
     if case["slab"] is not None:
         init = case["slab"][case["slot_ids"][b]][None]

@@ -234,6 +234,32 @@ def pin_varlen_packing(fwd):
     _close(st_c[2], st_b[0], 0.0, "entry past T is clamped to T")
 
 
+def pin_seq_lens(fwd):
+    """seq_lens bounds each uniform-packed request to its first tokens (CLIKA
+    "gatedDeltaUpdate"): the same as packing those prefixes with cu_seqlens;
+    padding rows keep whatever o held; a zero length copies the state; lengths
+    outside [0, L] clamp."""
+    r = _rng(17)
+    B, L, H, HV, DK, DV = 4, 7, 1, 2, 5, 3
+    q, k = r.standard_normal((B, L, H, DK)), _unit(r.standard_normal((B, L, H, DK)))
+    v = r.standard_normal((B, L, HV, DV))
+    g, beta = -r.uniform(0, 1, (B, L, HV)), r.uniform(0, 1, (B, L, HV))
+    S0 = r.standard_normal((B, HV, DV, DK))
+    lens = np.array([12, 3, 0, 6], dtype=np.int32)      # 12 clamps to 7
+    sentinel = np.full((B, L, HV, DV), 5.5)
+    o, st = fwd(q, k, v, gate=g, beta=beta, initial_state=S0, seq_lens=lens, o_init=sentinel)
+    eff = np.minimum(np.maximum(lens, 0), L)
+    flat = lambda x: np.concatenate([x[b, :eff[b]] for b in range(B)])
+    cu = np.concatenate([[0], np.cumsum(eff)]).astype(np.int32)
+    o2, st2 = fwd(flat(q), flat(k), flat(v), gate=flat(g), beta=flat(beta), initial_state=S0,
+                  cu_seqlens=cu)
+    _close(flat(o), o2, 1e-14, "seq_lens o")
+    _close(st, st2, 1e-14, "seq_lens state")
+    for b in range(B):
+        assert np.array_equal(o[b, eff[b]:], sentinel[b, eff[b]:]), "padding rows must keep o"
+    _close(st[2], S0[2], 0.0, "zero-length request copies its state")
+
+
 def pin_slots(fwd):
     r = _rng(8)
     B, L, H, HV, DK, DV, NS = 3, 4, 1, 2, 4, 3, 7
@@ -271,6 +297,20 @@ def pin_gate_arms(fwd):
     o2, st2 = fwd(q, k, v, gate=decay, beta=_expit(braw))
     _close(o, o2, 1e-13, "qwen/sigmoid arms o")
     _close(st, st2, 1e-13, "qwen/sigmoid arms state")
+    # the folded scale (CLIKA "gatedDeltaUpdate": gate_scale = -exp(A_log)) is the same arm
+    o3, st3 = fwd(q, k, v, gate=a, gate_scale=-np.exp(a_log), dt_bias=dt_bias,
+                  gate_activation="qwen", beta=braw, beta_activation="sigmoid")
+    _close(o3, o2, 1e-13, "gate_scale arm o")
+    _close(st3, st2, 1e-13, "gate_scale arm state")
+    # per-key raw gate with its [HV, K] bias (same page): decay per key channel
+    ak = 3.0 * r.standard_normal((T, HV, DK))
+    bias_k = r.uniform(-1, 1, (HV, DK))
+    o4, st4 = fwd(q, k, v, gate=ak, a_log=a_log, dt_bias=bias_k, gate_activation="qwen",
+                  beta=braw, beta_activation="sigmoid")
+    dk_ = -np.exp(a_log)[None, :, None] * _softplus(ak + bias_k[None, :, :])
+    o5, st5 = fwd(q, k, v, gate=dk_, beta=_expit(braw))
+    _close(o4, o5, 1e-13, "per-key qwen arm o")
+    _close(st4, st5, 1e-13, "per-key qwen arm state")
 
 
 def pin_l2_norm(fwd):
@@ -388,13 +428,17 @@ def pin_chunked_equivalence(fwd):
     erase = r.uniform(0, 1, (T, HV, DK))
     raw = r.standard_normal((T, HV, DK))
     a_log, dt_bias = np.log(r.uniform(1, 16, HV)), r.uniform(0, 1, HV)
+    bias_k = r.uniform(-1, 1, (HV, DK))
     cases = [
         ("gated_delta per-key", dict(update_rule="gated_delta", gate=gk, beta=beta)),
         ("gated per-key", dict(update_rule="gated", gate=gk)),
         ("gated_delta_v2 per-key", dict(update_rule="gated_delta_v2", gate=gk, erase=erase)),
         ("gated_delta_v2 per-head", dict(update_rule="gated_delta_v2", gate=g, erase=erase)),
         ("gated_delta per-key qwen", dict(update_rule="gated_delta", gate=raw, beta=beta,
-                                          gate_activation="qwen", a_log=a_log, dt_bias=dt_bias)),
+                                          gate_activation="qwen", a_log=a_log, dt_bias=bias_k)),
+        ("gated_delta_v2 per-key folded scale", dict(update_rule="gated_delta_v2", gate=raw, erase=erase,
+                                                     gate_activation="qwen", gate_scale=-np.exp(a_log),
+                                                     dt_bias=bias_k)),
     ]
     for name, kw in cases:
         kw.update(initial_state=S0, cu_seqlens=cu)
@@ -432,7 +476,7 @@ def pin_row_split_invariance(fwd):
 
 ALL_PINS = [
     pin_golden_hand, pin_linear_closed_form, pin_gated_closed_form, pin_delta_invariant,
-    pin_beta_zero, pin_orthonormal_keys, pin_gqa_mapping, pin_varlen_packing, pin_slots,
+    pin_beta_zero, pin_orthonormal_keys, pin_gqa_mapping, pin_varlen_packing, pin_seq_lens, pin_slots,
     pin_gate_arms, pin_l2_norm, pin_scale, pin_rule_reductions, pin_v2_reductions,
     pin_chunked_equivalence, pin_kmajor_cross, pin_row_split_invariance,
 ]

@@ -396,3 +396,55 @@ def test_chunked_per_key_matches_recurrent_and_is_deterministic():
 def test_perkey_erase_workload_full_chunked():
     case = workloads.perkey_erase()
     _sampled(case, "chunked", [(0, [0, 3]), (2, [17]), (3, [31])], TOL_CHUNKED, "perkey+erase chunked")
+
+
+# ------------------------------------------------------------------ raw per-key gate, folded scale, seq_lens
+# (CLIKA "gatedDeltaUpdate": gate_bias [HV, K] beside a [B, T, HV, K] gate,
+# gate_scale = the once-folded -exp(A_log), seq_lens bounding ragged rows)
+RAW_GATE_CASES = [("decode", 1), ("recurrent", 70), ("chunked", 150)]
+
+
+@pytest.mark.parametrize("algo,L", RAW_GATE_CASES, ids=[c[0] for c in RAW_GATE_CASES])
+@pytest.mark.parametrize("rule", ["gated_delta", "gated_delta_v2"])
+def test_per_key_raw_gate_folded_scale(algo, L, rule):
+    case = workloads.random_case(zlib.crc32(("rawpk/%s/%s" % (algo, rule)).encode()) % 1000,
+                                 rank4_batch=(3, L), H=2, HV=4, DK=128, DV=128, dtype=np.float16,
+                                 update_rule=rule, per_key=True, gate_activation="qwen",
+                                 beta_activation="sigmoid" if rule == "gated_delta" else "none",
+                                 folded_scale=True)
+    assert case["gate"].dtype == np.float16 and case["dt_bias"].shape == (4, 128)
+    _check_full(case, algo, "per-key raw gate %s %s" % (rule, algo))
+
+
+SEQ_LEN_CASES = [("decode", 6, [6, 0, 3, 9]), ("recurrent", 90, [90, 1, 0, 37]),
+                 ("chunked", 200, [200, 64, 0, 129]), ("chunked_pk", 200, [130, 0, 199, 65])]
+
+
+@pytest.mark.parametrize("algo,L,lens", SEQ_LEN_CASES, ids=[c[0] for c in SEQ_LEN_CASES])
+def test_seq_lens_bound_uniform_requests(algo, L, lens):
+    per_key = algo == "chunked_pk"
+    case = workloads.random_case(zlib.crc32(("seqlens/%s" % algo).encode()) % 1000,
+                                 rank4_batch=(4, L), H=2, HV=4, DK=128, DV=128, dtype=np.float16,
+                                 update_rule="gated_delta_v2" if per_key else "gated_delta",
+                                 per_key=per_key, gate_activation="none" if per_key else "qwen",
+                                 beta_activation="none" if per_key else "sigmoid",
+                                 seq_lens=lens, slots=(9,) if algo == "decode" else None)
+    import torch
+    sentinel = np.full(case["v"].shape, 3.0, dtype=np.float16)
+    out = torch.from_numpy(sentinel.copy()).cuda()
+    say("case %s seq_lens %s" % (case["name"], lens))
+    o, st = gpu_forward(case, "chunked" if per_key else algo, out=out)
+    ro, rs = oracle_forward(case, o_init=sentinel)
+    assert_close(o, ro, TOL_F16 if algo in ("decode", "recurrent") else TOL_CHUNKED, "seq_lens o")
+    if case["slab"] is not None:
+        ids = case["slot_ids"]
+        assert_close(st[ids], rs[ids], TOL_F16, "seq_lens slab rows")
+    else:
+        assert_close(st, rs, TOL_F16 if algo == "recurrent" else TOL_CHUNKED, "seq_lens state")
+    for b, n in enumerate(lens):
+        n = min(max(n, 0), L)
+        assert np.all(o[b, n:] == 3.0), "rows past seq_lens[%d] must stay unwritten" % b
+    if case["initial_state"] is not None:
+        z = lens.index(0)
+        assert np.array_equal(st[z], case["initial_state"][z].astype(np.float64)), \
+            "a zero-length request copies its state"

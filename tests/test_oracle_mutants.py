@@ -24,8 +24,12 @@ MUTANTS = [
     ("retrieve_before_decay", "r += Si[j] * kn[j];", "r += Si[j] / alpha[j] * kn[j];"),
     ("retrieve_with_query", "r += Si[j] * kn[j];", "r += Si[j] * qn[j];"),
     ("gqa_modulo", "(int)(((int64_t)h * H) / HV);", "h % H;"),
-    ("softplus_bias_sign", "softplus(raw + p->dt_bias[h])", "softplus(raw - p->dt_bias[h])"),
-    ("decay_scale_no_exp", "-exp(p->a_log[h]) * softplus", "-p->a_log[h] * softplus"),
+    ("softplus_bias_sign", "softplus(raw + bias)", "softplus(raw - bias)"),
+    ("decay_scale_no_exp", ": -exp(p->a_log[h]);", ": -p->a_log[h];"),
+    ("per_key_bias_per_head", "p->dt_bias[(size_t)h * DK + j]", "p->dt_bias[h]"),
+    ("gate_scale_ignored", "p->gate_scale ? p->gate_scale[h]", "p->gate_scale ? -1.0"),
+    ("seq_lens_ignored", "len = p->seq_lens[b];", "len = p->L;"),
+    ("seq_lens_no_upper_clamp", "if (len > p->L) len = p->L;", "if (len > 100000) len = p->L;"),
     ("sigmoid_sign", "1.0 / (1.0 + exp(-x))", "1.0 / (1.0 + exp(x))"),
     ("l2_no_sqrt", "1.0 / sqrt(qss + 1e-12)", "1.0 / (qss + 1e-12)"),
     ("erase_value_axis", "if (bt && !p->erase_value_axis)", "if (bt && p->erase_value_axis)"),
