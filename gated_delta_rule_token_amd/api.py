@@ -57,6 +57,7 @@ class Problem(ctypes.Structure):
         ("chunk_size", ctypes.c_int32),
         ("algo", ctypes.c_int32),
         ("state_update_capacity", ctypes.c_int32),
+        ("beta_per_token", ctypes.c_int32),
         ("scale", ctypes.c_float),
     ]
 
@@ -170,6 +171,8 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
             L = T // B if B else 0
     HV, dv = v.shape[-2], v.shape[-1]
     per_key = gate is not None and gate.dim() == q.dim()
+    # beta (..., 1): one update rate per token for every value head
+    beta_tok = beta is not None and HV > 1 and beta.dim() == q.dim() - 1 and beta.shape[-1] == 1
     p = Problem(
         total_tokens=T, batch=B, seq_len=L, num_heads_qk=H, num_heads_v=HV, head_dim_k=dk,
         head_dim_v=dv, num_slots=0 if state is None else state.shape[0],
@@ -178,7 +181,7 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
         update_rule=RULES[update_rule], gate_activation=GATES[gate_activation],
         beta_activation=BETAS[beta_activation], qk_l2_norm=int(bool(qk_l2_norm)),
         decay_per_key=int(per_key), rank4=int(rank4), chunk_size=int(chunk_size),
-        algo=ALGOS[algo], state_update_capacity=0, scale=float(scale))
+        algo=ALGOS[algo], state_update_capacity=0, beta_per_token=int(beta_tok), scale=float(scale))
     return p
 
 
@@ -203,7 +206,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
 
     q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
     decay, or the raw projection with gate_activation='qwen'): (...,HV) or
-    per key (...,HV,dk); beta: (...,HV) fp32; erase: (...,HV,dk) fp32.
+    per key (...,HV,dk); beta: (...,HV) fp32, or (...,1) for one rate per
+    token; erase: (...,HV,dk) fp32.
     Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a per-key gate, and either
     a_log (HV,) or the folded gate_scale = -exp(a_log) (HV,).  seq_lens (B,)
     int32 bounds each uniform-packed request to its first seq_lens[b] tokens

@@ -58,6 +58,9 @@ gdr_status check_problem(const gdr_problem *p)
     if (!p) return fail(GDR_E_INVALID, "problem is NULL");
     if (p->state_update_capacity != 0)
         return fail(GDR_E_UNSUPPORTED, "state_update_capacity must be 0 (compact capture is not implemented)");
+    if (p->beta_per_token != 0 && p->beta_per_token != 1) return fail(GDR_E_INVALID, "beta_per_token must be 0 or 1");
+    if (p->beta_per_token && !gdr::rule_has_beta(p->update_rule))
+        return fail(GDR_E_INVALID, "beta_per_token given to an update_rule without beta");
     if (p->act_dtype != GDR_F32 && p->act_dtype != GDR_F16)
         return fail(GDR_E_INVALID, "act_dtype must be GDR_F32 or GDR_F16");
     if (p->gate_dtype != GDR_F32 && p->gate_dtype != p->act_dtype)
@@ -152,7 +155,7 @@ gdr_status check_tensors(const gdr_problem *p, const gdr_tensors *t)
         rng("k", t->k, (size_t)T * H * dk * a),
         rng("v", t->v, (size_t)T * HV * dv * a),
         rng("gate", t->gate, (size_t)T * HV * (p->decay_per_key ? dk : 1) * dsize(p->gate_dtype)),
-        rng("beta", t->beta, (size_t)T * HV * 4),
+        rng("beta", t->beta, (size_t)T * (p->beta_per_token ? 1 : HV) * 4),
         rng("erase", t->erase, (size_t)T * HV * dk * 4),
         rng("a_log", t->a_log, (size_t)HV * 4),
         rng("gate_scale", t->gate_scale, (size_t)HV * 4),
@@ -288,6 +291,7 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     k.gate_f16 = p.gate_dtype == GDR_F16;
     k.beta_sigmoid = p.beta_activation == GDR_BETA_SIGMOID;
     k.qk_l2_norm = p.qk_l2_norm != 0;
+    k.beta_bcast = p.beta_per_token != 0;
     k.scale = p.scale != 0.f ? p.scale : 1.f / std::sqrt((float)p.head_dim_k);
     if (p.batch == 0) return GDR_OK;
 

@@ -38,6 +38,7 @@ struct Params {
     int64_t T;
     int32_t B, L, H, HV, dk, dv, num_slots;
     int32_t gate_qwen, gate_f16, beta_sigmoid, qk_l2_norm;
+    int32_t beta_bcast;        // 1: beta is (T, 1), one update rate per token for every head
     float scale;
 };
 
@@ -121,9 +122,17 @@ __device__ __forceinline__ float log_decay_key(const Params &p, size_t th, int h
     return p.gate_qwen ? key_decay_from_raw(p, x, h, j) : x;
 }
 
-__device__ __forceinline__ float update_rate(const Params &p, size_t idx)
+// Element of beta for token-head th (= t * HV + h); a (T, 1) beta is one rate
+// per token for every value head (the ONNX issue's LinearAttention schema
+// restricts beta's last axis to {kv_num_heads, 1}).
+__device__ __forceinline__ size_t beta_index(const Params &p, size_t th)
 {
-    float b = p.beta[idx];
+    return p.beta_bcast ? th / (size_t)p.HV : th;
+}
+
+__device__ __forceinline__ float update_rate(const Params &p, size_t th)
+{
+    float b = p.beta[beta_index(p, th)];
     return p.beta_sigmoid ? sigmoid_f32(b) : b;
 }
 

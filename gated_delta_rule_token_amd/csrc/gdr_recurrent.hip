@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
             const size_t th = (size_t)tok(tb0 + (tid < NB ? tid : NB - 1)) * HV + h;
             if constexpr (DEC && (!VD || !PK)) r.g = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[th])
                                                                  : static_cast<const float *>(p.gate)[th];
-            if constexpr (BETA) r.bt = p.beta[th];
+            if constexpr (BETA) r.bt = p.beta[beta_index(p, th)];
         }
     };
     // LDS operands of the block starting at tb0 (nb valid tokens) from its raw inputs

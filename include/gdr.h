@@ -29,7 +29,9 @@
  *   v, o            (T, HV, dv)  act dtype
  *   gate            (T, HV) or (T, HV, dk) per key; fp32, or the act dtype
  *                   when gate_activation = QWEN and gate_dtype = act dtype
- *   beta            (T, HV)      fp32
+ *   beta            (T, HV) fp32, or (T, 1) with beta_per_token: one rate per
+ *                   token for every value head (the ONNX issue's LinearAttention
+ *                   schema allows beta's last axis in {kv_num_heads, 1})
  *   erase           (T, HV, dk)  fp32 (GATED_DELTA_V2 only)
  *   a_log           (HV)         fp32 (gate_activation = QWEN, unless gate_scale)
  *   gate_scale      (HV)         fp32: the once-folded -exp(a_log), instead of a_log
@@ -143,6 +145,7 @@ typedef struct {
     int32_t chunk_size;         /* scheduling hint for GDR_ALGO_CHUNKED (0 -> 64) */
     int32_t algo;               /* gdr_algo */
     int32_t state_update_capacity; /* must be 0 (README, Attributes) */
+    int32_t beta_per_token;     /* 1: beta is (T, 1), shared by every value head */
     float scale;                /* 0 -> 1 / sqrt(dk) (README, Attributes) */
 } gdr_problem;
 

@@ -177,6 +177,9 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
 
     per_key = gate is not None and np.asarray(gate).ndim == len(lead) + 2
     gate = flat(gate, (HV, DK) if per_key else (HV,))
+    if beta is not None and np.asarray(beta).shape[-1] == 1 and HV > 1:
+        # (..., 1): one update rate per token for every value head
+        beta = np.broadcast_to(np.asarray(beta), lead + (HV,))
     beta = flat(beta, (HV,))
     erase = flat(erase, (HV, DK))
     cu = _i32(cu_seqlens)

@@ -105,6 +105,9 @@ BAD = [
     ("gate_scale_without_qwen", dict(gate_activation=0, a_log=None, dt_bias=None,
                                      gate_scale=_fake(13)), api.GDR_E_INVALID),
     ("seq_lens_with_cu_seqlens", dict(seq_lens=_fake(14)), api.GDR_E_INVALID),
+    ("beta_per_token_without_beta", dict(update_rule=api.RULES["gated"], beta=None, beta_activation=0,
+                                         beta_per_token=1), api.GDR_E_INVALID),
+    ("beta_per_token_value", dict(beta_per_token=2), api.GDR_E_INVALID),
     ("dt_bias_aliases_o_per_key", dict(decay_per_key=1, o=_fake(8) + 256), api.GDR_E_ALIAS),
     ("decode_needs_128", dict(algo=api.ALGOS["decode"]), api.GDR_E_UNSUPPORTED),
     ("chunked_needs_128_f16", dict(algo=api.ALGOS["chunked"]), api.GDR_E_UNSUPPORTED),
@@ -148,6 +151,9 @@ def test_raw_gate_spellings_and_seq_lens(lib):
     p, t = _good(cu_seqlens=None, seq_len=8, seq_lens=_fake(14))
     assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
     p.rank4 = 1
+    assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
+    # beta (T, 1) shared by the value heads
+    p, t = _good(beta_per_token=1)
     assert _validate(lib, p, t) == api.GDR_OK, lib.gdr_last_error()
 
 

@@ -448,3 +448,21 @@ def test_seq_lens_bound_uniform_requests(algo, L, lens):
         z = lens.index(0)
         assert np.array_equal(st[z], case["initial_state"][z].astype(np.float64)), \
             "a zero-length request copies its state"
+
+
+# beta (..., 1): one update rate per token for every value head (the ONNX
+# issue quotes LinearAttention's schema: beta's last axis in {kv_num_heads, 1})
+BETA_TOK_CASES = [("decode", 2, False), ("recurrent", 50, False), ("chunked", 140, False),
+                  ("chunked", 140, True)]
+
+
+@pytest.mark.parametrize("algo,L,per_key", BETA_TOK_CASES,
+                         ids=["%s%s" % (c[0], "_pk" if c[2] else "") for c in BETA_TOK_CASES])
+def test_beta_one_per_token(algo, L, per_key):
+    case = workloads.random_case(zlib.crc32(("betatok/%s/%d" % (algo, per_key)).encode()) % 1000,
+                                 rank4_batch=(3, L), H=2, HV=4, DK=128, DV=128, dtype=np.float16,
+                                 update_rule="gated_delta", per_key=per_key,
+                                 beta_activation="sigmoid")
+    case["beta"] = np.ascontiguousarray(case["beta"][..., :1])
+    assert case["beta"].shape == (3, L, 1)
+    _check_full(case, algo, "beta per token %s%s" % (algo, " per-key" if per_key else ""))
