@@ -1000,11 +1000,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const uint32_t offQ = RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16;
         // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
         const int tok_bytes = HV * D128 * 2;
-        // after the LDS transpose each lane stores 16 bytes: token 16 tb + (lane >> 2),
-        // rows 8 (lane & 3) .. +7 of the tile (TR = 32: four lanes per token)
-        static_assert(TR == 32, "the output transpose assumes 32-row tiles");
-        const int st_tok = lane >> 2, st_q = lane & 3;
-        const uint32_t offO = (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q);
+        // after the LDS transpose each lane stores 16 bytes (8 rows of a token):
+        // TR / 8 lanes per token, so a 32-row tile uses every lane for its 16
+        // tokens and a 16-row tile the first 32 lanes; the others get an offset
+        // past the store's range, which the buffer store drops
+        static_assert(TR == 32 || TR == 16, "the output transpose takes 16- or 32-row tiles");
+        constexpr int LPT = TR / 8;
+        const bool st_live = lane / LPT < 16;
+        const int st_tok = st_live ? lane / LPT : 15, st_q = lane % LPT;
+        const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
         const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         auto fetch = [&](int jj, Ops &f) {
@@ -1116,9 +1120,10 @@ size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key)
     return table + (size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE);
 }
 
-// Row tile of the scan: 32 rows (measured on MI355X: 64-row tiles halve the
-// per-row operand reads but lengthen each chunk step by 1.7x, which loses on
-// both the single long sequence and the batched prefill).
+// Row tile of the scan: 16 * NVB rows, NVB = 1 or 2 (measured on MI355X:
+// 64-row tiles halve the per-row operand reads but lengthen each chunk step
+// by 1.7x, which loses on both the single long sequence and the batched
+// prefill).
 template <int RULE, int NVB, bool PK>
 static void launch_scan(const Params &p, const int32_t *off, const char *rec, hipStream_t s)
 {
@@ -1145,7 +1150,13 @@ static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
         else
             hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)(maxch * p.HV)), dim3(256), 0, s, p, off, rec);
     }
-    launch_scan<RULE, 2, PK>(p, off, rec, s);
+    // Few (request, head) pairs leave most CUs idle with 32-row tiles; 16-row
+    // tiles double the workgroups and shorten each chunk step (measured on
+    // MI355X: one 65,536-token sequence x 16 heads 2.65 -> 2.18 ms), while with
+    // many pairs the GPU is full and the larger tiles amortise the operand reads
+    // (8 x 32 heads: 1.27 ms with 32-row tiles, 1.47 ms with 16-row tiles).
+    if ((int64_t)p.B * p.HV <= 32) launch_scan<RULE, 1, PK>(p, off, rec, s);
+    else launch_scan<RULE, 2, PK>(p, off, rec, s);
     return hipGetLastError();
 }
 
