@@ -369,6 +369,19 @@ def test_chunked_per_key_strong_decay(rule):
     _check_full(case, "chunked", "chunked per-key strong decay %s" % rule)
 
 
+def test_chunked_per_key_growing_channels():
+    """Channels whose log decay alternates +5 / -5 per token grow by more than
+    80 nats inside a chunk in total (while their state stays bounded), which
+    sends every Gram block of those chunks to the term-by-term path."""
+    case = workloads.random_case(78, lengths=[150, 70], H=2, HV=4, DK=128, DV=128,
+                                 dtype=np.float16, update_rule="gated_delta_v2", per_key=True)
+    g = case["gate"].copy()
+    sign = np.where(np.arange(g.shape[0]) % 2 == 0, 5.0, -5.0).astype(np.float32)
+    g[:, :, 3::9] = sign[:, None, None]
+    case["gate"] = g
+    _check_full(case, "chunked", "chunked per-key growing channels")
+
+
 def test_chunked_per_key_gqa_and_slab():
     case = workloads.random_case(43, rank4_batch=(3, 150), H=2, HV=8, DK=128, DV=128,
                                  dtype=np.float16, update_rule="gated_delta_v2", per_key=True,
