@@ -22,7 +22,7 @@ _lib = None
 
 ABI_VERSION = 2  # GDR_ABI_VERSION of include/gdr.h the structs below mirror
 GDR_OK, GDR_E_INVALID, GDR_E_UNSUPPORTED, GDR_E_ALIAS, GDR_E_WORKSPACE, GDR_E_HIP = range(6)
-F32, F16 = 0, 1
+F32, F16, BF16 = 0, 1, 2
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3, "gated_delta_v2": 4}
 GATES = {"none": 0, "qwen": 1}
 BETAS = {"none": 0, "sigmoid": 1}
@@ -124,7 +124,9 @@ def _dtype_code(dt):
         return F32
     if dt == torch.float16:
         return F16
-    raise GDRError("GDR_E_INVALID", "unsupported dtype %s (float32 or float16)" % dt)
+    if dt == torch.bfloat16:
+        return BF16
+    raise GDRError("GDR_E_INVALID", "unsupported dtype %s (float32, float16 or bfloat16)" % dt)
 
 
 def _need(t, name, dtype=None, device=None):

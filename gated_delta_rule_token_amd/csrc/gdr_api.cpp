@@ -29,7 +29,7 @@ gdr_status fail(gdr_status st, const char *fmt, ...)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t dsize(int32_t dt) { return dt == GDR_F16 ? 2 : 4; }
+size_t dsize(int32_t dt) { return dt == GDR_F32 ? 4 : 2; }
 
 struct Range {
     const char *name;
@@ -61,8 +61,8 @@ gdr_status check_problem(const gdr_problem *p)
     if (p->beta_per_token != 0 && p->beta_per_token != 1) return fail(GDR_E_INVALID, "beta_per_token must be 0 or 1");
     if (p->beta_per_token && !gdr::rule_has_beta(p->update_rule))
         return fail(GDR_E_INVALID, "beta_per_token given to an update_rule without beta");
-    if (p->act_dtype != GDR_F32 && p->act_dtype != GDR_F16)
-        return fail(GDR_E_INVALID, "act_dtype must be GDR_F32 or GDR_F16");
+    if (p->act_dtype != GDR_F32 && p->act_dtype != GDR_F16 && p->act_dtype != GDR_BF16)
+        return fail(GDR_E_INVALID, "act_dtype must be GDR_F32, GDR_F16 or GDR_BF16");
     if (p->gate_dtype != GDR_F32 && p->gate_dtype != p->act_dtype)
         return fail(GDR_E_INVALID, "gate_dtype must be GDR_F32 or the activation dtype");
     if (p->update_rule < GDR_RULE_LINEAR || p->update_rule > GDR_RULE_GATED_DELTA_V2)
@@ -288,21 +288,21 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     k.dv = p.head_dim_v;
     k.num_slots = p.num_slots;
     k.gate_qwen = p.gate_activation == GDR_GATE_QWEN;
-    k.gate_f16 = p.gate_dtype == GDR_F16;
+    k.gate_dt = p.gate_dtype == GDR_F16 ? 1 : p.gate_dtype == GDR_BF16 ? 2 : 0;
     k.beta_sigmoid = p.beta_activation == GDR_BETA_SIGMOID;
     k.qk_l2_norm = p.qk_l2_norm != 0;
     k.beta_bcast = p.beta_per_token != 0;
     k.scale = p.scale != 0.f ? p.scale : 1.f / std::sqrt((float)p.head_dim_k);
     if (p.batch == 0) return GDR_OK;
 
-    const bool f16 = p.act_dtype == GDR_F16;
+    const int act = p.act_dtype == GDR_F16 ? 1 : p.act_dtype == GDR_BF16 ? 2 : 0;
     const bool pk = p.decay_per_key != 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (pick_algo(problem)) {
-    case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, f16, s); break;
+    case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, act, s); break;
     case GDR_ALGO_CHUNKED: err = gdr::launch_chunked(k, p.update_rule, pk, workspace, s); break;
-    default: err = gdr::launch_recurrent(k, p.update_rule, pk, f16, dk_tile(p.head_dim_k), rows_group(problem), s); break;
+    default: err = gdr::launch_recurrent(k, p.update_rule, pk, act, dk_tile(p.head_dim_k), rows_group(problem), s); break;
     }
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GDR_OK;
@@ -314,10 +314,11 @@ gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a, 
     g_last_error.clear();
     if (count < 0 || heads < 1) return fail(GDR_E_INVALID, "count must be >= 0 and heads >= 1");
     if (count % heads != 0) return fail(GDR_E_INVALID, "count must be a multiple of heads (last axis)");
-    if (dtype != GDR_F32 && dtype != GDR_F16) return fail(GDR_E_INVALID, "dtype must be GDR_F32 or GDR_F16");
+    if (dtype != GDR_F32 && dtype != GDR_F16 && dtype != GDR_BF16)
+        return fail(GDR_E_INVALID, "dtype must be GDR_F32, GDR_F16 or GDR_BF16");
     if (count > 0 && (!a || !dt_bias || !decay_scale || !decay)) return fail(GDR_E_INVALID, "a, dt_bias, decay_scale and decay are required");
     if (beta && !b) return fail(GDR_E_INVALID, "beta requested without b");
-    hipError_t err = gdr::launch_gate(count, heads, dtype == GDR_F16, a, dt_bias, decay_scale, beta ? b : nullptr,
+    hipError_t err = gdr::launch_gate(count, heads, dtype == GDR_F16 ? 1 : dtype == GDR_BF16 ? 2 : 0, a, dt_bias, decay_scale, beta ? b : nullptr,
                                       decay, beta, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GDR_OK;

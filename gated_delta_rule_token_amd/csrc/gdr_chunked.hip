@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         if (r < n) {
             const size_t th = (size_t)(t0 + r) * HV + h;
             if constexpr (PKG) {
-                if (!p.gate_f16 && !p.gate_qwen) {
+                if (p.gate_dt == 0 && !p.gate_qwen) {
                     ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
                 } else {
 #pragma unroll

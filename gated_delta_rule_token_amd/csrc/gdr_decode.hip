@@ -221,9 +221,11 @@ static hipError_t by_rule(const Params &p, int rule, bool pk, hipStream_t s)
     }
 }
 
-hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s)
+hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hipStream_t s)
 {
-    return f16 ? by_rule<half_t>(p, rule, per_key, s) : by_rule<float>(p, rule, per_key, s);
+    if (act == 1) return by_rule<half_t>(p, rule, per_key, s);
+    if (act == 2) return by_rule<bf16_t>(p, rule, per_key, s);
+    return by_rule<float>(p, rule, per_key, s);
 }
 
 }  // namespace gdr

@@ -37,12 +37,13 @@ struct Params {
     float *state;           // outgoing states, or the slab updated in place
     int64_t T;
     int32_t B, L, H, HV, dk, dv, num_slots;
-    int32_t gate_qwen, gate_f16, beta_sigmoid, qk_l2_norm;
+    int32_t gate_qwen, gate_dt, beta_sigmoid, qk_l2_norm;  // gate_dt: 0 fp32, 1 fp16, 2 bf16
     int32_t beta_bcast;        // 1: beta is (T, 1), one update rate per token for every head
     float scale;
 };
 
 typedef _Float16 half_t;
+typedef __bf16 bf16_t;
 
 template <typename TA> __device__ __forceinline__ float to_f32(TA x) { return static_cast<float>(x); }
 template <typename TA> __device__ __forceinline__ TA from_f32(float x) { return static_cast<TA>(x); }
@@ -95,12 +96,19 @@ __device__ __forceinline__ float gate_scale(const Params &p, int h)
     return p.gate_scale ? p.gate_scale[h] : -expf(p.a_log[h]);
 }
 
+// One gate element: fp32, or the activations' 16-bit dtype (raw-gate arm).
+__device__ __forceinline__ float load_gate(const Params &p, size_t idx)
+{
+    if (p.gate_dt == 1) return to_f32(static_cast<const half_t *>(p.gate)[idx]);
+    if (p.gate_dt == 2) return to_f32(static_cast<const bf16_t *>(p.gate)[idx]);
+    return static_cast<const float *>(p.gate)[idx];
+}
+
 // Log decay g for token t, head h (scalar gate): README Attributes
-// gate_activation; the raw-gate arm reads the projection in fp16 or fp32.
+// gate_activation; the raw-gate arm reads the projection in its dtype.
 __device__ __forceinline__ float log_decay(const Params &p, size_t idx, int h)
 {
-    float x = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[idx])
-                         : static_cast<const float *>(p.gate)[idx];
+    float x = load_gate(p, idx);
     if (p.gate_qwen) x = gate_scale(p, h) * softplus_f32(x + p.dt_bias[h]);
     return x;
 }
@@ -116,9 +124,7 @@ __device__ __forceinline__ float key_decay_from_raw(const Params &p, float x, in
 // Log decay of key channel j for token-head th (= t * HV + h) of a per-key gate.
 __device__ __forceinline__ float log_decay_key(const Params &p, size_t th, int h, int j)
 {
-    const size_t idx = th * p.dk + j;
-    float x = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[idx])
-                         : static_cast<const float *>(p.gate)[idx];
+    const float x = load_gate(p, th * p.dk + j);
     return p.gate_qwen ? key_decay_from_raw(p, x, h, j) : x;
 }
 
@@ -185,7 +191,7 @@ __device__ __forceinline__ void load_act(const TA *__restrict__ ptr, float (&out
 #pragma unroll
         for (int i = 0; i < N; i += 4) {
             const uint2 w = *reinterpret_cast<const uint2 *>(ptr + i);
-            const half_t *h = reinterpret_cast<const half_t *>(&w);
+            const TA *h = reinterpret_cast<const TA *>(&w);
             out[i] = to_f32(h[0]); out[i + 1] = to_f32(h[1]);
             out[i + 2] = to_f32(h[2]); out[i + 3] = to_f32(h[3]);
         }

@@ -23,22 +23,24 @@ __global__ __launch_bounds__(256) void k_gate(int64_t count, int heads, const T 
     }
 }
 
-hipError_t launch_gate(int64_t count, int heads, bool f16, const void *a, const float *dt_bias,
+template <typename T>
+static void launch_typed(int64_t count, int heads, const void *a, const float *dt_bias, const float *decay_scale,
+                         const void *b, void *decay, void *beta, hipStream_t s)
+{
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(k_gate<T>, dim3((unsigned)blocks), dim3(256), 0, s, count, heads,
+                       static_cast<const T *>(a), dt_bias, decay_scale, static_cast<const T *>(b),
+                       static_cast<T *>(decay), static_cast<T *>(beta));
+}
+
+hipError_t launch_gate(int64_t count, int heads, int dtype, const void *a, const float *dt_bias,
                        const float *decay_scale, const void *b, void *decay, void *beta, hipStream_t s)
 {
     if (count == 0) return hipSuccess;
-    int64_t blocks = (count + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (f16)
-        hipLaunchKernelGGL(k_gate<half_t>, dim3((unsigned)blocks), dim3(256), 0, s, count, heads,
-                           static_cast<const half_t *>(a), dt_bias, decay_scale,
-                           static_cast<const half_t *>(b), static_cast<half_t *>(decay),
-                           static_cast<half_t *>(beta));
-    else
-        hipLaunchKernelGGL(k_gate<float>, dim3((unsigned)blocks), dim3(256), 0, s, count, heads,
-                           static_cast<const float *>(a), dt_bias, decay_scale,
-                           static_cast<const float *>(b), static_cast<float *>(decay),
-                           static_cast<float *>(beta));
+    if (dtype == 1) launch_typed<half_t>(count, heads, a, dt_bias, decay_scale, b, decay, beta, s);
+    else if (dtype == 2) launch_typed<bf16_t>(count, heads, a, dt_bias, decay_scale, b, decay, beta, s);
+    else launch_typed<float>(count, heads, a, dt_bias, decay_scale, b, decay, beta, s);
     return hipGetLastError();
 }
 

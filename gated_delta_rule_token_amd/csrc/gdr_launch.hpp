@@ -10,10 +10,10 @@ namespace gdr {
 
 // Recurrent kernel: dkt in {32, 64, 128, 256} (>= dk), g in {1, 2, 4}
 // (rows per workgroup = 16 * g).
-hipError_t launch_recurrent(const Params &p, int rule, bool per_key, bool f16, int dkt, int g, hipStream_t s);
+hipError_t launch_recurrent(const Params &p, int rule, bool per_key, int act, int dkt, int g, hipStream_t s);
 
 // Decode kernel, dk = dv = 128 only.
-hipError_t launch_decode128(const Params &p, int rule, bool per_key, bool f16, hipStream_t s);
+hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hipStream_t s);
 
 // Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations); the
 // per-key form (per_key) serves a decay per key channel and the erase gate.
@@ -22,7 +22,7 @@ size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key);
 hipError_t launch_chunked(const Params &p, int rule, bool per_key, void *ws, hipStream_t s);
 
 // Standalone gate fusion.
-hipError_t launch_gate(int64_t count, int heads, bool f16, const void *a, const float *dt_bias,
+hipError_t launch_gate(int64_t count, int heads, int dtype, const void *a, const float *dt_bias,
                        const float *decay_scale, const void *b, void *decay, void *beta, hipStream_t s);
 
 }  // namespace gdr

@@ -116,10 +116,10 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                 r.q[i] = *reinterpret_cast<const AV *>(qp + col0);
                 r.k[i] = *reinterpret_cast<const AV *>(kp + col0);
                 if constexpr (VD && PK) {
-                    // a per-key raw gate comes in the activations' dtype (fp16 gates only with fp16 activations)
-                    bool f16_gate = false;
-                    if constexpr (sizeof(TA) == 2) f16_gate = p.gate_f16 != 0;
-                    if (f16_gate) {
+                    // a per-key raw gate comes in fp32 or the activations' dtype
+                    bool act_gate = false;
+                    if constexpr (sizeof(TA) == 2) act_gate = p.gate_dt != 0;
+                    if (act_gate) {
                         const AV gh = *reinterpret_cast<const AV *>(static_cast<const TA *>(p.gate) + th * dk + col0);
 #pragma unroll
                         for (int c = 0; c < C; ++c) r.dec[i][c] = to_f32((TA)gh[c]);
@@ -136,8 +136,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
                     r.q[i][c] = qp[col];
                     r.k[i][c] = kp[col];
                     if constexpr (VD && PK)
-                        r.dec[i][c] = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[th * dk + col])
-                                                 : static_cast<const float *>(p.gate)[th * dk + col];
+                        r.dec[i][c] = load_gate(p, th * dk + col);
                     if constexpr (RULE == GATED_DELTA_V2) r.er[i][c] = p.erase[th * dk + col];
                 }
             }
@@ -154,8 +153,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
         r.bt = 1.f;
         {
             const size_t th = (size_t)tok(tb0 + (tid < NB ? tid : NB - 1)) * HV + h;
-            if constexpr (DEC && (!VD || !PK)) r.g = p.gate_f16 ? to_f32(static_cast<const half_t *>(p.gate)[th])
-                                                                 : static_cast<const float *>(p.gate)[th];
+            if constexpr (DEC && (!VD || !PK)) r.g = load_gate(p, th);
             if constexpr (BETA) r.bt = p.beta[beta_index(p, th)];
         }
     };
@@ -386,9 +384,11 @@ static hipError_t by_rule(const Params &p, int rule, bool pk, int dkt, int g, hi
     }
 }
 
-hipError_t launch_recurrent(const Params &p, int rule, bool per_key, bool f16, int dkt, int g, hipStream_t s)
+hipError_t launch_recurrent(const Params &p, int rule, bool per_key, int act, int dkt, int g, hipStream_t s)
 {
-    return f16 ? by_rule<half_t>(p, rule, per_key, dkt, g, s) : by_rule<float>(p, rule, per_key, dkt, g, s);
+    if (act == 1) return by_rule<half_t>(p, rule, per_key, dkt, g, s);
+    if (act == 2) return by_rule<bf16_t>(p, rule, per_key, dkt, g, s);
+    return by_rule<float>(p, rule, per_key, dkt, g, s);
 }
 
 }  // namespace gdr

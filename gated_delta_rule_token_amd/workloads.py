@@ -46,6 +46,23 @@ def unit_rows(rng, shape, dtype):
     return (x / n.astype(np.float32)).astype(dtype)
 
 
+def bf16_grid(x):
+    """float32 array rounded to the nearest bfloat16 value (ties to even), kept
+    as float32: numpy has no bfloat16, and these values convert to bfloat16
+    exactly on the device."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def _draw(rng, shape, dtype, unit=False):
+    """N(0,1) draw (unit rows with unit=True) in fp32/fp16, or on the bf16 grid."""
+    if dtype == "bf16":
+        x = unit_rows(rng, shape, np.float32) if unit else _normal(rng, shape, np.float32)
+        return bf16_grid(x)
+    return unit_rows(rng, shape, dtype) if unit else _normal(rng, shape, dtype)
+
+
 def _log_uniform_alog(rng, n):
     # A_log = log U(1, 16): the per-head log decay rate
     return np.log(rng.uniform(1.0, 16.0, size=n)).astype(np.float32)
@@ -215,17 +232,17 @@ def random_case(seed, *, T=None, lengths=None, H=2, HV=4, DK=32, DV=32, dtype=np
     else:
         B, cu = 1, None
         lead = (T,)
-    act = "f32" if dtype == np.float32 else "f16"
-    q = _normal(rng, lead + (H, DK), dtype)
-    k = unit_rows(rng, lead + (H, DK), dtype) if unit_keys else _normal(rng, lead + (H, DK), dtype)
-    v = _normal(rng, lead + (HV, DV), dtype)
+    act = "bf16" if dtype == "bf16" else ("f32" if dtype == np.float32 else "f16")
+    q = _draw(rng, lead + (H, DK), dtype)
+    k = _draw(rng, lead + (H, DK), dtype, unit=unit_keys)
+    v = _draw(rng, lead + (HV, DV), dtype)
     case = base(name="random_%s_s%d" % (update_rule, seed), q=q, k=k, v=v, cu_seqlens=cu,
                 update_rule=update_rule, gate_activation=gate_activation,
                 beta_activation=beta_activation, qk_l2_norm=qk_l2_norm, act_dtype=act)
     if update_rule in ("gated", "gated_delta", "gated_delta_v2"):
         gshape = lead + ((HV, DK) if per_key else (HV,))
         if gate_activation == "qwen":
-            case["gate"] = _normal(rng, gshape, dtype)
+            case["gate"] = _draw(rng, gshape, dtype)
             case["a_log"] = _log_uniform_alog(rng, HV)
             case["dt_bias"] = rng.uniform(0.0, 1.0, size=(HV, DK) if per_key else HV).astype(np.float32)
             if folded_scale:

@@ -45,7 +45,7 @@
  *                   place at rows slot_ids[b] (CLIKA "gatedDeltaUpdate")
  * with T total tokens, H query/key heads, HV value heads (a positive multiple
  * of H; value head h reads q/k head floor(h * H / HV), README Description),
- * act dtype fp32 or fp16 (README, Type constraints).
+ * act dtype fp32 or fp16 (README, Type constraints), or bf16.
  *
  * Requests: with cu_seqlens, request b covers tokens
  * [clamp(cu[b], 0, T), clamp(cu[b+1], 0, T)) and is empty when the end is not
@@ -95,7 +95,11 @@ typedef enum {
     GDR_E_HIP = 5           /* a HIP runtime call failed (message in gdr_last_error) */
 } gdr_status;
 
-typedef enum { GDR_F32 = 0, GDR_F16 = 1 } gdr_dtype;
+/* Activation dtypes.  bf16 goes beyond the pages' type list (fp32, fp16;
+ * README, Type constraints): the loads widen it exactly to fp32 and the
+ * output is rounded to nearest even on store; the chunked kernels take fp16
+ * only, so bf16 runs on the decode and recurrent kernels. */
+typedef enum { GDR_F32 = 0, GDR_F16 = 1, GDR_BF16 = 2 } gdr_dtype;
 
 typedef enum {
     GDR_RULE_LINEAR = 0,
@@ -199,7 +203,7 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors,
  *   decay[n] = decay_scale[h] * softplus(a[n] + dt_bias[h])
  *   beta[n]  = sigmoid(b[n])          (only when beta != NULL; needs b)
  * for n over `count` elements whose last axis is the head axis (h = n % heads).
- * a, b, decay, beta share `dtype` (F32 or F16); dt_bias and decay_scale are
+ * a, b, decay, beta share `dtype` (F32, F16 or BF16); dt_bias and decay_scale are
  * fp32 (heads).  Arithmetic in fp32, narrowed only on store.  b may be given
  * without beta (it is then unused). */
 gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a,

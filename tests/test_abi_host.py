@@ -200,11 +200,15 @@ def test_workspace_and_algo_selection(lib):
     assert api.selected_algo(p) == "chunked"
     assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
     assert n.value > n_head
-    # short requests stay on the recurrent kernel, fp32 activations too
+    # short requests stay on the recurrent kernel, fp32 and bf16 activations too
     p.total_tokens = 2 * 100
     assert api.selected_algo(p) == "recurrent"
     p.total_tokens, p.act_dtype = 4096, api.F32
     assert api.selected_algo(p) == "recurrent"
+    p.act_dtype = api.BF16
+    assert api.selected_algo(p) == "recurrent"
+    p.algo = api.ALGOS["chunked"]
+    assert lib.gdr_validate(ctypes.byref(p), None) == api.GDR_E_UNSUPPORTED
 
 
 def test_gate_argument_checks(lib):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_token_amd import workloads
-from tests.gpu_helpers import (TOL_CHUNKED, TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
+from tests.gpu_helpers import (TOL_BF16_O, TOL_CHUNKED, TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
                                sub_case, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -29,11 +29,15 @@ def _tol(case):
     return TOL_F32 if case["act_dtype"] == "f32" else TOL_F16
 
 
+def _tol_o(case):
+    return TOL_BF16_O if case["act_dtype"] == "bf16" else _tol(case)
+
+
 def _check_full(case, algo, what):
     say("case %s algo=%s" % (case["name"], algo))
     o, st = gpu_forward(case, algo)
     ro, rs = oracle_forward(case)
-    assert_close(o, ro, _tol(case), "%s o" % what)
+    assert_close(o, ro, _tol_o(case), "%s o" % what)
     assert_close(st, rs, _tol(case), "%s state" % what)
     return o, st
 
@@ -256,20 +260,24 @@ def test_rule_reduction_gated_delta_zero_gate():
 
 
 # ------------------------------------------------------------------ standalone gate
-@pytest.mark.parametrize("dtype", [np.float32, np.float16], ids=["f32", "f16"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16, "bf16"], ids=["f32", "f16", "bf16"])
 def test_gate_kernel(dtype):
     from gated_delta_rule_token_amd import api
     rng = np.random.Generator(np.random.PCG64(31))
-    a = (3 * rng.standard_normal((37, 5))).astype(dtype)
+    a = (3 * rng.standard_normal((37, 5))).astype(np.float32 if dtype == "bf16" else dtype)
     a[0, 0], a[1, 1] = 30.0, -30.0
-    b = rng.standard_normal((37, 5)).astype(dtype)
+    b = rng.standard_normal((37, 5)).astype(np.float32 if dtype == "bf16" else dtype)
+    if dtype == "bf16":
+        a, b = workloads.bf16_grid(a), workloads.bf16_grid(b)
     dt_bias = rng.uniform(0, 1, 5).astype(np.float32)
     dscale = -np.exp(np.log(rng.uniform(1, 16, 5))).astype(np.float32)
     tt = lambda x: torch.from_numpy(x).cuda()
-    decay, beta = api.gate(tt(a), tt(dt_bias), tt(dscale), b=tt(b), want_beta=True)
+    ta = (lambda x: tt(x).to(torch.bfloat16)) if dtype == "bf16" else tt
+    decay, beta = api.gate(ta(a), tt(dt_bias), tt(dscale), b=ta(b), want_beta=True)
     ref_decay = dscale.astype(np.float64) * np.logaddexp(0.0, a.astype(np.float64) + dt_bias)
     ref_beta = 1.0 / (1.0 + np.exp(-b.astype(np.float64)))
-    tol = 1e-6 if dtype == np.float32 else 1e-3
+    # relative rounding of one store: 2^-24 (f32), 2^-11 (f16), 2^-8 (bf16)
+    tol = {np.float32: 1e-6, np.float16: 1e-3, "bf16": 8e-3}[dtype]
     got_d = decay.double().cpu().numpy()
     got_b = beta.double().cpu().numpy()
     assert np.max(np.abs(got_d - ref_decay) / np.maximum(np.abs(ref_decay), 1e-3)) < tol
@@ -479,3 +487,20 @@ def test_beta_one_per_token(algo, L, per_key):
     case["beta"] = np.ascontiguousarray(case["beta"][..., :1])
     assert case["beta"].shape == (3, L, 1)
     _check_full(case, algo, "beta per token %s%s" % (algo, " per-key" if per_key else ""))
+
+
+# ------------------------------------------------------------------ bf16 activations
+# (beyond the pages' type list; loads widen bf16 exactly, o is rounded on store)
+BF16_CASES = [("decode", 128, 128, 2), ("recurrent", 128, 128, 70), ("recurrent", 64, 48, 33)]
+
+
+@pytest.mark.parametrize("algo,dk,dv,L", BF16_CASES, ids=["%s_%dx%d" % c[:3] for c in BF16_CASES])
+@pytest.mark.parametrize("rule,per_key", [("gated_delta", False), ("gated_delta_v2", True)],
+                         ids=["gated_delta_qwen", "gated_delta_v2_pk"])
+def test_bf16_activations(algo, dk, dv, L, rule, per_key):
+    case = workloads.random_case(zlib.crc32(("bf16/%s/%d/%s" % (algo, dk, rule)).encode()) % 1000,
+                                 rank4_batch=(3, L), H=2, HV=4, DK=dk, DV=dv, dtype="bf16",
+                                 update_rule=rule, per_key=per_key,
+                                 gate_activation="none" if per_key else "qwen",
+                                 beta_activation="none" if per_key else "sigmoid", qk_l2_norm=1)
+    _check_full(case, algo, "bf16 %s %s" % (rule, algo))
