@@ -504,3 +504,39 @@ def test_bf16_activations(algo, dk, dv, L, rule, per_key):
                                  gate_activation="none" if per_key else "qwen",
                                  beta_activation="none" if per_key else "sigmoid", qk_l2_norm=1)
     _check_full(case, algo, "bf16 %s %s" % (rule, algo))
+
+
+# ------------------------------------------------------------------ sizes past 32-bit byte offsets
+def test_decode_slab_beyond_4gib():
+    """A 4.3 GiB slab (2,200 slots x 32 heads x 64 KiB) addressed at slots past
+    the 4 GiB mark: offsets are 64-bit, untouched slots keep their bytes."""
+    import torch
+    case = workloads.decode_slab(B=64, num_slots=2200, with_slab=False)
+    rng = workloads.rng_for(202)
+    ids = (2200 - 1 - rng.permutation(150)[:64]).astype(np.int32)   # slots 2050 .. 2199
+    rows = workloads._normal(rng, (64, 32, 128, 128), np.float32, std=0.05)
+    say("case decode slab 4.3 GiB, slots %d..%d" % (ids.min(), ids.max()))
+    slab = torch.full((2200, 32, 128, 128), 0.25, dtype=torch.float32, device="cuda")
+    slab[torch.from_numpy(ids).long().cuda()] = torch.from_numpy(rows).cuda()
+    d = to_dev(dict(case, slab=None))
+    d["slot_ids"] = torch.from_numpy(ids).cuda()
+    d["slab"] = slab
+    from gated_delta_rule_token_amd import api
+    o, st = api.forward(d["q"], d["k"], d["v"], gate=d["gate"], beta=d["beta"], a_log=d["a_log"],
+                        dt_bias=d["dt_bias"], slot_ids=d["slot_ids"], state=slab,
+                        update_rule="gated_delta", gate_activation="qwen", beta_activation="sigmoid")
+    torch.cuda.synchronize()
+    ro, rs = oracle_forward(dict(case, slab=None, slot_ids=None, initial_state=rows))
+    assert_close(o.double().cpu().numpy(), ro, TOL_F16, "decode 4.3 GiB slab o")
+    assert_close(st[torch.from_numpy(ids).long().cuda()].double().cpu().numpy(), rs, TOL_F16,
+                 "decode 4.3 GiB slab rows")
+    mask = torch.ones(2200, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(ids).long().cuda()] = False
+    assert bool(torch.all(st[mask] == 0.25)), "untouched slots must keep their bytes"
+
+
+def test_chunked_workspace_beyond_4gib():
+    """262,144 tokens x 16 heads: a 7.6 GB chunk workspace (64-bit record
+    offsets) and 1 GiB q/k/v; the oracle checks sampled heads."""
+    case = workloads.long_prefill(T=262144)
+    _sampled(case, "chunked", [(0, [0]), (0, [15])], TOL_CHUNKED, "chunked 262k tokens")
