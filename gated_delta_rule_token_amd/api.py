@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(_PKG, "libgdr.so")
 _lock = threading.Lock()
 _lib = None
 
-ABI_VERSION = 2  # GDR_ABI_VERSION of include/gdr.h the structs below mirror
+ABI_VERSION = 3  # GDR_ABI_VERSION of include/gdr.h the structs below mirror
 GDR_OK, GDR_E_INVALID, GDR_E_UNSUPPORTED, GDR_E_ALIAS, GDR_E_WORKSPACE, GDR_E_HIP = range(6)
 F32, F16, BF16 = 0, 1, 2
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3, "gated_delta_v2": 4}
@@ -59,6 +59,7 @@ class Problem(ctypes.Structure):
         ("state_update_capacity", ctypes.c_int32),
         ("beta_per_token", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("scan_segments", ctypes.c_int32),
     ]
 
 
@@ -149,7 +150,7 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
                   cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
                   update_rule="gated_delta", gate_activation="none", beta_activation="none",
                   qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", batch=None,
-                  gate_scale=None, seq_lens=None):
+                  gate_scale=None, seq_lens=None, scan_segments=0):
     """Problem descriptor from tensor shapes (no device access)."""
     rank4 = q.dim() == 4
     if rank4:
@@ -183,7 +184,8 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
         update_rule=RULES[update_rule], gate_activation=GATES[gate_activation],
         beta_activation=BETAS[beta_activation], qk_l2_norm=int(bool(qk_l2_norm)),
         decay_per_key=int(per_key), rank4=int(rank4), chunk_size=int(chunk_size),
-        algo=ALGOS[algo], state_update_capacity=0, beta_per_token=int(beta_tok), scale=float(scale))
+        algo=ALGOS[algo], state_update_capacity=0, beta_per_token=int(beta_tok), scale=float(scale),
+        scan_segments=int(scan_segments))
     return p
 
 
@@ -203,7 +205,8 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
             cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
             update_rule="gated_delta", gate_activation="none", beta_activation="none",
             qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", out=None,
-            final_state=None, workspace=None, batch=None, gate_scale=None, seq_lens=None):
+            final_state=None, workspace=None, batch=None, gate_scale=None, seq_lens=None,
+            scan_segments=0):
     """Run the gated delta rule on the GPU.
 
     q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
@@ -213,7 +216,9 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a per-key gate, and either
     a_log (HV,) or the folded gate_scale = -exp(a_log) (HV,).  seq_lens (B,)
     int32 bounds each uniform-packed request to its first seq_lens[b] tokens
-    (rows past it in ``o`` are left as they are).
+    (rows past it in ``o`` are left as they are).  scan_segments: for the
+    chunked form, 0 lets the library choose, 1 runs each request's chunks in
+    one serial pass, n > 1 splits that chain into n composed segments.
     With ``state`` (a slab (num_slots,HV,dv,dk) fp32) and ``slot_ids``, the
     slab is updated in place and returned as the second result; otherwise a
     final state (B,HV,dv,dk) is allocated (or ``final_state`` is filled).
@@ -245,7 +250,7 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
                       state=state, update_rule=update_rule, gate_activation=gate_activation,
                       beta_activation=beta_activation, qk_l2_norm=qk_l2_norm, scale=scale,
                       chunk_size=chunk_size, algo=algo, batch=batch, gate_scale=gate_scale,
-                      seq_lens=seq_lens)
+                      seq_lens=seq_lens, scan_segments=scan_segments)
     HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
     lead = tuple(q.shape[:-2])
     if out is None:
@@ -308,7 +313,7 @@ class Prepared:
             "gate", "beta", "erase", "a_log", "dt_bias", "cu_seqlens", "initial_state",
             "slot_ids", "state", "gate_scale", "seq_lens")}, **{key: kw[key] for key in (
                 "update_rule", "gate_activation", "beta_activation", "qk_l2_norm", "scale",
-                "chunk_size", "algo", "batch") if key in kw})
+                "chunk_size", "algo", "batch", "scan_segments") if key in kw})
         HV, dv, dk = p.num_heads_v, p.head_dim_v, p.head_dim_k
         out = kw.get("out")
         if out is None:

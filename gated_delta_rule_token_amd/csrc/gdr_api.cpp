@@ -81,6 +81,7 @@ gdr_status check_problem(const gdr_problem *p)
     if (p->total_tokens < 0 || p->batch < 0 || p->seq_len < 0 || p->num_slots < 0 || p->chunk_size < 0)
         return fail(GDR_E_INVALID, "negative size");
     if (p->total_tokens > INT32_MAX) return fail(GDR_E_INVALID, "total_tokens above 2^31-1");
+    if (p->scan_segments < 0 || p->scan_segments > 16) return fail(GDR_E_INVALID, "scan_segments must lie in [0, 16]");
     const bool decays = gdr::rule_decays(p->update_rule);
     if (p->gate_activation == GDR_GATE_QWEN && !decays)
         return fail(GDR_E_INVALID, "gate_activation qwen needs a decayed update_rule");
@@ -186,6 +187,26 @@ int32_t pick_algo(const gdr_problem *p)
     return GDR_ALGO_RECURRENT;
 }
 
+// Segments of the chunked scan's chain: the caller's count, or a split of
+// long requests when few (request, head) pairs leave most CUs idle.  Each
+// segment pass then runs about 32 (request, head, segment) groups, one
+// 16-row-tile workgroup per CU (measured on MI355X, chunk scan + prologue:
+// 65,536 tokens x 16 heads 2.12 -> 1.82 ms in 3 segments; x 8 heads
+// 1.85 -> 1.10 ms in 5; 32,768 tokens x 4 heads 0.79 -> 0.47 ms in 5; with 32
+// pairs or more a split is slower, 1.41 -> 1.72 ms at 32,768 tokens x 32).
+// Segments shorter than 16 chunks are not worth the extra passes.
+int scan_segments(const gdr_problem *p)
+{
+    if (p->scan_segments > 0) return p->scan_segments;
+    const int64_t pairs = (int64_t)p->batch * p->num_heads_v;
+    const int64_t chunks_per_req = p->batch > 0 ? p->total_tokens / p->batch / 64 : 0;
+    if (pairs < 1 || pairs > 16 || chunks_per_req < 128) return 1;
+    int64_t n = 1 + 32 / pairs;
+    if (n > 16) n = 16;
+    if (n > chunks_per_req / 16) n = chunks_per_req / 16;
+    return n >= 3 ? (int)n : 1;
+}
+
 int dk_tile(int dk) { return dk <= 32 ? 32 : dk <= 64 ? 64 : dk <= 128 ? 128 : 256; }
 
 // rows per workgroup = 16 * g.  Measured on MI355X (dv = 128): g = 2 beats
@@ -234,7 +255,7 @@ gdr_status gdr_workspace_size(const gdr_problem *problem, size_t *bytes)
     if (st != GDR_OK) return st;
     *bytes = pick_algo(problem) == GDR_ALGO_CHUNKED
                  ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_v,
-                                                               chunked_per_key(problem))
+                                                chunked_per_key(problem), scan_segments(problem))
                  : 0;
     return GDR_OK;
 }
@@ -301,7 +322,9 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     hipError_t err;
     switch (pick_algo(problem)) {
     case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, act, s); break;
-    case GDR_ALGO_CHUNKED: err = gdr::launch_chunked(k, p.update_rule, pk, workspace, s); break;
+    case GDR_ALGO_CHUNKED:
+        err = gdr::launch_chunked(k, p.update_rule, pk, scan_segments(problem), workspace, s);
+        break;
     default: err = gdr::launch_recurrent(k, p.update_rule, pk, act, dk_tile(p.head_dim_k), rows_group(problem), s); break;
     }
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));

@@ -119,6 +119,22 @@ __device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
     }
 }
 
+// Segments of the scan's chain (see k_chunk_scan).  pass 0: one pass over
+// every chunk; pass 1 / 2: the two passes of an nseg-segment scan.  xs holds,
+// per (request, head), seg_slots(nseg) states of 128 x 128 fp32: the start of
+// segment p (1 <= p < nseg), and the carry and transition of middle segment p
+// (1 <= p < nseg - 1).
+struct ScanSeg {
+    int nseg;
+    int pass;
+    float *xs;
+};
+enum SegMode : int { SEG_REAL = 0, SEG_CARRY = 1, SEG_TRANS = 2 };
+__host__ __device__ constexpr int seg_slots(int nseg) { return 3 * nseg; }
+__host__ __device__ constexpr int seg_start(int p) { return p; }
+__host__ __device__ constexpr int seg_carry(int nseg, int p) { return nseg + p; }
+__host__ __device__ constexpr int seg_trans(int nseg, int p) { return 2 * nseg + p; }
+
 // Locate request b and the chunk's first token for global chunk index ci.
 __device__ __forceinline__ int chunk_request(const int32_t *off, int B, int64_t ci)
 {
@@ -809,8 +825,19 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 // With a decay per key channel (PK) the state decays by a vector gamma_C, and
 // Kd^T and Qg carry fp32 values split into (hi, lo) planes, so stage E and O1
 // take three products each; stage E then reads D^T directly (no kd D copy).
+//
+// Segmented chain.  A chunk step maps every state row affinely,
+// s <- s M_j + c_j (M_j = gamma_C I - W^T diag(kd) K, c_j the row's share of
+// kd U K), so a request's chunks can be cut into nseg segments that run side
+// by side.  Pass 1 runs segment 0 for real (writing its end state as the start
+// of segment 1) and, for each middle segment p, a carry tile (zero start:
+// c_p = the segment's end state from zero) and a transition tile (the 128 rows
+// of the identity as start, U left out: M_p = the product of the segment's
+// M_j).  k_seg_combine then forms start_{p+1} = start_p M_p + c_p, and pass 2
+// runs segments 1 .. nseg-1 for real from those starts.  The longest serial
+// chain shrinks from n chunk steps to about 2 n / nseg.
 template <int RULE, int NVB, bool PK>
-__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws)
+__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const ScanSeg sg)
 {
     using RC = Rec<PK>;
     constexpr int NPL = PK ? 2 : 1;       // fp16 planes of the K^T and q operands
@@ -828,10 +855,19 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     __shared__ __align__(16) half_t sO[4][16][TR + 8];   // per output wave: [token][row] staging for the store
 
     const int HV = p.HV;
-    // XCD-aware order: blocks i, i + 8, ... (one XCD) are the row tiles of one head
-    const int xl = blockIdx.x & 7, tile = (blockIdx.x >> 3) % NTILE, grp = blockIdx.x / (8 * NTILE);
-    const int bh = grp * 8 + xl;
-    if (bh >= p.B * HV) return;
+    // A group is one (request, head) -- with segments one (request, head,
+    // segment) -- and its units are its row tiles (pass 1: carry tiles, then
+    // transition tiles).  XCD-aware order: blocks i, i + 8, ... (one XCD) are
+    // the units of one group, which read the same chunk records.
+    const int NU = (sg.pass == 1 ? 2 : 1) * NTILE;
+    const int nsg = sg.pass == 0 ? 1 : sg.nseg - 1;  // groups per (request, head)
+    const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
+    const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
+    if (gi >= (int64_t)p.B * HV * nsg) return;
+    const int bh = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    const int tile = unit % NTILE;
+    const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
+    if (mode == SEG_TRANS && seg == 0) return;  // segment 0 has no transition tiles
     const int b = bh / HV, h = bh % HV;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
@@ -844,18 +880,43 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     int64_t rs, re;
     request_range(p, b, rs, re);
     const int c0 = off[b], nch = off[b + 1] - off[b];
+    // this unit's chunks [cb, ce) of the request, its start state and where its end state goes
+    const int ns = sg.pass == 0 ? 1 : sg.nseg;
+    const int cb = (int)((int64_t)seg * nch / ns), ce = (int)((int64_t)(seg + 1) * nch / ns);
+    const float *from = src;
+    float *to = dst;
+    if (sg.pass != 0) {
+        float *xs = sg.xs + (size_t)bh * seg_slots(ns) * (D128 * D128);
+        if (mode == SEG_REAL) {
+            from = seg == 0 ? src : xs + (size_t)seg_start(seg) * (D128 * D128);
+            to = seg == ns - 1 ? dst : seg == 0 ? xs + (size_t)seg_start(1) * (D128 * D128) : nullptr;
+        } else {
+            from = nullptr;
+            to = xs + (size_t)(mode == SEG_CARRY ? seg_carry(ns, seg) : seg_trans(ns, seg)) * (D128 * D128);
+        }
+    }
     const int tb = wave & 3;  // token block of this wave (D rows for the chain, O columns for the output)
 
     if (wave < 4) {
         // ================================================================ chain
+        const float um = mode == SEG_TRANS ? 0.f : 1.f;  // a transition tile leaves U out
         // Sc[a][rt][i] = S[row0 + 16 rt + lr][16 (2 wave + a) + 4 lq + i]
         f4v Sc[2][NVB];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int rt = 0; rt < NVB; ++rt)
-                Sc[a][rt] = src ? *reinterpret_cast<const f4v *>(src + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq)
-                                : f4v{0.f, 0.f, 0.f, 0.f};
+            {
+                const int row = row0 + 16 * rt + lr, col = 16 * (2 * wave + a) + 4 * lq;
+                if (from) {
+                    Sc[a][rt] = *reinterpret_cast<const f4v *>(from + (size_t)row * D128 + col);
+                } else {
+                    // zero, or row `row` of the identity for a transition tile
+                    const float one = mode == SEG_TRANS ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sc[a][rt][i] = row == col + i ? one : 0.f;
+                }
+            }
         struct Ops {
             h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
             h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
@@ -906,7 +967,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = hi;
                     *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = lo;
                 }
-            fetch(j + 1 < nch ? j + 1 : j, nxt);  // the last chunk re-reads itself
+            fetch(j + 1 < ce ? j + 1 : j, nxt);  // the last chunk re-reads itself
             // keep the prefetch where it is: neither the optimiser nor the
             // scheduler may move the loads past this point in either direction
             asm volatile("" ::: "memory");
@@ -940,7 +1001,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             for (int vb = 0; vb < NVB; ++vb) {
                 f4v d;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) d[i] = cur.u[vb][i] - accD[vb][i];
+                for (int i = 0; i < 4; ++i) d[i] = um * cur.u[vb][i] - accD[vb][i];
                 h4 dh, dl;
                 split4(d, dh, dl);
                 const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
@@ -993,16 +1054,25 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         };
         // two operand sets used in turn, so no register copy waits on a prefetch
         Ops opa, opb;
-        if (nch > 0) fetch(0, opa);
-        for (int j = 0; j < nch; j += 2) {
+        if (ce > cb) fetch(cb, opa);
+        for (int j = cb; j < ce; j += 2) {
             step(j, opa, opb);
-            if (j + 1 < nch) step(j + 1, opb, opa);
+            if (j + 1 < ce) step(j + 1, opb, opa);
         }
+        if (to) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int rt = 0; rt < NVB; ++rt)
-                *reinterpret_cast<f4v *>(dst + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt];
+                for (int rt = 0; rt < NVB; ++rt)
+                    *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt];
+        }
+    } else if (mode != SEG_REAL) {
+        // carry and transition tiles write no output: these waves only keep
+        // the chain's two barriers per chunk step
+        for (int j = cb; j < ce; ++j) {
+            lds_barrier();
+            lds_barrier();
+        }
     } else {
         // ================================================================ outputs
         half_t *o = static_cast<half_t *>(p.o);
@@ -1044,15 +1114,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         // write nothing (a branch here would make every later wait drain it).
         auto store_out = [&](int jo) {
             const int64_t t0 = rs + (int64_t)jo * CH;
-            const int n = jo >= 0 ? (int)((re - t0) < CH ? (re - t0) : CH) : 0;
-            half_t *base = jo >= 0 ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
+            const int n = jo >= cb ? (int)((re - t0) < CH ? (re - t0) : CH) : 0;
+            half_t *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
             const __amdgpu_buffer_rsrc_t ro =
                 __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
             __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok][8 * st_q]), ro, offO, 0, 0);
         };
         auto step = [&](int j, const Ops &cur, Ops &nxt) {
             const int bf = j & 1;
-            fetch(j + 1 < nch ? j + 1 : j, nxt);
+            fetch(j + 1 < ce ? j + 1 : j, nxt);
             asm volatile("" ::: "memory");  // pin the prefetch (see the chain role)
             __builtin_amdgcn_sched_barrier(0);
             lds_barrier();  // 1 (also completes this wave's staging of chunk j - 1)
@@ -1105,7 +1175,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             }
         };
         Ops opa, opb;
-        if (nch > 0) fetch(0, opa);
+        if (ce > cb) fetch(cb, opa);
         {
             // a store that writes nothing (empty resource): on entry the loop
             // then sees the same outstanding pattern as in steady state (the
@@ -1114,24 +1184,71 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, 0x00020000);
             __builtin_amdgcn_raw_buffer_store_b128(u4v{0u, 0u, 0u, 0u}, none, 0, 0, 0);
         }
-        for (int j = 0; j < nch; j += 2) {
+        for (int j = cb; j < ce; j += 2) {
             step(j, opa, opb);
-            if (j + 1 < nch) step(j + 1, opb, opa);
+            if (j + 1 < ce) step(j + 1, opb, opa);
         }
-        if (nch > 0) {
+        if (ce > cb) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging has landed
-            store_out(nch - 1);
+            store_out(ce - 1);
         }
+    }
+}
+
+// ------------------------------------------------------------------ segment starts
+// start_{p+1} = start_p M_p + c_p for the middle segments p = 1 .. nseg - 2,
+// in order; rows are independent, so one workgroup takes 16 rows of one
+// (request, head) and keeps them in LDS from one segment to the next.
+__global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanSeg sg)
+{
+    const int64_t bh = blockIdx.x >> 3;
+    const int rb = blockIdx.x & 7;
+    if (bh >= (int64_t)p.B * p.HV) return;
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, (int)(bh / p.HV), (int)(bh % p.HV), src, dst)) return;
+    __shared__ float sR[16][D128];
+    const int tid = threadIdx.x, c = tid & 127, r0 = (tid >> 7) * 8;
+    constexpr size_t HEAD = (size_t)D128 * D128;
+    float *xs = sg.xs + (size_t)bh * seg_slots(sg.nseg) * HEAD;
+    const size_t rows = (size_t)(16 * rb) * D128;
+    for (int i = tid; i < 16 * D128; i += 256) sR[i >> 7][i & 127] = xs[seg_start(1) * HEAD + rows + i];
+    __syncthreads();
+    for (int sp = 1; sp + 1 < sg.nseg; ++sp) {
+        const float *M = xs + (size_t)seg_trans(sg.nseg, sp) * HEAD;
+        const float *C = xs + (size_t)seg_carry(sg.nseg, sp) * HEAD + rows;
+        float acc[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] = C[(size_t)(r0 + r) * D128 + c];
+        for (int j = 0; j < D128; ++j) {
+            const float m = M[(size_t)j * D128 + c];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[r] = fmaf(sR[r0 + r][j], m, acc[r]);
+        }
+        __syncthreads();  // every thread has read the old rows
+        float *S = xs + (size_t)seg_start(sp + 1) * HEAD + rows;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            sR[r0 + r][c] = acc[r];
+            S[(size_t)(r0 + r) * D128 + c] = acc[r];
+        }
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------ host side
 
-size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key)
+static size_t seg_offset(int64_t T, int B, int HV, bool per_key)
 {
     const int64_t maxch = (T + CH - 1) / CH + B;
     const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
-    return table + (size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE);
+    return table + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
+}
+
+size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg)
+{
+    const size_t segs = nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0;
+    return seg_offset(T, B, HV, per_key) + segs;
 }
 
 // Row tile of the scan: 16 * NVB rows, NVB = 1 or 2 (measured on MI355X:
@@ -1139,24 +1256,55 @@ size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key)
 // by 1.7x, which loses on both the single long sequence and the batched
 // prefill).
 template <int RULE, int NVB, bool PK>
-static void launch_scan(const Params &p, const int32_t *off, const char *rec, hipStream_t s)
+static void launch_scan(const Params &p, const int32_t *off, const char *rec, const ScanSeg &sg, hipStream_t s)
 {
     constexpr int NTILE = D128 / (16 * NVB);
-    const int64_t nbh = (int64_t)p.B * p.HV;
-    const int64_t blocks = (nbh + 7) / 8 * 8 * NTILE;
-    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec);
+    const int64_t groups = (int64_t)p.B * p.HV * (sg.pass == 0 ? 1 : sg.nseg - 1);
+    const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
+    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, sg);
+}
+
+// Scan launches.  Few (request, head) pairs leave most CUs idle with 32-row
+// tiles; 16-row tiles double the workgroups and shorten each chunk step
+// (measured on MI355X: one 65,536-token sequence x 16 heads 2.65 -> 2.18 ms),
+// while with many pairs the GPU is full and the larger tiles amortise the
+// operand reads (8 x 32 heads: 1.27 ms with 32-row tiles, 1.47 ms with 16-row
+// tiles).  A segmented scan runs pass 1 (carry and transition tiles: twice
+// the workgroups of pass 2) in 32-row tiles and pass 2 by the same rule as a
+// single pass over its (request, head, segment) groups: two workgroups of
+// this kernel on one CU share its vector-memory pipeline and each chunk step
+// then takes about twice as long (measured on MI355X, 65,536 tokens x 16
+// heads in 3 segments: 1.82 ms with 32-row pass-1 tiles, 1.89 ms with 16-row).
+template <int RULE, bool PK>
+static void launch_scans(const Params &p, const int32_t *off, const char *rec, float *xs, int nseg, hipStream_t s)
+{
+    const int64_t pairs = (int64_t)p.B * p.HV;
+    if (nseg <= 1) {
+        const ScanSeg one{1, 0, nullptr};
+        if (pairs <= 32) launch_scan<RULE, 1, PK>(p, off, rec, one, s);
+        else launch_scan<RULE, 2, PK>(p, off, rec, one, s);
+        return;
+    }
+    launch_scan<RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 1, xs}, s);
+    if (nseg > 2) {
+        const int64_t blocks = pairs * 8;
+        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, ScanSeg{nseg, 0, xs});
+    }
+    if (pairs * (nseg - 1) <= 32) launch_scan<RULE, 1, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
+    else launch_scan<RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
 }
 
 // PK: the per-key record and kernels; PKG: the gate itself is per key (else
 // a per-head gate broadcast over the key channels, used by the erase gate).
 template <int RULE, bool PK, bool PKG>
-static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
+static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s)
 {
     const int64_t maxch = (p.T + CH - 1) / CH + p.B;
     const size_t table = ((size_t)(p.B + 1) * 4 + 255) / 256 * 256;
     char *base = static_cast<char *>(ws);
     int32_t *off = reinterpret_cast<int32_t *>(base);
     char *rec = base + table;
+    float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.HV, PK));
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
     if (maxch * p.HV > 0) {
         if constexpr (PK)
@@ -1164,26 +1312,20 @@ static hipError_t launch_rule(const Params &p, void *ws, hipStream_t s)
         else
             hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
     }
-    // Few (request, head) pairs leave most CUs idle with 32-row tiles; 16-row
-    // tiles double the workgroups and shorten each chunk step (measured on
-    // MI355X: one 65,536-token sequence x 16 heads 2.65 -> 2.18 ms), while with
-    // many pairs the GPU is full and the larger tiles amortise the operand reads
-    // (8 x 32 heads: 1.27 ms with 32-row tiles, 1.47 ms with 16-row tiles).
-    if ((int64_t)p.B * p.HV <= 32) launch_scan<RULE, 1, PK>(p, off, rec, s);
-    else launch_scan<RULE, 2, PK>(p, off, rec, s);
+    launch_scans<RULE, PK>(p, off, rec, xs, nseg, s);
     return hipGetLastError();
 }
 
-hipError_t launch_chunked(const Params &p, int rule, bool per_key, void *ws, hipStream_t s)
+hipError_t launch_chunked(const Params &p, int rule, bool per_key, int nseg, void *ws, hipStream_t s)
 {
     if (rule == GATED_DELTA_V2)
-        return per_key ? launch_rule<GATED_DELTA_V2, true, true>(p, ws, s) : launch_rule<GATED_DELTA_V2, true, false>(p, ws, s);
-    if (per_key) return rule == GATED ? launch_rule<GATED, true, true>(p, ws, s) : launch_rule<GATED_DELTA, true, true>(p, ws, s);
+        return per_key ? launch_rule<GATED_DELTA_V2, true, true>(p, nseg, ws, s) : launch_rule<GATED_DELTA_V2, true, false>(p, nseg, ws, s);
+    if (per_key) return rule == GATED ? launch_rule<GATED, true, true>(p, nseg, ws, s) : launch_rule<GATED_DELTA, true, true>(p, nseg, ws, s);
     switch (rule) {
-    case LINEAR: return launch_rule<LINEAR, false, false>(p, ws, s);
-    case GATED: return launch_rule<GATED, false, false>(p, ws, s);
-    case DELTA: return launch_rule<DELTA, false, false>(p, ws, s);
-    default: return launch_rule<GATED_DELTA, false, false>(p, ws, s);
+    case LINEAR: return launch_rule<LINEAR, false, false>(p, nseg, ws, s);
+    case GATED: return launch_rule<GATED, false, false>(p, nseg, ws, s);
+    case DELTA: return launch_rule<DELTA, false, false>(p, nseg, ws, s);
+    default: return launch_rule<GATED_DELTA, false, false>(p, nseg, ws, s);
     }
 }
 

@@ -17,9 +17,11 @@ hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hi
 
 // Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations); the
 // per-key form (per_key) serves a decay per key channel and the erase gate.
-// `ws` holds chunked_workspace_bytes(T, B, HV, per_key) bytes.
-size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key);
-hipError_t launch_chunked(const Params &p, int rule, bool per_key, void *ws, hipStream_t s);
+// nseg > 1 cuts each request's chain of chunk steps into that many segments
+// (two scan passes and a combine step).  `ws` holds
+// chunked_workspace_bytes(T, B, HV, per_key, nseg) bytes.
+size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg);
+hipError_t launch_chunked(const Params &p, int rule, bool per_key, int nseg, void *ws, hipStream_t s);
 
 // Standalone gate fusion.
 hipError_t launch_gate(int64_t count, int heads, int dtype, const void *a, const float *dt_bias,

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum {
     GDR_OK = 0,
@@ -151,6 +151,12 @@ typedef struct {
     int32_t state_update_capacity; /* must be 0 (README, Attributes) */
     int32_t beta_per_token;     /* 1: beta is (T, 1), shared by every value head */
     float scale;                /* 0 -> 1 / sqrt(dk) (README, Attributes) */
+    int32_t scan_segments;      /* chunked form only, a scheduling choice like chunk_size:
+                                 * 0 -> chosen from the shapes; 1 -> each request's chunks
+                                 * in one serial pass; 2..16 -> each request's chain of
+                                 * chunk steps cut into that many segments whose affine
+                                 * transitions are composed (more workgroups, two passes).
+                                 * The result is the same up to rounding. */
 } gdr_problem;
 
 typedef struct {

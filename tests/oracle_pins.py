@@ -449,6 +449,40 @@ def pin_chunked_equivalence(fwd):
             _close(s_c, s_ref, 1e-10, "chunked %s C=%d state" % (name, c))
 
 
+def pin_segment_composition(fwd):
+    """The recurrence maps the state affinely: over a run of tokens each
+    V-major row goes s -> s M + c, where row r of M is the run started from
+    row r of the identity with every value zero, and c the run started from
+    zero.  Cutting a request into segments and composing (M, c) in order
+    must therefore give the one-pass final state (the reading the segmented
+    chunk scan relies on)."""
+    r = _rng(17)
+    T, H, HV, D = 23, 1, 2, 5
+    q, k = r.standard_normal((T, H, D)), _unit(r.standard_normal((T, H, D)))
+    v = r.standard_normal((T, HV, D))
+    S0 = r.standard_normal((1, HV, D, D))
+    eye = np.broadcast_to(np.eye(D), (1, HV, D, D)).copy()
+    cases = [
+        ("gated_delta", dict(update_rule="gated_delta", gate=-r.uniform(0, 0.3, (T, HV)), beta=r.uniform(0, 1, (T, HV)))),
+        ("linear", dict(update_rule="linear")),
+        ("gated_delta_v2 per-key", dict(update_rule="gated_delta_v2", gate=-r.uniform(0, 0.3, (T, HV, D)),
+                                        erase=r.uniform(0, 1, (T, HV, D)))),
+    ]
+    cuts = [0, 7, 8, 19, T]
+    for name, kw in cases:
+        _, s_ref = fwd(q, k, v, initial_state=S0, **kw)
+        s = S0
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            seg = {key: (val[a:b] if isinstance(val, np.ndarray) else val) for key, val in kw.items()}
+            _, M = fwd(q[a:b], k[a:b], np.zeros_like(v[a:b]), initial_state=eye, **seg)
+            _, c = fwd(q[a:b], k[a:b], v[a:b], initial_state=np.zeros_like(S0), **seg)
+            s = np.einsum("bhij,bhjk->bhik", s, M) + c
+        _close(s, s_ref, 1e-12, "segment composition %s" % name)
+        # and the map really depends on the start (M is not zero)
+        _, s_zero = fwd(q, k, v, initial_state=np.zeros_like(S0), **kw)
+        assert np.max(np.abs(s_ref - s_zero)) > 1e-3, name
+
+
 def pin_kmajor_cross(fwd):
     r = _rng(15)
     B, L, H, HV, DK, DV = 2, 6, 2, 4, 5, 3
@@ -478,5 +512,5 @@ ALL_PINS = [
     pin_golden_hand, pin_linear_closed_form, pin_gated_closed_form, pin_delta_invariant,
     pin_beta_zero, pin_orthonormal_keys, pin_gqa_mapping, pin_varlen_packing, pin_seq_lens, pin_slots,
     pin_gate_arms, pin_l2_norm, pin_scale, pin_rule_reductions, pin_v2_reductions,
-    pin_chunked_equivalence, pin_kmajor_cross, pin_row_split_invariance,
+    pin_chunked_equivalence, pin_segment_composition, pin_kmajor_cross, pin_row_split_invariance,
 ]

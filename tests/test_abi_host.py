@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(api.EXPORTS), names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gdr_abi_version() == api.ABI_VERSION == 2
+    assert lib.gdr_abi_version() == api.ABI_VERSION == 3
 
 
 def test_status_strings(lib):
@@ -209,6 +209,32 @@ def test_workspace_and_algo_selection(lib):
     assert api.selected_algo(p) == "recurrent"
     p.algo = api.ALGOS["chunked"]
     assert lib.gdr_validate(ctypes.byref(p), None) == api.GDR_E_UNSUPPORTED
+
+
+def test_scan_segments_workspace(lib):
+    """A segmented chunk scan keeps per (request, head) segment states in the
+    workspace; the count is validated on the host."""
+    p, _ = _good()
+    p.head_dim_k = p.head_dim_v = 128
+    p.total_tokens, p.batch, p.act_dtype, p.gate_dtype = 4096, 2, api.F16, api.F16
+    n1, n4 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p.scan_segments = 1
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == api.GDR_OK
+    p.scan_segments = 4
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n4)) == api.GDR_OK
+    heads = p.batch * p.num_heads_v
+    assert n4.value - n1.value >= heads * 3 * 4 * 128 * 128 * 4
+    for bad in (-1, 17):
+        p.scan_segments = bad
+        assert lib.gdr_validate(ctypes.byref(p), None) == api.GDR_E_INVALID
+        assert b"scan_segments" in lib.gdr_last_error()
+    # the automatic choice splits one long request over few heads, not many short ones
+    p.scan_segments, p.batch, p.num_heads_qk, p.num_heads_v = 0, 1, 16, 16
+    p.total_tokens = 65536
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n4)) == api.GDR_OK
+    p.scan_segments = 1
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == api.GDR_OK
+    assert n4.value > n1.value
 
 
 def test_gate_argument_checks(lib):

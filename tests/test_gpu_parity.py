@@ -334,6 +334,100 @@ def test_chunked_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def _mild(case, seed, per_key=False):
+    """Weak decay and small update rates (input recipe only), so that a long
+    segment's transition matrix stays far from zero and a mistake in how the
+    segments are composed shows in the result."""
+    rng = workloads.rng_for(seed)
+    lead = case["v"].shape[:-2]
+    HV = case["v"].shape[-2]
+    if case["gate"] is not None:
+        shape = lead + ((HV, case["k"].shape[-1]) if per_key else (HV,))
+        case["gate"] = (-0.001 * rng.random(shape)).astype(np.float32)
+        case["gate_activation"], case["a_log"], case["dt_bias"] = "none", None, None
+    if case["beta"] is not None:
+        case["beta"] = (0.01 + 0.05 * rng.random(lead + (HV,))).astype(np.float32)
+        case["beta_activation"] = "none"
+    if case["erase"] is not None:
+        case["erase"] = (0.05 * rng.random(case["erase"].shape)).astype(np.float32)
+    for key in ("initial_state", "slab"):
+        if case[key] is not None:
+            case[key] = case[key] * np.float32(10.0)
+    return case
+
+
+def _start_matters(case, label):
+    # the final state must depend on the initial state, or segment composition is untested
+    _, rs = oracle_forward(case)
+    _, rz = oracle_forward(dict(case, initial_state=None))
+    d = np.max(np.abs(rs - rz)) / np.max(np.abs(rs))
+    say("  %s: initial state moves the final state by %.2f (relative)" % (label, d))
+    assert d > 0.05
+
+
+@pytest.mark.parametrize("nseg", [2, 3, 5, 16])
+def test_chunked_segmented_scan(nseg):
+    """The chain of chunk steps cut into nseg composed segments (two scan
+    passes around the combine step) against the oracle and the one-pass scan,
+    on one request of 38 chunks with a ragged tail."""
+    case = _mild(workloads.random_case(71, lengths=[64 * 37 + 19], H=1, HV=2, DK=128, DV=128,
+                                       dtype=np.float16, update_rule="gated_delta"), 72)
+    if nseg == 2:
+        _start_matters(case, "segmented scan")
+    say("case segmented scan nseg=%d" % nseg)
+    o, st = gpu_forward(case, "chunked", scan_segments=nseg)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "segmented o")
+    assert_close(st, rs, TOL_CHUNKED, "segmented state")
+    o1, st1 = gpu_forward(case, "chunked", scan_segments=1)
+    assert_close(o, o1, TOL_CHUNKED, "segmented vs one pass o")
+    assert_close(st, st1, TOL_CHUNKED, "segmented vs one pass state")
+    assert np.array_equal(gpu_forward(case, "chunked", scan_segments=nseg)[1], st), "deterministic"
+
+
+@pytest.mark.parametrize("rule", ["linear", "gated", "delta", "gated_delta"])
+def test_chunked_segmented_varlen_slab(rule):
+    """Segmented scans over varlen requests in a slot slab: requests shorter
+    than the segment count (empty segments), an empty request, a ragged tail,
+    an out-of-range slot (skipped: no output, no state touched)."""
+    case = _mild(workloads.random_case(zlib.crc32(("seg/" + rule).encode()) % 1000,
+                                       lengths=[700, 0, 5, 130, 1500], H=2, HV=4, DK=128, DV=128,
+                                       dtype=np.float16, update_rule=rule, slots=(9,)), 73)
+    ids = case["slot_ids"].copy()
+    ids[3] = 9  # out of range
+    case["slot_ids"] = ids
+    d = to_dev(case)
+    T = case["q"].shape[0]
+    sentinel = torch.full((T, 4, 128), 7.0, dtype=torch.float16, device="cuda")
+    say("case segmented varlen slab %s" % rule)
+    o, slab = gpu_forward(case, "chunked", dev=d, out=sentinel, scan_segments=3)
+    cu = case["cu_seqlens"]
+    assert np.all(o[cu[3]:cu[4]] == 7.0), "the skipped request writes no output"
+    keep = np.setdiff1d(np.arange(9), ids[[0, 1, 2, 4]])
+    assert np.array_equal(slab[keep], case["slab"][keep].astype(np.float64)), "unaddressed slots untouched"
+    ro, rs = oracle_forward(case)
+    rows = np.r_[cu[0]:cu[3], cu[4]:cu[5]]
+    assert_close(o[rows], ro[rows], TOL_CHUNKED, "segmented varlen o")
+    live = ids[[0, 1, 2, 4]]
+    assert_close(slab[live], rs[live], TOL_CHUNKED, "segmented varlen slab rows")
+    assert np.array_equal(slab[ids[1]], case["slab"][ids[1]].astype(np.float64)), "empty request copies its state"
+
+
+@pytest.mark.parametrize("rule", ["gated_delta", "gated_delta_v2"])
+def test_chunked_segmented_per_key(rule):
+    """The per-key chunked form (decay per key channel; the erase gate) with
+    a segmented scan."""
+    case = _mild(workloads.random_case(74 if rule == "gated_delta" else 75, lengths=[64 * 21 + 33, 400],
+                                       H=1, HV=2, DK=128, DV=128, dtype=np.float16,
+                                       update_rule=rule, per_key=True), 76, per_key=True)
+    _start_matters(case, "per-key segmented scan")
+    say("case segmented per-key %s" % rule)
+    o, st = gpu_forward(case, "chunked", scan_segments=4)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "segmented per-key o")
+    assert_close(st, rs, TOL_CHUNKED, "segmented per-key state")
+
+
 def test_long_prefill_workload_full_chunked():
     case = workloads.long_prefill()
     _sampled(case, "chunked", [(0, [0]), (0, [7]), (0, [15])], TOL_CHUNKED, "long chunked")
