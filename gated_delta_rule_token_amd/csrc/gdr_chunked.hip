@@ -365,40 +365,108 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
     }
     lds_barrier();
 
-    // ---- [W | U] = (I + A)^-1 [diag(beta gamma / |k|) K | diag(beta) V]; column per thread
-    const int col = tid & (D128 - 1);
-    const bool wcol = tid < D128;
-    float x[CH];
-    if constexpr (RET) {
+    if constexpr (!RET) {
+        // no retrieval: U = V, stored in fragment order by the row-column threads
+        const int col = tid & (D128 - 1);
+        if (tid >= D128) {
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            // four independent partial sums keep the FMA pipeline busy
-            float r[4] = {wcol ? sRw[t] * (float)sK[t][col] : sBeta[t] * (float)sV[t][col], 0.f, 0.f, 0.f};
+            for (int qd = 0; qd < CH / 4; ++qd) {
+                f4v u;
 #pragma unroll
-            for (int s = 0; s < t; ++s) r[s & 3] = fmaf(-sA[t][s], x[s], r[s & 3]);
-            x[t] = (r[0] + r[1]) + (r[2] + r[3]);
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < CH; ++t) x[t] = wcol ? 0.f : (float)sV[t][col];
-    }
-    // U in fragment order: tokens 4 qd .. 4 qd + 3 of row col (block (qd / 4) * 8 + col / 16)
-    if (!wcol) {
-#pragma unroll
-        for (int qd = 0; qd < CH / 4; ++qd)
-            *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) =
-                f4v{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-    }
-    if constexpr (RET) {
-        lds_barrier();  // K and V are dead: W (hi, lo) rows take their place
-        if (wcol) {
-#pragma unroll
-            for (int t = 0; t < CH; ++t) {
-                const half_t hi = (half_t)x[t];
-                sW[0][t][col] = hi;
-                sW[1][t][col] = (half_t)(x[t] - (float)hi);
+                for (int i = 0; i < 4; ++i) u[i] = (float)sV[4 * qd + i][col];
+                *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) = u;
             }
         }
+        return;
+    } else {
+        // ---- [W | U] = T [diag(beta gamma / |k|) K | diag(beta) V],  T = (I + A)^-1.
+        // T by column substitution on wave 0 (lane j = column j):
+        //   T_tj = [t == j] - sum_{s<t} A_ts T_sj,
+        // T's row t is written over A's row t once every lane has read it (rows
+        // past t are read later, row t never again); zeros above the diagonal.
+        if (wave == 0) {
+            float x[CH];
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
+                x[t] = (r[0] + r[1]) + (r[2] + r[3]);
+                sA[t][lane] = x[t];
+            }
+        }
+        lds_barrier();  // T is complete
+        // Wave w forms key columns and value rows 32 w .. 32 w + 31 on the matrix
+        // cores.  Right-hand-side fragments hold 8 consecutive tokens of one key
+        // or value column; W's right-hand side is fp32 and gets (hi, lo) fp16
+        // planes, V is exact in fp16.
+        h8 bwh[2][2], bwl[2][2], bv[2][2];  // [column block c][token step ks]
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int cc = 16 * (2 * wave + c) + lr, s0 = 32 * ks + lk;
+                float xw[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    xw[x] = sRw[s0 + x] * (float)sK[s0 + x][cc];
+                    bv[c][ks][x] = sV[s0 + x][cc];
+                }
+                split8(xw, bwh[c][ks], bwl[c][ks]);
+            }
+        f4v accW[4][2], accU[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) accW[mb][c] = accU[mb][c] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < (mb < 2 ? 1 : 2); ++ks) {
+                // T rows 16 mb + lr, columns 32 ks + 8 lq .. +7 (zero above the diagonal)
+                const int t = 16 * mb + lr, s0 = 32 * ks + lk;
+                const f4v t0v = *reinterpret_cast<const f4v *>(&sA[t][s0]);
+                const f4v t1v = *reinterpret_cast<const f4v *>(&sA[t][s0 + 4]);
+                float tv[8], tb8[8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    tv[x] = t0v[x];
+                    tv[4 + x] = t1v[x];
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) tb8[x] = tv[x] * sBeta[s0 + x];
+                h8 th, tl, uh, ul;
+                split8(tv, th, tl);
+                split8(tb8, uh, ul);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    accW[mb][c] = mfma16(th, bwh[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(th, bwl[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(tl, bwh[c][ks], accW[mb][c]);
+                    accU[mb][c] = mfma16(uh, bv[c][ks], accU[mb][c]);
+                    accU[mb][c] = mfma16(ul, bv[c][ks], accU[mb][c]);
+                }
+            }
+        }
+        // U in fragment order: block tb * 8 + rt holds tokens 16 tb + 4 lq .. +3 of value row 16 rt + lr,
+        // which is the accumulator layout of (mb = tb, value row block 2 wave + c)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)((mb * 8 + 2 * wave + c) * 64 + lane)) * 16) = accU[mb][c];
+        lds_barrier();  // every wave holds its K and V fragments: W rows may overwrite them
+        // W (hi, lo) rows into LDS over K and V: accumulator (mb, c) holds
+        // tokens 16 mb + 4 lq + i of key 16 (2 wave + c) + lr
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float w = accW[mb][c][i];
+                    const half_t hi = (half_t)w;
+                    sW[0][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = hi;
+                    sW[1][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = (half_t)(w - (float)hi);
+                }
         lds_barrier();
         // W fragments: f = block * 64 + lane, block = (tb * 4 + kk) * 2 + plane
 #pragma unroll

@@ -126,7 +126,14 @@ typedef enum {
     GDR_ALGO_AUTO = 0,
     GDR_ALGO_RECURRENT = 1,  /* state tile in registers across the token loop */
     GDR_ALGO_DECODE = 2,     /* one workgroup streams one (request, head) state */
-    GDR_ALGO_CHUNKED = 3     /* chunk-parallel form (scalar-decay rules) */
+    GDR_ALGO_CHUNKED = 3     /* chunk-parallel form (fp16, dk = dv = 128).  Its products
+                              * run on fp16 matrix cores with every fp32 operand split
+                              * into an fp16 (hi, lo) pair: state entries and effective
+                              * value updates must stay below 65504 in magnitude (beyond
+                              * it the result is not finite), and a state whose every
+                              * entry is below about 1e-4 loses relative precision in the
+                              * lo part (its absolute error stays near 2^-24).  Use
+                              * GDR_ALGO_RECURRENT (all fp32) outside that range. */
 } gdr_algo;
 
 typedef struct {
