@@ -43,8 +43,12 @@ __device__ __forceinline__ void st4(f4 *p, f4 x)
 
 // G row groups (4 rows each) per wave, WAVES waves per workgroup; a head's
 // 128 rows are split over 128 / (4 * G * WAVES) workgroups.  NT marks the
-// state stream non-temporal (read once, written once).
-template <typename TA, int RULE, bool PK, int G, int WAVES, bool NT>
+// state stream non-temporal (read once, written once).  STG stages the token
+// inputs of up to 8 tokens at a time through LDS: the workgroup loads them
+// together (alongside the state, for the first block) instead of one global
+// round trip per token inside the loop; used when requests carry several
+// tokens (speculative / multi-token verify).
+template <typename TA, int RULE, bool PK, int G, int WAVES, bool NT, bool STG>
 __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
 {
     constexpr int DK = 128, C = 8;
@@ -89,26 +93,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
     const TA *__restrict__ v = static_cast<const TA *>(p.v);
     TA *__restrict__ o = static_cast<TA *>(p.o);
 
-    for (int64_t t = s; t < e; ++t) {
+    // One token: q and k columns (l16*4 .. +3, 64 + l16*4 .. +3) of this lane,
+    // v of its rows, and for a per-key decay / the erase gate their values at
+    // the lane's columns (gk: log decay, er: erase).  ga, bt: scalar log decay
+    // and update rate.
+    auto token = [&](int64_t t, float (&qv)[C], float (&kv)[C], const float (&vi)[G], float ga, float bt,
+                     const float (&gk)[C], const float (&er)[C]) {
         const size_t th = (size_t)t * HV + h;
-        float qv[C], kv[C];
-        {
-            const TA *qp = q + ((size_t)t * H + qh) * DK + l16 * 4;
-            const TA *kp = k + ((size_t)t * H + qh) * DK + l16 * 4;
-            float lo[4], hi[4];
-            load_act<TA, 4>(qp, lo);
-            load_act<TA, 4>(qp + 64, hi);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { qv[x] = lo[x]; qv[4 + x] = hi[x]; }
-            load_act<TA, 4>(kp, lo);
-            load_act<TA, 4>(kp + 64, hi);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { kv[x] = lo[x]; kv[4 + x] = hi[x]; }
-        }
-        float vi[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) vi[g] = to_f32(v[th * DK + wrow0 + g * 4 + r4]);
-
         float qss = 0.f, kss = 0.f, qk = 0.f;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -130,20 +121,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
         }
 
         float a = 1.f, bb = 1.f;
-        if constexpr (DEC && !VD) a = expf(log_decay(p, th, h));
-        if constexpr (BETA) bb = update_rate(p, th);
+        if constexpr (DEC && !VD) a = expf(ga);
+        if constexpr (BETA) bb = bt;
         float av[C], kb[C];
         if constexpr (VD) {
-            float sa = 0.f;
-            if constexpr (!PK) sa = log_decay(p, th, h);
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                const int col = (c < 4 ? 0 : 64) + l16 * 4 + (c & 3);
-                const float g = PK ? log_decay_key(p, th, h, col) : sa;
-                av[c] = expf(g);
-                float er = 1.f;
-                if constexpr (RULE == GATED_DELTA_V2) er = p.erase[th * DK + col];
-                kb[c] = er * av[c] * kv[c];
+                av[c] = expf(gk[c]);
+                kb[c] = (RULE == GATED_DELTA_V2 ? er[c] : 1.f) * av[c] * kv[c];
                 qv[c] *= av[c];
             }
         }
@@ -179,6 +164,84 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
             for (int x = 0; x < 4; ++x) { S[g][0][x] = sv[x]; S[g][1][x] = sv[4 + x]; }
             if (l16 == 0) o[th * DK + wrow0 + g * 4 + r4] = from_f32<TA>(p.scale * (u + qk * cc));
         }
+    };
+    auto col_of = [&](int c) { return (c < 4 ? 0 : 64) + l16 * 4 + (c & 3); };
+
+    if constexpr (!STG) {
+        for (int64_t t = s; t < e; ++t) {
+            const size_t th = (size_t)t * HV + h;
+            float qv[C], kv[C];
+            {
+                const TA *qp = q + ((size_t)t * H + qh) * DK + l16 * 4;
+                const TA *kp = k + ((size_t)t * H + qh) * DK + l16 * 4;
+                float lo[4], hi[4];
+                load_act<TA, 4>(qp, lo);
+                load_act<TA, 4>(qp + 64, hi);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) { qv[x] = lo[x]; qv[4 + x] = hi[x]; }
+                load_act<TA, 4>(kp, lo);
+                load_act<TA, 4>(kp + 64, hi);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) { kv[x] = lo[x]; kv[4 + x] = hi[x]; }
+            }
+            float vi[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) vi[g] = to_f32(v[th * DK + wrow0 + g * 4 + r4]);
+            float ga = 0.f, bt = 1.f, gk[C] = {}, er[C] = {};
+            if constexpr (DEC && !VD) ga = log_decay(p, th, h);
+            if constexpr (BETA) bt = update_rate(p, th);
+            if constexpr (VD) {
+                float sa = 0.f;
+                if constexpr (!PK) sa = log_decay(p, th, h);
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    gk[c] = PK ? log_decay_key(p, th, h, col_of(c)) : sa;
+                    if constexpr (RULE == GATED_DELTA_V2) er[c] = p.erase[th * DK + col_of(c)];
+                }
+            }
+            token(t, qv, kv, vi, ga, bt, gk, er);
+        }
+    } else {
+        // token inputs of up to TB tokens, widened to fp32 in LDS
+        constexpr int TB = 8, NTH = 64 * WAVES;
+        constexpr bool ER = RULE == GATED_DELTA_V2;
+        __shared__ float stq[TB][DK], stk[TB][DK], stv[TB][DK];
+        __shared__ float stg[VD ? TB : 1][DK], ste[ER ? TB : 1][DK];
+        __shared__ float sts[TB][2];
+        for (int64_t t0 = s; t0 < e; t0 += TB) {
+            const int nt = (int)((e - t0) < TB ? (e - t0) : TB);
+            for (int i = tid; i < nt * DK; i += NTH) {
+                const int tt = i >> 7, c = i & (DK - 1);
+                const size_t t = (size_t)(t0 + tt), th = t * HV + h;
+                stq[tt][c] = to_f32(q[(t * H + qh) * DK + c]);
+                stk[tt][c] = to_f32(k[(t * H + qh) * DK + c]);
+                stv[tt][c] = to_f32(v[th * DK + c]);
+                if constexpr (VD) stg[tt][c] = PK ? log_decay_key(p, th, h, c) : log_decay(p, th, h);
+                if constexpr (ER) ste[tt][c] = p.erase[th * DK + c];
+            }
+            if (tid < nt) {
+                const size_t th = (size_t)(t0 + tid) * HV + h;
+                float ga = 0.f;
+                if constexpr (DEC && !VD) ga = log_decay(p, th, h);
+                sts[tid][0] = ga;
+                sts[tid][1] = BETA ? update_rate(p, th) : 1.f;
+            }
+            lds_barrier();
+            for (int tt = 0; tt < nt; ++tt) {
+                float qv[C], kv[C], vi[G], gk[C] = {}, er[C] = {};
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    qv[c] = stq[tt][col_of(c)];
+                    kv[c] = stk[tt][col_of(c)];
+                    if constexpr (VD) gk[c] = stg[tt][col_of(c)];
+                    if constexpr (ER) er[c] = ste[tt][col_of(c)];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) vi[g] = stv[tt][wrow0 + g * 4 + r4];
+                token(t0 + tt, qv, kv, vi, sts[tt][0], sts[tt][1], gk, er);
+            }
+            lds_barrier();  // every wave is done with this block before the next one lands
+        }
     }
 
 #pragma unroll
@@ -198,14 +261,20 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
 constexpr int DEC_G = 8, DEC_WAVES = 4;
 constexpr bool DEC_NT = true;
 
+// Requests of several tokens (more tokens than requests) take the staged
+// variant; one token per request keeps the direct loads.
 template <typename TA, int RULE, bool PK>
 static hipError_t launch_one(const Params &p, hipStream_t stream)
 {
     constexpr int PARTS = 128 / (4 * DEC_G * DEC_WAVES);
     const int64_t blocks = (int64_t)p.B * p.HV * PARTS;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_decode128<TA, RULE, PK, DEC_G, DEC_WAVES, DEC_NT>), dim3((unsigned)blocks),
-                       dim3(64 * DEC_WAVES), 0, stream, p);
+    if (p.T > p.B)
+        hipLaunchKernelGGL((k_decode128<TA, RULE, PK, DEC_G, DEC_WAVES, DEC_NT, true>), dim3((unsigned)blocks),
+                           dim3(64 * DEC_WAVES), 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_decode128<TA, RULE, PK, DEC_G, DEC_WAVES, DEC_NT, false>), dim3((unsigned)blocks),
+                           dim3(64 * DEC_WAVES), 0, stream, p);
     return hipGetLastError();
 }
 
