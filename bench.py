@@ -13,10 +13,11 @@ Infinity Cache.
 
 Also reported: prefill tokens/s on the varlen workload (8 requests of
 512..8192 tokens, H=16, HV=32, dk=dv=128, fp16, raw-gate arm, qk L2-norm,
-fp32 initial/final states), on one 65,536-token sequence (H=HV=16), and on
-the per-key-decay / erase-gate workload (4 x 4096 tokens, H=8, HV=32), each
-with its algorithmic flop rate against the fp32 vector peak, and the fp64
-CPU oracle timed on the host cores on the decode step (``cpu_baseline``).
+fp32 initial/final states), on one 65,536-token sequence (H=HV=16), on
+the per-key-decay / erase-gate workload (4 x 4096 tokens, H=8, HV=32) and on
+the varlen workload with bf16 activations, each with its algorithmic flop
+rate against the fp32 vector peak, and the fp64 CPU oracle timed on the host
+cores on the decode step (``cpu_baseline``).
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 run on (torch's current stream), around every timed launch.
@@ -135,11 +136,14 @@ def bench_prefill(args, which):
     import torch
     from gated_delta_rule_token_amd import api, workloads
     case = {"varlen": workloads.varlen_prefill, "long": workloads.long_prefill,
-            "perkey": workloads.perkey_erase}[which]()
+            "perkey": workloads.perkey_erase,
+            "varlen_bf16": lambda: workloads.as_bf16(workloads.varlen_prefill())}[which]()
     q, k, v = case["q"], case["k"], case["v"]
     T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
     dk, HV, dv = q.shape[-1], v.shape[-2], v.shape[-1]
-    call = api.prepare(_t(q), _t(k), _t(v), gate=_t(case["gate"]), beta=_t(case["beta"]),
+    act = (lambda x: _t(x).to(torch.bfloat16)) if case["act_dtype"] == "bf16" else _t
+    gate = act(case["gate"]) if case["gate_activation"] == "qwen" else _t(case["gate"])
+    call = api.prepare(act(q), act(k), act(v), gate=gate, beta=_t(case["beta"]),
                        erase=_t(case["erase"]),
                        a_log=_t(case["a_log"]), dt_bias=_t(case["dt_bias"]),
                        cu_seqlens=_t(case["cu_seqlens"]), initial_state=_t(case["initial_state"]),
@@ -190,7 +194,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--decode-algo", default="auto")
     ap.add_argument("--prefill-algo", default="auto")
-    ap.add_argument("--only", choices=["decode", "mtp", "prefill", "varlen", "long", "perkey"], default=None)
+    ap.add_argument("--only", choices=["decode", "mtp", "prefill", "varlen", "long", "perkey", "bf16"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
@@ -251,6 +255,9 @@ def main():
         result["prefill_long"] = bench_prefill(args, "long")
     if args.only in (None, "prefill", "perkey"):
         result["prefill_perkey_erase"] = bench_prefill(args, "perkey")
+    if args.only in (None, "prefill", "bf16"):
+        # the varlen workload with bf16 activations (beyond the pages' type list)
+        result["prefill_bf16"] = bench_prefill(args, "varlen_bf16")
     print(json.dumps(result), flush=True)
 
 

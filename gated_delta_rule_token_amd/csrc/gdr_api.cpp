@@ -45,12 +45,12 @@ int64_t state_rows(const gdr_problem *p) { return p->num_slots > 0 ? p->num_slot
 // and the erase gate take the per-key form).
 bool chunked_per_key(const gdr_problem *p)
 {
-    return p->decay_per_key != 0 || p->update_rule == GDR_RULE_GATED_DELTA_V2;
+    return p->decay_per_key != 0 || p->update_rule == GDR_RULE_GATED_DELTA_V2 || p->act_dtype == GDR_BF16;
 }
 
 bool chunked_ok(const gdr_problem *p)
 {
-    return p->head_dim_k == 128 && p->head_dim_v == 128 && p->act_dtype == GDR_F16;
+    return p->head_dim_k == 128 && p->head_dim_v == 128 && (p->act_dtype == GDR_F16 || p->act_dtype == GDR_BF16);
 }
 
 gdr_status check_problem(const gdr_problem *p)
@@ -92,7 +92,7 @@ gdr_status check_problem(const gdr_problem *p)
     if (p->algo == GDR_ALGO_DECODE && (p->head_dim_k != 128 || p->head_dim_v != 128))
         return fail(GDR_E_UNSUPPORTED, "the decode kernel needs dk = dv = 128");
     if (p->algo == GDR_ALGO_CHUNKED && !chunked_ok(p))
-        return fail(GDR_E_UNSUPPORTED, "the chunked kernels need dk = dv = 128 and fp16 activations");
+        return fail(GDR_E_UNSUPPORTED, "the chunked kernels need dk = dv = 128 and fp16 or bf16 activations");
     return GDR_OK;
 }
 
@@ -323,7 +323,7 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     switch (pick_algo(problem)) {
     case GDR_ALGO_DECODE: err = gdr::launch_decode128(k, p.update_rule, pk, act, s); break;
     case GDR_ALGO_CHUNKED:
-        err = gdr::launch_chunked(k, p.update_rule, pk, scan_segments(problem), workspace, s);
+        err = gdr::launch_chunked(k, p.update_rule, pk, scan_segments(problem), act, workspace, s);
         break;
     default: err = gdr::launch_recurrent(k, p.update_rule, pk, act, dk_tile(p.head_dim_k), rows_group(problem), s); break;
     }

@@ -1,0 +1,1411 @@
+// gdr_chunked.hpp -- chunk-parallel prefill (chunk = 64 tokens) on MFMA.
+//
+// The "com.microsoft.GatedDeltaNet" README (Attributes, chunk_size) names a
+// chunk-parallel prefill whose chunk size does not change the result.  The
+// form used here is the recurrence of the README's Description unrolled over
+// one chunk (scalar per-head decay; V-major state S, rows = value index):
+//   gamma_t = exp(G_t), G_t = sum of the log decays up to t inside the chunk,
+//   A_ts = beta_t (gamma_t / gamma_s) kn_t.kn_s (s < t),  kn = k / |k|,
+//   W = (I+A)^-1 diag(beta gamma |k|^-1) K,   U = (I+A)^-1 diag(beta) V,
+//   D = U - W S0^T                     (the chunk's effective value updates)
+//   S_C = gamma_C S0 + D^T diag(kd) K,  kd_t = (gamma_C / gamma_t) / |k_t|,
+//   O = gq (Q S0^T) + P D,  P_ts = scale (gamma_t/gamma_s) q_t.k_s/(|q_t||k_s|) (s <= t),
+//   gq_t = scale gamma_t / |q_t|.
+// Rules without retrieval (linear, gated) have D = V.
+//
+// Three launches:
+//   k_chunk_table  one workgroup: per-request chunk offsets (exclusive scan of
+//                  ceil(len/64)); the host never reads cu_seqlens.
+//   k_chunk_prep   one workgroup per (chunk, head), all chunks in parallel:
+//                  K Q^T and K K^T on 16x16x32 f16 MFMA (q/k are fp16, so the
+//                  products are exact up to fp32 accumulation), the unit
+//                  lower-triangular solve for [W | U] by fp32 forward
+//                  substitution (one column per thread), the per-token
+//                  scalars, and every operand of the scan written in the
+//                  order the scan's lanes load it.
+//   k_chunk_scan   one workgroup per (request, head, 32 state rows), chunks
+//                  in order; the transposed state tile lives in MFMA
+//                  accumulators.  Each chunk: D = U - W S^T, then
+//                  S^T <- gamma_C S^T + K^T (kd D) on four "chain" waves, and
+//                  O^T = gq S Q^T + D^T P^T on four "output" waves.
+// Every fp32 operand is split into fp16 hi + lo and multiplied as
+// hi*hi + hi*lo + lo*hi (fp16 operands need no split), which keeps the
+// products at about fp32 accuracy on the f16 matrix cores.  The four row
+// tiles of a head are dispatched to the same XCD so their identical
+// per-chunk reads are shared through its L2.
+
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+// Each translation unit that includes this file names its own namespace for
+// the kernels (one unit per activation dtype, compiled in parallel), so the
+// kernels of different units never share a symbol.
+#ifndef GDR_CHUNK_NS
+#error "define GDR_CHUNK_NS before including gdr_chunked.hpp"
+#endif
+
+namespace gdr {
+namespace GDR_CHUNK_NS {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// 8- and 4-element vectors of an activation dtype (16- and 8-byte loads)
+template <typename TA> struct ActVec;
+template <> struct ActVec<half_t> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+};
+template <> struct ActVec<bf16_t> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+};
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u4v ld_b128_lds(const void *p) { return *reinterpret_cast<const u4v *>(p); }
+
+constexpr int CH = 64;          // chunk length
+constexpr int D128 = 128;       // dk = dv
+
+// Workspace record of one (chunk, head).  Every operand of the scan is stored
+// in MFMA fragment order: 1 KB blocks holding the 16 bytes lane l (= 16 lq + lr)
+// of a wave loads at l * 16, so each wave-wide load reads 1 KB of consecutive
+// bytes (eight whole cache lines).  Per-head decay (PK = false):
+//   W   W (hi, lo) fp16, block (tb * 4 + kk) * 2 + plane: token 16 tb + lr, keys 32 kk + 8 lq .. +7
+//   KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
+//   U   U fp32,          block tb * 8 + rt:              tokens 16 tb + 4 lq .. +3, row 16 rt + lr
+//   Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
+//   P   P (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr, tokens 32 ks + 8 lq .. +7
+//   SC  fp32 scalars: kd[64], gq[64], gamma_C
+// Decay per key channel (PK = true): the per-token weights kd and gq become
+// per-element factors, so two operands carry fp32 values and get two planes:
+//   KT  Kd^T (hi, lo),   block (mt * 2 + ks) * 2 + plane,  Kd = kn o exp(G_C - G)
+//   Q   Qg (hi, lo),     block (tb * 4 + kk) * 2 + plane,  Qg = scale qn o exp(G)
+//   SC  fp32 gamma_C of each of the 128 key channels
+template <bool PK>
+struct Rec {
+    static constexpr uint32_t W = 0;
+    static constexpr uint32_t KT = W + 32 * 1024;
+    static constexpr uint32_t U = KT + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t Q = U + 32 * 1024;
+    static constexpr uint32_t P = Q + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t SC = P + 16 * 1024;
+    static constexpr uint32_t SIZE = SC + 1024;
+};
+constexpr uint32_t R_W = Rec<false>::W, R_KT = Rec<false>::KT, R_U = Rec<false>::U, R_Q = Rec<false>::Q,
+                   R_P = Rec<false>::P, R_SC = Rec<false>::SC, WS_REC = Rec<false>::SIZE;
+
+__device__ __forceinline__ f4v mfma16(h8 a, h8 b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> (hi, lo) fp16 pair with hi + lo ~ x to about 22 bits
+__device__ __forceinline__ void split8(const float (&x)[8], h8 &hi, h8 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const half_t h = (half_t)x[i];
+        hi[i] = h;
+        lo[i] = (half_t)(x[i] - (float)h);
+    }
+}
+
+__device__ __forceinline__ h8 ld_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
+
+// Raw buffer resource over one workspace record of `bytes` bytes (an offset
+// past it reads zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *rec, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(rec), 0, (int)bytes, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// four fp32 -> (hi, lo) fp16 quads
+__device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (half_t)x[i];
+        lo[i] = (half_t)(x[i] - (float)hi[i]);
+    }
+}
+
+// Segments of the scan's chain (see k_chunk_scan).  pass 0: one pass over
+// every chunk; pass 1 / 2: the two passes of an nseg-segment scan.  xs holds,
+// per (request, head), seg_slots(nseg) states of 128 x 128 fp32: the start of
+// segment p (1 <= p < nseg), and the carry and transition of middle segment p
+// (1 <= p < nseg - 1).
+struct ScanSeg {
+    int nseg;
+    int pass;
+    float *xs;
+};
+enum SegMode : int { SEG_REAL = 0, SEG_CARRY = 1, SEG_TRANS = 2 };
+__host__ __device__ constexpr int seg_slots(int nseg) { return 3 * nseg; }
+__host__ __device__ constexpr int seg_start(int p) { return p; }
+__host__ __device__ constexpr int seg_carry(int nseg, int p) { return nseg + p; }
+__host__ __device__ constexpr int seg_trans(int nseg, int p) { return 2 * nseg + p; }
+
+// Locate request b and the chunk's first token for global chunk index ci.
+__device__ __forceinline__ int chunk_request(const int32_t *off, int B, int64_t ci)
+{
+    int lo = 0, hi = B;  // largest b in [0, B) with off[b] <= ci
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= ci) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Chunk and value head of a prologue workgroup.  Blocks x and x + 8 run on
+// the same XCD (workgroups go round-robin over the 8 XCDs), so they take
+// heads h and h + 1 of one chunk: value heads that share a q/k head read its
+// rows once into that XCD's L2 instead of once per head from HBM (measured on
+// the varlen workload: 0.75 -> 0.47 GB read by the prologue).
+__device__ __forceinline__ void prep_block(int HV, int64_t &ci, int &h)
+{
+    const int64_t x = blockIdx.x, rest = x >> 3;
+    h = (int)(rest % HV);
+    ci = (rest / HV) * 8 + (x & 7);
+}
+
+// ------------------------------------------------------------------ table
+__global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *off)
+{
+    __shared__ int32_t s[256];
+    __shared__ int32_t carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < p.B; base += 256) {
+        const int b = base + tid;
+        int n = 0;
+        if (b < p.B) {
+            int64_t st, en;
+            request_range(p, b, st, en);
+            n = (int)((en - st + CH - 1) / CH);
+        }
+        s[tid] = n;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int v = tid >= o ? s[tid - o] : 0;
+            __syncthreads();
+            s[tid] += v;
+            __syncthreads();
+        }
+        if (b < p.B) off[b] = carry + s[tid] - n;
+        __syncthreads();
+        if (tid == 255) carry += s[255];
+        __syncthreads();
+    }
+    if (tid == 0) off[p.B] = carry;
+}
+
+
+// ------------------------------------------------------------------ phase 1
+// 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
+// K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
+template <int RULE>
+__global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int32_t *__restrict__ off,
+                                                   char *__restrict__ ws)
+{
+    constexpr bool DEC = rule_decays(RULE);
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr bool BETA = rule_has_beta(RULE);
+    constexpr int LD = D128 + 8;  // padded fp16 row (bank spread)
+    constexpr int LA = CH + 4;    // 16-byte rows: the solve reads A rows as float4 broadcasts
+    constexpr int SLOT = CH * LD * 2;
+    static_assert(CH * LA * 4 == SLOT, "Q rows and A rows share one LDS footprint");
+
+    __shared__ __align__(16) char sm[3 * SLOT];
+    half_t(*sK)[LD] = reinterpret_cast<half_t(*)[LD]>(sm);
+    half_t(*sV)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + SLOT);
+    half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + 2 * SLOT);
+    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + 2 * SLOT);
+    half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm);  // [hi, lo][token][key], after the solve
+    __shared__ float sG[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
+
+    const int HV = p.HV, H = p.H;
+    int64_t ci;
+    int h;
+    prep_block(HV, ci, h);
+    if (ci >= off[p.B]) return;
+    const int b = chunk_request(off, p.B, ci);
+    int64_t rs, re;
+    request_range(p, b, rs, re);
+    const int64_t t0 = rs + (ci - off[b]) * CH;
+    const int n = (int)((re - t0) < CH ? (re - t0) : CH);
+    const int qh = (int)(((int64_t)h * H) / HV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
+    char *rec = ws + ((size_t)ci * HV + h) * WS_REC;
+
+    const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
+    const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
+    const half_t *__restrict__ v = static_cast<const half_t *>(p.v);
+
+    // ---- chunk rows of K, Q (head qh) and V (head h): issue the loads first,
+    // compute the gates while they are in flight, then park them in LDS
+    h8 ldk[4], ldq[4], ldv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        ldk[i] = ldq[i] = ldv[i] = h8{};
+        if (r < n) {
+            const size_t tq = ((size_t)(t0 + r) * H + qh) * D128 + c8;
+            ldk[i] = ld_h8(k + tq);
+            ldq[i] = ld_h8(q + tq);
+            ldv[i] = ld_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
+        }
+    }
+    // ---- per-token log decay (cumulated over the chunk by a 64-lane scan) and update rate
+    if (tid < CH) {
+        const int t = tid;
+        float g = 0.f, bt = 0.f;
+        if (t < n) {
+            const size_t th = (size_t)(t0 + t) * HV + h;
+            if constexpr (DEC) g = log_decay(p, th, h);
+            bt = BETA ? update_rate(p, th) : 1.f;
+        }
+#pragma unroll
+        for (int o = 1; o < CH; o <<= 1) {
+            const float y = __shfl_up(g, o, CH);
+            if (t >= o) g += y;
+        }
+        sG[t] = g;  // inclusive cumulative log decay inside the chunk
+        sBeta[t] = bt;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<h8 *>(&sK[r][c8]) = ldk[i];
+        *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
+        *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
+        // q in fragment order for the scan's output waves (rows past the end are zero)
+        *reinterpret_cast<h8 *>(rec + R_Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
+    }
+    lds_barrier();
+
+    // ---- K^T fragments (key 16 mt + lr, tokens 32 ks + 8 lq .. +7); fragment f = block * 64 + lane
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
+        const int key = 16 * (blk >> 1) + (fl & 15), tk = 32 * (blk & 1) + 8 * (fl >> 4);
+        h8 col;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) col[x] = sK[tk + x][key];
+        *reinterpret_cast<h8 *>(rec + R_KT + (size_t)f * 16) = col;
+    }
+    // ---- inverse L2 norms of the chunk's q and k rows: 4 threads per row
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float ss = 0.f, sq = 0.f;
+        if (p.qk_l2_norm) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const h8 kk = ld_h8(&sK[t][32 * part + 8 * g]);
+                const h8 qq = ld_h8(&sQ[t][32 * part + 8 * g]);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    ss = fmaf((float)kk[x], (float)kk[x], ss);
+                    sq = fmaf((float)qq[x], (float)qq[x], sq);
+                }
+            }
+            ss += dpp_mov<0xB1>(ss);  // sum over the 4 lanes of the row
+            ss += dpp_mov<0x4E>(ss);
+            sq += dpp_mov<0xB1>(sq);
+            sq += dpp_mov<0x4E>(sq);
+        }
+        if (part == 0) {
+            const bool on = p.qk_l2_norm && t < n;
+            sIk[t] = on ? 1.f / sqrtf(ss + 1e-12f) : 1.f;
+            sIq[t] = on ? 1.f / sqrtf(sq + 1e-12f) : 1.f;
+        }
+    }
+    lds_barrier();
+    const float scale = p.scale;
+    if (tid < CH) {
+        const int t = tid;
+        const float gl = sG[n - 1];
+        sRw[t] = sBeta[t] * expf(sG[t]) * sIk[t];  // row scale of K in W's right-hand side
+        float *sc = reinterpret_cast<float *>(rec + R_SC);
+        sc[t] = t < n ? expf(gl - sG[t]) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
+        sc[CH + t] = scale * sIq[t] * expf(sG[t]);        // gq: read-out weight of the incoming state
+        if (t == 0) sc[2 * CH] = DEC ? expf(gl) : 1.f;    // gamma_C
+    }
+
+    // ---- K Q^T and K K^T, 16 x 16 tiles (wave = token block tb, tiles sb <= tb);
+    // the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr]
+    {
+        const int tb = wave;
+        f4v accq[4], acck[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            accq[sb] = acck[sb] = f4v{0.f, 0.f, 0.f, 0.f};
+            if (sb <= tb) {
+#pragma unroll
+                for (int kk = 0; kk < D128; kk += 32) {
+                    const h8 ak = ld_h8(&sK[16 * sb + lr][kk + lk]);
+                    accq[sb] = mfma16(ak, ld_h8(&sQ[16 * tb + lr][kk + lk]), accq[sb]);
+                    if constexpr (RET) acck[sb] = mfma16(ak, ld_h8(&sK[16 * tb + lr][kk + lk]), acck[sb]);
+                }
+            }
+        }
+        lds_barrier();  // Q is dead: A takes its rows
+        const int t = 16 * tb + lr;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            const int s0 = 16 * sb + 4 * lq;
+            f4v pv, av;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = s0 + i;
+                const float dg = (s <= t) ? expf(sG[t] - sG[s]) : 0.f;
+                pv[i] = scale * sIq[t] * sIk[s] * dg * accq[sb][i];
+                av[i] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
+            }
+            h4 hi, lo;
+            split4(pv, hi, lo);
+            // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane
+            const uint32_t po = R_P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = hi;
+            *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
+        }
+    }
+    lds_barrier();
+
+    if constexpr (!RET) {
+        // no retrieval: U = V, stored in fragment order by the row-column threads
+        const int col = tid & (D128 - 1);
+        if (tid >= D128) {
+#pragma unroll
+            for (int qd = 0; qd < CH / 4; ++qd) {
+                f4v u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = (float)sV[4 * qd + i][col];
+                *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) = u;
+            }
+        }
+        return;
+    } else {
+        // ---- [W | U] = T [diag(beta gamma / |k|) K | diag(beta) V],  T = (I + A)^-1.
+        // T by column substitution on wave 0 (lane j = column j):
+        //   T_tj = [t == j] - sum_{s<t} A_ts T_sj,
+        // T's row t is written over A's row t once every lane has read it (rows
+        // past t are read later, row t never again); zeros above the diagonal.
+        if (wave == 0) {
+            float x[CH];
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
+                x[t] = (r[0] + r[1]) + (r[2] + r[3]);
+                sA[t][lane] = x[t];
+            }
+        }
+        lds_barrier();  // T is complete
+        // Wave w forms key columns and value rows 32 w .. 32 w + 31 on the matrix
+        // cores.  Right-hand-side fragments hold 8 consecutive tokens of one key
+        // or value column; W's right-hand side is fp32 and gets (hi, lo) fp16
+        // planes, V is exact in fp16.
+        h8 bwh[2][2], bwl[2][2], bv[2][2];  // [column block c][token step ks]
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int cc = 16 * (2 * wave + c) + lr, s0 = 32 * ks + lk;
+                float xw[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    xw[x] = sRw[s0 + x] * (float)sK[s0 + x][cc];
+                    bv[c][ks][x] = sV[s0 + x][cc];
+                }
+                split8(xw, bwh[c][ks], bwl[c][ks]);
+            }
+        f4v accW[4][2], accU[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) accW[mb][c] = accU[mb][c] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < (mb < 2 ? 1 : 2); ++ks) {
+                // T rows 16 mb + lr, columns 32 ks + 8 lq .. +7 (zero above the diagonal)
+                const int t = 16 * mb + lr, s0 = 32 * ks + lk;
+                const f4v t0v = *reinterpret_cast<const f4v *>(&sA[t][s0]);
+                const f4v t1v = *reinterpret_cast<const f4v *>(&sA[t][s0 + 4]);
+                float tv[8], tb8[8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    tv[x] = t0v[x];
+                    tv[4 + x] = t1v[x];
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) tb8[x] = tv[x] * sBeta[s0 + x];
+                h8 th, tl, uh, ul;
+                split8(tv, th, tl);
+                split8(tb8, uh, ul);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    accW[mb][c] = mfma16(th, bwh[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(th, bwl[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(tl, bwh[c][ks], accW[mb][c]);
+                    accU[mb][c] = mfma16(uh, bv[c][ks], accU[mb][c]);
+                    accU[mb][c] = mfma16(ul, bv[c][ks], accU[mb][c]);
+                }
+            }
+        }
+        // U in fragment order: block tb * 8 + rt holds tokens 16 tb + 4 lq .. +3 of value row 16 rt + lr,
+        // which is the accumulator layout of (mb = tb, value row block 2 wave + c)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)((mb * 8 + 2 * wave + c) * 64 + lane)) * 16) = accU[mb][c];
+        lds_barrier();  // every wave holds its K and V fragments: W rows may overwrite them
+        // W (hi, lo) rows into LDS over K and V: accumulator (mb, c) holds
+        // tokens 16 mb + 4 lq + i of key 16 (2 wave + c) + lr
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float w = accW[mb][c][i];
+                    const half_t hi = (half_t)w;
+                    sW[0][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = hi;
+                    sW[1][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = (half_t)(w - (float)hi);
+                }
+        lds_barrier();
+        // W fragments: f = block * 64 + lane, block = (tb * 4 + kk) * 2 + plane
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
+            const int tb = blk >> 3, kk = (blk >> 1) & 3, pl = blk & 1;
+            *reinterpret_cast<h8 *>(rec + R_W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][32 * kk + 8 * (fl >> 4)]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ phase 1, per-key decay
+// Decay per key channel (Ascend "aclnnRecurrentGatedDeltaRule", Formula) and
+// the key-axis erase gate of Gated DeltaNet-2 (ONNX issue "Spec gap ...
+// Gated DeltaNet-2", "The GDN-2 recurrence").  With G[t][j] the cumulative
+// log decay of key channel j up to token t inside the chunk, kn = k / |k|,
+// qn = q / |q| (or the raw vectors without qk_l2_norm), and the retrieval key
+// l_t = beta_t kn_t (delta rules) or b_t o kn_t (erase gate), unrolling the
+// recurrence over the chunk gives
+//   A_ts = sum_j l_tj kn_sj exp(G_tj - G_sj)  (s < t),   P_ts = scale sum_j qn_tj kn_sj exp(G_tj - G_sj)  (s <= t)
+//   W = (I + A)^-1 (l o e^G),   U = (I + A)^-1 diag(w) V   (w = beta, or 1 for the erase gate)
+//   Qg = scale qn o e^G,   Kd = kn o e^(G_C - G),   gamma_C = e^(G_C)
+// and the scan's chunk step D = U - W S^T, O = Qg S^T + P D,
+// S^T <- Diag(gamma_C) S^T + Kd^T D.
+//
+// A and P are 16 x 16 blocks (s block sb <= t block tb) of fp32 matrix-core
+// products over the key channels.  Each block splits its decay at the last
+// token e = 16 sb + 15 of block sb: exp(G_t - G_s) = exp(G_t - G_e) exp(G_e - G_s).
+// For decaying channels the second factor is <= 1, and so is the first off
+// the diagonal; on the diagonal the first is >= 1 and bounded by the decay
+// inside the block.  A diagonal block whose decay can exceed DIAG_NATS in
+// some channel (and, with growing channels, every block of the chunk) is
+// summed term by term instead, so no factor leaves the fp32 range.
+//
+// 256 threads, two workgroups per CU.  LDS: K and Q rows (fp16) and G (fp32);
+// after the Gram products A takes Q's rows and V takes K's, and after the
+// solve the W (hi, lo) rows take Q's and G's.
+constexpr float DIAG_NATS = 80.f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (one instruction; results below the normal
+// range flush toward zero, which only ever drops terms smaller than 1e-38)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename TA, int RULE, bool PKG>
+__global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const int32_t *__restrict__ off,
+                                                          char *__restrict__ ws)
+{
+    using RC = Rec<true>;
+    typedef typename ActVec<TA>::v8 a8;
+    typedef typename ActVec<TA>::v4 a4;
+    constexpr bool DEC = rule_decays(RULE);
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr bool BETA = rule_has_beta(RULE);
+    constexpr bool V2 = RULE == GATED_DELTA_V2;
+    constexpr int LD = D128 + 8;   // padded fp16 row
+    constexpr int LF = D128 + 4;   // padded fp32 row
+    constexpr int LA = CH + 4;
+    constexpr int SLOT = CH * LD * 2;
+    static_assert(CH * LA * 4 == SLOT, "A rows fill Q's slot");
+    static_assert(2 * SLOT <= SLOT + CH * LF * 4, "W planes fit over Q and G");
+
+    __shared__ __align__(16) char sm[2 * SLOT + CH * LF * 4];
+    TA(*sK)[LD] = reinterpret_cast<TA(*)[LD]>(sm);            // K rows; V rows after the Gram
+    TA(*sQ)[LD] = reinterpret_cast<TA(*)[LD]>(sm + SLOT);     // Q rows
+    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + SLOT);       // A after the Gram
+    float(*sG)[LF] = reinterpret_cast<float(*)[LF]>(sm + 2 * SLOT);   // G log2(e): cumulative log2 decay
+    half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm + SLOT);  // W (hi, lo) after the solve
+    __shared__ float sIk[CH], sIq[CH], sWt[CH];
+    __shared__ float sTot[2][D128], sPos[2][D128];
+    __shared__ int sFlag;
+
+    const int HV = p.HV, H = p.H;
+    int64_t ci;
+    int h;
+    prep_block(HV, ci, h);
+    if (ci >= off[p.B]) return;
+    const int b = chunk_request(off, p.B, ci);
+    int64_t rs, re;
+    request_range(p, b, rs, re);
+    const int64_t t0 = rs + (ci - off[b]) * CH;
+    const int n = (int)((re - t0) < CH ? (re - t0) : CH);
+    const int qh = (int)(((int64_t)h * H) / HV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int col = tid & (D128 - 1);
+    char *rec = ws + ((size_t)ci * HV + h) * RC::SIZE;
+    const TA *__restrict__ q = static_cast<const TA *>(p.q);
+    const TA *__restrict__ k = static_cast<const TA *>(p.k);
+    const TA *__restrict__ v = static_cast<const TA *>(p.v);
+    const float scale = p.scale;
+    // erase gate row of chunk token t (rows past the end read the last token's)
+    auto erase_row = [&](int t) { return p.erase + ((size_t)(t0 + (t < n ? t : n - 1)) * HV + h) * D128; };
+
+    // ---- load phase: K, Q, V rows (fp16), log decay rows (fp32); the W-column
+    // threads also fetch their erase-gate column for the solve's right-hand side
+    a8 ldk[4], ldq[4], ldv[4];
+    f4v ldg[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        ldk[i] = ldq[i] = ldv[i] = a8{};
+        if (r < n) {
+            const size_t tq = ((size_t)(t0 + r) * H + qh) * D128 + c8;
+            ldk[i] = *reinterpret_cast<const a8 *>(k + tq);
+            ldq[i] = *reinterpret_cast<const a8 *>(q + tq);
+            ldv[i] = *reinterpret_cast<const a8 *>(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+        ldg[i] = f4v{0.f, 0.f, 0.f, 0.f};
+        if (r < n) {
+            const size_t th = (size_t)(t0 + r) * HV + h;
+            if constexpr (PKG) {
+                if (p.gate_dt == 0 && !p.gate_qwen) {
+                    ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) ldg[i][x] = log_decay_key(p, th, h, c4 + x);
+                }
+            } else {
+                const float g = DEC ? log_decay(p, th, h) : 0.f;
+                ldg[i] = f4v{g, g, g, g};
+            }
+        }
+    }
+    float ev[CH];  // erase gate column of a W-column thread
+    if constexpr (V2) {
+        if (tid < D128) {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) ev[t] = erase_row(t)[col];
+        }
+    }
+    if (tid < CH) {
+        const int t = tid;
+        float w = 0.f;
+        if (t < n) w = BETA ? update_rate(p, (size_t)(t0 + t) * HV + h) : 1.f;
+        sWt[t] = w;
+    }
+    if (tid == 0) sFlag = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<a8 *>(&sK[r][c8]) = ldk[i];
+        *reinterpret_cast<a8 *>(&sQ[r][c8]) = ldq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+        *reinterpret_cast<f4v *>(&sG[r][c4]) = ldg[i];
+    }
+    lds_barrier();
+
+    // ---- cumulative log decay: thread (key col, half hf) scans tokens
+    // 32 hf .. 32 hf + 31 (bands 2 hf, 2 hf + 1), then adds the first half's total.
+    // Guard sums: the decay inside each band (past its first token) bounds the
+    // diagonal split factor; the total growth of the chunk bounds every other.
+    {
+        const int hf = tid >> 7;
+        float run = 0.f, pos = 0.f, neg[2] = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const int t = 32 * hf + r;
+            const float g = sG[t][col];
+            run += g;
+            sG[t][col] = run;
+            pos += fmaxf(g, 0.f);
+            if (r & 15) neg[r >> 4] += fmaxf(-g, 0.f);
+        }
+        sTot[hf][col] = run;
+        sPos[hf][col] = pos;
+        int big = 0;
+        if (neg[0] > DIAG_NATS) big |= 1 << (2 * hf);
+        if (neg[1] > DIAG_NATS) big |= 1 << (2 * hf + 1);
+        if (big) atomicOr(&sFlag, big);
+    }
+    // ---- inverse L2 norms of the chunk's q and k rows: 4 threads per row
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float ss = 0.f, sq = 0.f;
+        if (p.qk_l2_norm) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const a8 kk = *reinterpret_cast<const a8 *>(&sK[t][32 * part + 8 * g]);
+                const a8 qq = *reinterpret_cast<const a8 *>(&sQ[t][32 * part + 8 * g]);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    ss = fmaf((float)kk[x], (float)kk[x], ss);
+                    sq = fmaf((float)qq[x], (float)qq[x], sq);
+                }
+            }
+            ss += dpp_mov<0xB1>(ss);  // sum over the 4 lanes of the row
+            ss += dpp_mov<0x4E>(ss);
+            sq += dpp_mov<0xB1>(sq);
+            sq += dpp_mov<0x4E>(sq);
+        }
+        if (part == 0) {
+            const bool on = p.qk_l2_norm && t < n;
+            sIk[t] = on ? 1.f / sqrtf(ss + 1e-12f) : 1.f;
+            sIq[t] = on ? 1.f / sqrtf(sq + 1e-12f) : 1.f;
+        }
+    }
+    lds_barrier();
+    // second half adds the first half's total; both convert to log2 units
+    if (tid >= D128) {
+        const float add = sTot[0][col];
+#pragma unroll
+        for (int r = 32; r < CH; ++r) sG[r][col] = (sG[r][col] + add) * LOG2E;
+    } else {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) sG[r][col] *= LOG2E;
+        if (sPos[0][col] + sPos[1][col] > DIAG_NATS) atomicOr(&sFlag, 16);
+    }
+    lds_barrier();
+
+    // ---- operands built from G: Kd^T and Qg fragments (4 + 4 per thread), gamma_C
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // Kd^T: key j, tokens 32 ks + 8 l4 .. +7
+        const int f = tid + 256 * i, j = f & (D128 - 1), grp = f >> 7, ks = grp >> 2, l4 = grp & 3;
+        const float gc = sG[CH - 1][j];
+        float x8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int u = 32 * ks + 8 * l4 + x;
+            x8[x] = (float)sK[u][j] * sIk[u] * ex2(gc - sG[u][j]);
+        }
+        h8 hi, lo;
+        split8(x8, hi, lo);
+        char *dst = rec + RC::KT + ((uint32_t)(((j >> 4) * 2 + ks) * 2) * 64 + l4 * 16 + (j & 15)) * 16;
+        *reinterpret_cast<h8 *>(dst) = hi;
+        *reinterpret_cast<h8 *>(dst + 1024) = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // Qg: token 16 tb + lr, keys 32 kk + 8 lq .. +7
+        const int f = tid + 256 * i, blk = f >> 6, fl = f & 63;
+        const int t = 16 * (blk >> 2) + (fl & 15), key = 32 * (blk & 3) + 8 * (fl >> 4);
+        const a8 qq = *reinterpret_cast<const a8 *>(&sQ[t][key]);
+        float x8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * ex2(sG[t][key + x]);
+        h8 hi, lo;
+        split8(x8, hi, lo);
+        char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
+        *reinterpret_cast<h8 *>(dst) = hi;
+        *reinterpret_cast<h8 *>(dst + 1024) = lo;
+    }
+    if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
+
+    // ---- A and P, 16 x 16 blocks (sb <= tb) on the fp32 matrix cores; wave w
+    // takes pairs w, w + 4, w + 8.  Lane (lr, lq) sums key channels 32 lq .. 32 lq + 31,
+    // and the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr] without the
+    // per-token factors (applied below).
+    constexpr int8_t PTB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int8_t PSB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    const int flags = sFlag;
+    f4v resA[3], resP[3];
+#pragma unroll
+    for (int slot = 0; slot < 3; ++slot) {
+        const int pi = wave + 4 * slot;
+        resA[slot] = resP[slot] = f4v{0.f, 0.f, 0.f, 0.f};
+        if (pi < 10) {
+            const int tb = PTB[pi], sb = PSB[pi], e = 16 * sb + 15;
+            const int t = 16 * tb + lr, sr = 16 * sb + lr;
+            const float *er = V2 ? erase_row(t) : nullptr;
+            if ((flags & 16) || (tb == sb && ((flags >> tb) & 1))) {
+                // strong decay inside the block (or growth): every term with its own exponential
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * sb + 4 * lq + i;
+                    float a = 0.f, pq = 0.f;
+                    if (s <= t) {
+                        for (int j = 0; j < D128; ++j) {
+                            const float kx = (float)sK[s][j] * ex2(sG[t][j] - sG[s][j]);
+                            if constexpr (RET) a = fmaf((V2 ? er[j] : 1.f) * (float)sK[t][j], kx, a);
+                            pq = fmaf((float)sQ[t][j], kx, pq);
+                        }
+                    }
+                    resA[slot][i] = a;
+                    resP[slot][i] = pq;
+                }
+            } else {
+                f4v eb[8];
+                if constexpr (V2) {
+#pragma unroll
+                    for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
+                }
+                f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < 8; ++kq) {
+                    const int key = 32 * lq + 4 * kq;
+                    const f4v gt = *reinterpret_cast<const f4v *>(&sG[t][key]);
+                    const f4v ge = *reinterpret_cast<const f4v *>(&sG[e][key]);
+                    const f4v gs = *reinterpret_cast<const f4v *>(&sG[sr][key]);
+                    const a4 kt = *reinterpret_cast<const a4 *>(&sK[t][key]);
+                    const a4 ks = *reinterpret_cast<const a4 *>(&sK[sr][key]);
+                    const a4 qt = *reinterpret_cast<const a4 *>(&sQ[t][key]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float exa = ex2(gt[x] - ge[x]);
+                        const float right = (float)ks[x] * ex2(ge[x] - gs[x]);
+                        if constexpr (RET)
+                            accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (V2 ? eb[kq][x] : 1.f) * (float)kt[x] * exa, accA, 0, 0, 0);
+                        accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (float)qt[x] * exa, accP, 0, 0, 0);
+                    }
+                }
+                resA[slot] = accA;
+                resP[slot] = accP;
+            }
+        }
+    }
+    // ---- right-hand side of W for key column col (threads 0-127)
+    float x[CH];
+    if (tid < D128) {
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            const float lt = (V2 ? ev[t] : sWt[t]) * sIk[t] * (float)sK[t][col];
+            x[t] = RET ? lt * ex2(sG[t][col]) : 0.f;
+        }
+    }
+    lds_barrier();  // K and Q are dead: V takes K's rows, A takes Q's
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
+        *reinterpret_cast<a8 *>(&sK[r][c8]) = ldv[i];
+    }
+#pragma unroll
+    for (int slot = 0; slot < 3; ++slot) {
+        const int pi = wave + 4 * slot;
+        if (pi < 10) {
+            const int tb = PTB[pi], sb = PSB[pi];
+            const int t = 16 * tb + lr, s0 = 16 * sb + 4 * lq;
+            const float at = (V2 ? 1.f : sWt[t]) * sIk[t], pt = scale * sIq[t];
+            f4v pv, av;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = s0 + i;
+                pv[i] = s <= t ? pt * sIk[s] * resP[slot][i] : 0.f;
+                av[i] = s < t ? at * sIk[s] * resA[slot][i] : 0.f;
+            }
+            h4 hi, lo;
+            split4(pv, hi, lo);
+            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = hi;
+            *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
+        }
+    }
+#pragma unroll
+    for (int zi = 0; zi < 2; ++zi) {
+        // the P blocks above the diagonal are zero (the scan multiplies them anyway)
+        constexpr int8_t ZTB[6] = {0, 0, 0, 1, 1, 2};
+        constexpr int8_t ZSB[6] = {1, 2, 3, 2, 3, 3};
+        const int z = wave + 4 * zi;
+        if (z < 6) {
+            const int tb = ZTB[z], sb = ZSB[z], s0 = 16 * sb + 4 * lq;
+            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = h4{};
+            *reinterpret_cast<h4 *>(rec + po + 1024) = h4{};
+        }
+    }
+    lds_barrier();
+
+    // ---- [W | U] = (I + A)^-1 [l o e^G | diag(w) V]; one column per thread
+    const bool wcol = tid < D128;
+    if (!wcol) {
+#pragma unroll
+        for (int t = 0; t < CH; ++t) x[t] = (RET ? sWt[t] : 1.f) * (float)sK[t][col];
+    }
+    if constexpr (RET) {
+#pragma unroll
+        for (int t = 1; t < CH; ++t) {
+            float r[4] = {x[t], 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < t; ++s) r[s & 3] = fmaf(-sA[t][s], x[s], r[s & 3]);
+            x[t] = (r[0] + r[1]) + (r[2] + r[3]);
+        }
+    }
+    if (!wcol) {
+#pragma unroll
+        for (int qd = 0; qd < CH / 4; ++qd)
+            *reinterpret_cast<f4v *>(rec + RC::U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) =
+                f4v{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+    }
+    if constexpr (RET) {
+        lds_barrier();  // A and G are dead: W (hi, lo) rows take their place
+        if (wcol) {
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                const half_t hi = (half_t)x[t];
+                sW[0][t][col] = hi;
+                sW[1][t][col] = (half_t)(x[t] - (float)hi);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
+            const int tb = blk >> 3, kk = (blk >> 1) & 3, pl = blk & 1;
+            *reinterpret_cast<h8 *>(rec + RC::W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][32 * kk + 8 * (fl >> 4)]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ phase 2
+// 512 threads.  Waves 0-3 carry the state chain of a 32-row tile, kept
+// transposed (key rows, state-row columns) in MFMA accumulators; waves 4-7
+// compute the outputs from the chain's LDS copies of S and D.  Per chunk j
+// (LDS buffer j & 1):
+//   chain:  A  S (hi, lo) -> sS[b]                         | output: -
+//           == barrier 1 ==
+//           B  D = U - W S^T -> sDt[b], (kd D) -> sDs      | O1 O^T = S Q^T
+//           == barrier 2 ==
+//           E  S^T <- gamma_C S^T + K^T (kd D)             | O2 O^T = gq O^T + D^T P^T, store
+// S and D are double-buffered, so a buffer is rewritten only after every
+// output wave has passed the barrier that follows its last read.  Operands
+// are read with buffer loads: the chunk record's base goes into a scalar
+// resource descriptor and each lane's offset is a loop-invariant register, so
+// the loop does no vector address arithmetic.  The operands of chunk j + 1
+// are loaded during chunk j into the second of two register sets; every load
+// is unconditional, since a branch around a load makes the compiler wait for
+// it on the spot.
+// With a decay per key channel (PK) the state decays by a vector gamma_C, and
+// Kd^T and Qg carry fp32 values split into (hi, lo) planes, so stage E and O1
+// take three products each; stage E then reads D^T directly (no kd D copy).
+//
+// Segmented chain.  A chunk step maps every state row affinely,
+// s <- s M_j + c_j (M_j = gamma_C I - W^T diag(kd) K, c_j the row's share of
+// kd U K), so a request's chunks can be cut into nseg segments that run side
+// by side.  Pass 1 runs segment 0 for real (writing its end state as the start
+// of segment 1) and, for each middle segment p, a carry tile (zero start:
+// c_p = the segment's end state from zero) and a transition tile (the 128 rows
+// of the identity as start, U left out: M_p = the product of the segment's
+// M_j).  k_seg_combine then forms start_{p+1} = start_p M_p + c_p, and pass 2
+// runs segments 1 .. nseg-1 for real from those starts.  The longest serial
+// chain shrinks from n chunk steps to about 2 n / nseg.
+template <typename TA, int RULE, int NVB, bool PK>
+__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const ScanSeg sg)
+{
+    using RC = Rec<PK>;
+    constexpr int NPL = PK ? 2 : 1;       // fp16 planes of the K^T and q operands
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr int TR = 16 * NVB;          // state rows of this workgroup
+    constexpr int NTILE = D128 / TR;      // workgroups per head
+    constexpr int LS = D128 + 8;  // fp16 state row (272 B)
+    constexpr int LDT = CH + 8;   // fp16 row of the transposed delta (144 B)
+
+    // Row strides of 68 and 36 dwords put the 16 lanes of a 16-byte access
+    // phase on 16 distinct 4-bank groups.
+    __shared__ __align__(16) half_t sS[2][2][TR][LS];    // [buffer][hi, lo][row][key]
+    __shared__ __align__(16) half_t sDt[2][2][TR][LDT];  // [buffer][hi, lo][row][token] D^T
+    __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][LDT];  // [hi, lo][row][token] (kd D)^T, chain only
+    __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
+
+    const int HV = p.HV;
+    // A group is one (request, head) -- with segments one (request, head,
+    // segment) -- and its units are its row tiles (pass 1: carry tiles, then
+    // transition tiles).  XCD-aware order: blocks i, i + 8, ... (one XCD) are
+    // the units of one group, which read the same chunk records.
+    const int NU = (sg.pass == 1 ? 2 : 1) * NTILE;
+    const int nsg = sg.pass == 0 ? 1 : sg.nseg - 1;  // groups per (request, head)
+    const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
+    const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
+    if (gi >= (int64_t)p.B * HV * nsg) return;
+    const int bh = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    const int tile = unit % NTILE;
+    const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
+    if (mode == SEG_TRANS && seg == 0) return;  // segment 0 has no transition tiles
+    const int b = bh / HV, h = bh % HV;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
+    const int row0 = tile * TR;
+    const uint32_t l16 = (uint32_t)lane * 16;
+
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, b, h, src, dst)) return;
+    int64_t rs, re;
+    request_range(p, b, rs, re);
+    const int c0 = off[b], nch = off[b + 1] - off[b];
+    // this unit's chunks [cb, ce) of the request, its start state and where its end state goes
+    const int ns = sg.pass == 0 ? 1 : sg.nseg;
+    const int cb = (int)((int64_t)seg * nch / ns), ce = (int)((int64_t)(seg + 1) * nch / ns);
+    const float *from = src;
+    float *to = dst;
+    if (sg.pass != 0) {
+        float *xs = sg.xs + (size_t)bh * seg_slots(ns) * (D128 * D128);
+        if (mode == SEG_REAL) {
+            from = seg == 0 ? src : xs + (size_t)seg_start(seg) * (D128 * D128);
+            to = seg == ns - 1 ? dst : seg == 0 ? xs + (size_t)seg_start(1) * (D128 * D128) : nullptr;
+        } else {
+            from = nullptr;
+            to = xs + (size_t)(mode == SEG_CARRY ? seg_carry(ns, seg) : seg_trans(ns, seg)) * (D128 * D128);
+        }
+    }
+    const int tb = wave & 3;  // token block of this wave (D rows for the chain, O columns for the output)
+
+    if (wave < 4) {
+        // ================================================================ chain
+        const float um = mode == SEG_TRANS ? 0.f : 1.f;  // a transition tile leaves U out
+        // Sc[a][rt][i] = S[row0 + 16 rt + lr][16 (2 wave + a) + 4 lq + i]
+        f4v Sc[2][NVB];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rt = 0; rt < NVB; ++rt)
+            {
+                const int row = row0 + 16 * rt + lr, col = 16 * (2 * wave + a) + 4 * lq;
+                if (from) {
+                    Sc[a][rt] = *reinterpret_cast<const f4v *>(from + (size_t)row * D128 + col);
+                } else {
+                    // zero, or row `row` of the identity for a transition tile
+                    const float one = mode == SEG_TRANS ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sc[a][rt][i] = row == col + i ? one : 0.f;
+                }
+            }
+        struct Ops {
+            h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
+            h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
+            f4v u[NVB];         // U at this lane's D positions, one per row block
+            f4v kd;             // per head: kd of this lane's four D tokens
+            float gc;           // per head: gamma_C
+            f4v gk[2];          // per key: gamma_C of keys 16 (2 wave + a) + 4 lq .. +3
+        };
+        const uint32_t offW = RC::W + (uint32_t)tb * 8 * 1024 + l16;
+        const uint32_t offK = RC::KT + (uint32_t)(2 * wave) * 2 * NPL * 1024 + l16;
+        const uint32_t offU = RC::U + (uint32_t)(tb * 8 + NVB * tile) * 1024 + l16;
+        const uint32_t offKd = RC::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
+        const uint32_t offGk = RC::SC + (uint32_t)(32 * wave + 4 * lq) * 4;
+        auto fetch = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+            if constexpr (RET) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    f.wh[kk] = ld_b128<h8>(r, offW + 2048 * kk);
+                    f.wl[kk] = ld_b128<h8>(r, offW + 2048 * kk + 1024);
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int pl = 0; pl < NPL; ++pl) f.kt[a][ks][pl] = ld_b128<h8>(r, offK + ((2 * a + ks) * NPL + pl) * 1024);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) f.u[vb] = ld_b128<f4v>(r, offU + vb * 1024);
+            if constexpr (PK) {
+                f.gk[0] = ld_b128<f4v>(r, offGk);
+                f.gk[1] = ld_b128<f4v>(r, offGk + 64);
+            } else {
+                f.kd = ld_b128<f4v>(r, offKd);
+                f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, RC::SC + 2 * CH * 4, 0, 0));
+            }
+        };
+        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+            const int bf = j & 1;
+            // ---- A: state tile -> LDS (hi, lo), four consecutive keys per write
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt) {
+                    h4 hi, lo;
+                    split4(Sc[a][rt], hi, lo);
+                    *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = hi;
+                    *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = lo;
+                }
+            fetch(j + 1 < ce ? j + 1 : j, nxt);  // the last chunk re-reads itself
+            // keep the prefetch where it is: neither the optimiser nor the
+            // scheduler may move the loads past this point in either direction
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // 1
+            // ---- B: D = U - W S^T for token block tb and every row block (D rows = tokens)
+            f4v accD[NVB];
+            {
+                // hi*hi and lo*hi share a chain; with two row blocks hi*lo gets its
+                // own (enough independent chains to keep the matrix core busy)
+                constexpr int NA = NVB >= 4 ? 1 : 2;
+                f4v a2[NVB][2] = {};
+                if constexpr (RET) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                        for (int vb = 0; vb < NVB; ++vb) {
+                            const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
+                            const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                            a2[vb][0] = mfma16(cur.wh[kk], shi, a2[vb][0]);
+                            a2[vb][NA - 1] = mfma16(cur.wh[kk], slo, a2[vb][NA - 1]);
+                            a2[vb][0] = mfma16(cur.wl[kk], shi, a2[vb][0]);
+                        }
+                }
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) accD[vb] = NA == 2 ? a2[vb][0] + a2[vb][1] : a2[vb][0];
+            }
+            // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
+            // tokens per lane -> one 8-byte write per plane
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                f4v d;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[i] = um * cur.u[vb][i] - accD[vb][i];
+                h4 dh, dl;
+                split4(d, dh, dl);
+                const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
+                *reinterpret_cast<h4 *>(&sDt[bf][0][r][c]) = dh;
+                *reinterpret_cast<h4 *>(&sDt[bf][1][r][c]) = dl;
+                if constexpr (!PK) {
+                    f4v ds;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ds[i] = cur.kd[i] * d[i];
+                    h4 sh, sl;
+                    split4(ds, sh, sl);
+                    *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
+                    *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
+                }
+            }
+            lds_barrier();  // 2
+            // ---- E: S^T <- gamma_C S^T + K^T (kd D) for key tiles 2 wave + a, row blocks rt
+            // (per key: S^T <- Diag(gamma_C) S^T + Kd^T D)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt) {
+                    if constexpr (PK) Sc[a][rt] *= cur.gk[a];
+                    else Sc[a][rt] *= cur.gc;
+                }
+            {
+                // with two row blocks the lo products get their own chains
+                constexpr bool SEPL = NVB < 4 || PK;
+                f4v lo4[2][NVB] = {};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int rt = 0; rt < NVB; ++rt) {
+                        const h8 dhi = PK ? ld_h8(&sDt[bf][0][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[0][16 * rt + lr][32 * ks + lk]);
+                        const h8 dlo = PK ? ld_h8(&sDt[bf][1][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[1][16 * rt + lr][32 * ks + lk]);
+#pragma unroll
+                        for (int a = 0; a < 2; ++a) {
+                            Sc[a][rt] = mfma16(cur.kt[a][ks][0], dhi, Sc[a][rt]);
+                            if constexpr (SEPL) lo4[a][rt] = mfma16(cur.kt[a][ks][0], dlo, lo4[a][rt]);
+                            else Sc[a][rt] = mfma16(cur.kt[a][ks][0], dlo, Sc[a][rt]);
+                            if constexpr (PK) lo4[a][rt] = mfma16(cur.kt[a][ks][NPL - 1], dhi, lo4[a][rt]);
+                        }
+                    }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int rt = 0; rt < NVB; ++rt)
+                        if constexpr (SEPL) Sc[a][rt] += lo4[a][rt];
+            }
+        };
+        // two operand sets used in turn, so no register copy waits on a prefetch
+        Ops opa, opb;
+        if (ce > cb) fetch(cb, opa);
+        for (int j = cb; j < ce; j += 2) {
+            step(j, opa, opb);
+            if (j + 1 < ce) step(j + 1, opb, opa);
+        }
+        if (to) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt)
+                    *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt];
+        }
+    } else if (mode != SEG_REAL) {
+        // carry and transition tiles write no output: these waves only keep
+        // the chain's two barriers per chunk step
+        for (int j = cb; j < ce; ++j) {
+            lds_barrier();
+            lds_barrier();
+        }
+    } else {
+        // ================================================================ outputs
+        TA *o = static_cast<TA *>(p.o);
+        struct Ops {
+            h8 q[4][NPL];     // q rows (per key: Qg hi, lo) of token block tb, four k-steps of 32
+            h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
+            float gq;         // per head: gq of this lane's token
+        };
+        const uint32_t offQ = RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16;
+        // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
+        const int tok_bytes = HV * D128 * 2;
+        // after the LDS transpose each lane stores 16 bytes (8 rows of a token):
+        // TR / 8 lanes per token, so a 32-row tile uses every lane for its 16
+        // tokens and a 16-row tile the first 32 lanes; the others get an offset
+        // past the store's range, which the buffer store drops
+        static_assert(TR == 32 || TR == 16, "the output transpose takes 16- or 32-row tiles");
+        constexpr int LPT = TR / 8;
+        const bool st_live = lane / LPT < 16;
+        const int st_tok = st_live ? lane / LPT : 15, st_q = lane % LPT;
+        const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
+        const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
+        const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
+        auto fetch = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f.ph[ks] = ld_b128<h8>(r, offP + ks * 2048);
+                f.pl[ks] = ld_b128<h8>(r, offP + ks * 2048 + 1024);
+            }
+            if constexpr (!PK) f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
+        };
+        // Store the output tile of chunk jo, staged in sO, as one 16-byte write per
+        // lane.  The store is unconditional: the resource spans the chunk's
+        // valid tokens only (none for jo < 0), so lanes past the request's end
+        // write nothing (a branch here would make every later wait drain it).
+        auto store_out = [&](int jo) {
+            const int64_t t0 = rs + (int64_t)jo * CH;
+            const int n = jo >= cb ? (int)((re - t0) < CH ? (re - t0) : CH) : 0;
+            TA *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
+            const __amdgpu_buffer_rsrc_t ro =
+                __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok][8 * st_q]), ro, offO, 0, 0);
+        };
+        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+            const int bf = j & 1;
+            fetch(j + 1 < ce ? j + 1 : j, nxt);
+            asm volatile("" ::: "memory");  // pin the prefetch (see the chain role)
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // 1 (also completes this wave's staging of chunk j - 1)
+            store_out(j - 1);
+            // ---- O1: O^T = S Q^T for row blocks 0, 1 and token block tb:
+            // rows 16 vb + 4 lq + i, token 16 tb + lr
+            f4v acc[NVB], acl[NVB];
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = acl[vb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
+                    const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                    acc[vb] = mfma16(shi, cur.q[kk][0], acc[vb]);
+                    acl[vb] = mfma16(slo, cur.q[kk][0], acl[vb]);
+                    if constexpr (PK) acl[vb] = mfma16(shi, cur.q[kk][NPL - 1], acl[vb]);
+                }
+            lds_barrier();  // 2
+            // ---- O2: O^T = gq O^T + D^T P^T; P is lower triangular (zeros above the
+            // diagonal are multiplied anyway so every prefetched fragment is used)
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                if constexpr (PK) acc[vb] = acc[vb] + acl[vb];
+                else acc[vb] = cur.gq * (acc[vb] + acl[vb]);
+            }
+            {
+                f4v p3[NVB] = {};  // the two lo products in their own chain
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][32 * ks + lk]);
+                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][32 * ks + lk]);
+                        acc[vb] = mfma16(dhi, cur.ph[ks], acc[vb]);
+                        p3[vb] = mfma16(dlo, cur.ph[ks], p3[vb]);
+                        p3[vb] = mfma16(dhi, cur.pl[ks], p3[vb]);
+                    }
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
+            }
+            // stage the tile as [token][row]; the next chunk (or the loop's end) stores it
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                typename ActVec<TA>::v4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = from_f32<TA>(acc[vb][i]);
+                *reinterpret_cast<typename ActVec<TA>::v4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
+            }
+        };
+        Ops opa, opb;
+        if (ce > cb) fetch(cb, opa);
+        {
+            // a store that writes nothing (empty resource): on entry the loop
+            // then sees the same outstanding pattern as in steady state (the
+            // previous chunk's output store behind the prefetch), so the
+            // compiler's waits for the prefetch need not cover a real store
+            const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(u4v{0u, 0u, 0u, 0u}, none, 0, 0, 0);
+        }
+        for (int j = cb; j < ce; j += 2) {
+            step(j, opa, opb);
+            if (j + 1 < ce) step(j + 1, opb, opa);
+        }
+        if (ce > cb) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging has landed
+            store_out(ce - 1);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ segment starts
+// start_{p+1} = start_p M_p + c_p for the middle segments p = 1 .. nseg - 2,
+// in order; rows are independent, so one workgroup takes 16 rows of one
+// (request, head) and keeps them in LDS from one segment to the next.
+__global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanSeg sg)
+{
+    const int64_t bh = blockIdx.x >> 3;
+    const int rb = blockIdx.x & 7;
+    if (bh >= (int64_t)p.B * p.HV) return;
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, (int)(bh / p.HV), (int)(bh % p.HV), src, dst)) return;
+    __shared__ float sR[16][D128];
+    const int tid = threadIdx.x, c = tid & 127, r0 = (tid >> 7) * 8;
+    constexpr size_t HEAD = (size_t)D128 * D128;
+    float *xs = sg.xs + (size_t)bh * seg_slots(sg.nseg) * HEAD;
+    const size_t rows = (size_t)(16 * rb) * D128;
+    for (int i = tid; i < 16 * D128; i += 256) sR[i >> 7][i & 127] = xs[seg_start(1) * HEAD + rows + i];
+    __syncthreads();
+    for (int sp = 1; sp + 1 < sg.nseg; ++sp) {
+        const float *M = xs + (size_t)seg_trans(sg.nseg, sp) * HEAD;
+        const float *C = xs + (size_t)seg_carry(sg.nseg, sp) * HEAD + rows;
+        float acc[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] = C[(size_t)(r0 + r) * D128 + c];
+        for (int j = 0; j < D128; ++j) {
+            const float m = M[(size_t)j * D128 + c];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[r] = fmaf(sR[r0 + r][j], m, acc[r]);
+        }
+        __syncthreads();  // every thread has read the old rows
+        float *S = xs + (size_t)seg_start(sp + 1) * HEAD + rows;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            sR[r0 + r][c] = acc[r];
+            S[(size_t)(r0 + r) * D128 + c] = acc[r];
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+static size_t seg_offset(int64_t T, int B, int HV, bool per_key)
+{
+    const int64_t maxch = (T + CH - 1) / CH + B;
+    const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
+    return table + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
+}
+
+static size_t workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg)
+{
+    const size_t segs = nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0;
+    return seg_offset(T, B, HV, per_key) + segs;
+}
+
+// Row tile of the scan: 16 * NVB rows, NVB = 1 or 2 (measured on MI355X:
+// 64-row tiles halve the per-row operand reads but lengthen each chunk step
+// by 1.7x, which loses on both the single long sequence and the batched
+// prefill).
+template <typename TA, int RULE, int NVB, bool PK>
+static void launch_scan(const Params &p, const int32_t *off, const char *rec, const ScanSeg &sg, hipStream_t s)
+{
+    constexpr int NTILE = D128 / (16 * NVB);
+    const int64_t groups = (int64_t)p.B * p.HV * (sg.pass == 0 ? 1 : sg.nseg - 1);
+    const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
+    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, sg);
+}
+
+// Scan launches.  Few (request, head) pairs leave most CUs idle with 32-row
+// tiles; 16-row tiles double the workgroups and shorten each chunk step
+// (measured on MI355X: one 65,536-token sequence x 16 heads 2.65 -> 2.18 ms),
+// while with many pairs the GPU is full and the larger tiles amortise the
+// operand reads (8 x 32 heads: 1.27 ms with 32-row tiles, 1.47 ms with 16-row
+// tiles).  A segmented scan runs pass 1 (carry and transition tiles: twice
+// the workgroups of pass 2) in 32-row tiles and pass 2 by the same rule as a
+// single pass over its (request, head, segment) groups: two workgroups of
+// this kernel on one CU share its vector-memory pipeline and each chunk step
+// then takes about twice as long (measured on MI355X, 65,536 tokens x 16
+// heads in 3 segments: 1.82 ms with 32-row pass-1 tiles, 1.89 ms with 16-row).
+template <typename TA, int RULE, bool PK>
+static void launch_scans(const Params &p, const int32_t *off, const char *rec, float *xs, int nseg, hipStream_t s)
+{
+    const int64_t pairs = (int64_t)p.B * p.HV;
+    if (nseg <= 1) {
+        const ScanSeg one{1, 0, nullptr};
+        if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, one, s);
+        else launch_scan<TA, RULE, 2, PK>(p, off, rec, one, s);
+        return;
+    }
+    launch_scan<TA, RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 1, xs}, s);
+    if (nseg > 2) {
+        const int64_t blocks = pairs * 8;
+        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, ScanSeg{nseg, 0, xs});
+    }
+    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
+    else launch_scan<TA, RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
+}
+
+// PK: the per-key record and kernels; PKG: the gate itself is per key (else
+// a per-head gate broadcast over the key channels).  The per-head record and
+// prologue (PK = false) take fp16 activations only.
+template <typename TA, int RULE, bool PK, bool PKG>
+static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s)
+{
+    const int64_t maxch = (p.T + CH - 1) / CH + p.B;
+    const size_t table = ((size_t)(p.B + 1) * 4 + 255) / 256 * 256;
+    char *base = static_cast<char *>(ws);
+    int32_t *off = reinterpret_cast<int32_t *>(base);
+    char *rec = base + table;
+    float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.HV, PK));
+    hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
+    if (maxch * p.HV > 0) {
+        if constexpr (PK)
+            hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
+        else
+            hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
+    }
+    launch_scans<TA, RULE, PK>(p, off, rec, xs, nseg, s);
+    return hipGetLastError();
+}
+
+}  // namespace GDR_CHUNK_NS
+}  // namespace gdr

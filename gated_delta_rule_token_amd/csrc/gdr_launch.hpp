@@ -15,13 +15,15 @@ hipError_t launch_recurrent(const Params &p, int rule, bool per_key, int act, in
 // Decode kernel, dk = dv = 128 only.
 hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hipStream_t s);
 
-// Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 activations); the
-// per-key form (per_key) serves a decay per key channel and the erase gate.
+// Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 or bf16 activations,
+// act = 1 or 2); the per-key form serves a decay per key channel, the erase
+// gate and every bf16 problem (per_key here: the gate itself is per key).
 // nseg > 1 cuts each request's chain of chunk steps into that many segments
 // (two scan passes and a combine step).  `ws` holds
-// chunked_workspace_bytes(T, B, HV, per_key, nseg) bytes.
-size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg);
-hipError_t launch_chunked(const Params &p, int rule, bool per_key, int nseg, void *ws, hipStream_t s);
+// chunked_workspace_bytes(T, B, HV, per-key form, nseg) bytes.
+size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key_form, int nseg);
+hipError_t launch_chunked(const Params &p, int rule, bool per_key, int nseg, int act, void *ws, hipStream_t s);
+hipError_t launch_chunked_bf16(const Params &p, int rule, bool per_key, int nseg, void *ws, hipStream_t s);
 
 // Standalone gate fusion.
 hipError_t launch_gate(int64_t count, int heads, int dtype, const void *a, const float *dt_bias,

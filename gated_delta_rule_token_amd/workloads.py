@@ -207,6 +207,17 @@ def odd_shape(seed: int = 5, dtype=np.float32):
         act_dtype="f32" if dtype == np.float32 else "f16")
 
 
+def as_bf16(case):
+    """The same case with bf16 activations: q, k, v (and a raw gate given in
+    the activation dtype) rounded onto the bf16 grid, held as float32."""
+    out = dict(case, act_dtype="bf16", name=case["name"].replace("_f16", "") + "_bf16")
+    keys = ("q", "k", "v") + (("gate",) if case["gate_activation"] == "qwen" else ())
+    for key in keys:
+        if out[key] is not None:
+            out[key] = bf16_grid(out[key].astype(np.float32))
+    return out
+
+
 def random_case(seed, *, T=None, lengths=None, H=2, HV=4, DK=32, DV=32, dtype=np.float32,
                 update_rule="gated_delta", gate_activation="none", beta_activation="none",
                 qk_l2_norm=0, per_key=False, with_initial=True, unit_keys=True,

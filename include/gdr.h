@@ -97,8 +97,8 @@ typedef enum {
 
 /* Activation dtypes.  bf16 goes beyond the pages' type list (fp32, fp16;
  * README, Type constraints): the loads widen it exactly to fp32 and the
- * output is rounded to nearest even on store; the chunked kernels take fp16
- * only, so bf16 runs on the decode and recurrent kernels. */
+ * output is rounded to nearest even on store; on the chunked kernels bf16
+ * takes the per-key form, whose prologue works on fp32 values. */
 typedef enum { GDR_F32 = 0, GDR_F16 = 1, GDR_BF16 = 2 } gdr_dtype;
 
 typedef enum {
@@ -126,7 +126,7 @@ typedef enum {
     GDR_ALGO_AUTO = 0,
     GDR_ALGO_RECURRENT = 1,  /* state tile in registers across the token loop */
     GDR_ALGO_DECODE = 2,     /* one workgroup streams one (request, head) state */
-    GDR_ALGO_CHUNKED = 3     /* chunk-parallel form (fp16, dk = dv = 128).  Its products
+    GDR_ALGO_CHUNKED = 3     /* chunk-parallel form (fp16 or bf16, dk = dv = 128).  Its products
                               * run on fp16 matrix cores with every fp32 operand split
                               * into an fp16 (hi, lo) pair: state entries and effective
                               * value updates must stay below 65504 in magnitude (beyond

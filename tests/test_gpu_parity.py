@@ -125,7 +125,8 @@ def test_decode_workload_full():
     del slab0
 
 
-def _sampled(case, algo, pairs, tol, label):
+def _sampled(case, algo, pairs, tol, label, tol_state=None):
+    tol_state = tol if tol_state is None else tol_state
     say("case %s algo=%s (GPU full, oracle on %d sampled request-head pairs)" % (case["name"], algo, len(pairs)))
     o, st = gpu_forward(case, algo)
     T = o.shape[0] * (o.shape[1] if o.ndim == 4 else 1)
@@ -134,7 +135,7 @@ def _sampled(case, algo, pairs, tol, label):
         sc, (s, e) = sub_case(case, b, heads)
         ro, rs = oracle_forward(sc)
         assert_close(of[s:e][:, heads], ro, tol, "%s o req %d heads %s" % (label, b, heads))
-        assert_close(st[b][heads], rs[0], tol, "%s state req %d heads %s" % (label, b, heads))
+        assert_close(st[b][heads], rs[0], tol_state, "%s state req %d heads %s" % (label, b, heads))
 
 
 def test_decode_workload_four_tokens_per_request():
@@ -598,6 +599,50 @@ def test_bf16_activations(algo, dk, dv, L, rule, per_key):
                                  gate_activation="none" if per_key else "qwen",
                                  beta_activation="none" if per_key else "sigmoid", qk_l2_norm=1)
     _check_full(case, algo, "bf16 %s %s" % (rule, algo))
+
+
+BF16_CHUNK_RULES = [("linear", False), ("gated", False), ("gated", True), ("delta", False),
+                    ("gated_delta", False), ("gated_delta", True), ("gated_delta_v2", False),
+                    ("gated_delta_v2", True)]
+
+
+@pytest.mark.parametrize("rule,per_key", BF16_CHUNK_RULES,
+                         ids=["%s%s" % (r, "_pk" if k else "") for r, k in BF16_CHUNK_RULES])
+def test_bf16_chunked(rule, per_key):
+    """bf16 activations on the chunked kernels (every rule takes the per-key
+    form): several chunks, a ragged tail, one token, an empty request; raw
+    gate in bf16 and sigmoid update rate where the rule has them."""
+    kw = dict(qk_l2_norm=1)
+    if rule in ("gated", "gated_delta", "gated_delta_v2") and not per_key:
+        kw["gate_activation"] = "qwen"
+    if rule in ("delta", "gated_delta"):
+        kw["beta_activation"] = "sigmoid"
+    case = workloads.random_case(zlib.crc32(("bf16chunk/%s/%d" % (rule, per_key)).encode()) % 1000,
+                                 lengths=[200, 1, 0, 64, 130], H=2, HV=4, DK=128, DV=128, dtype="bf16",
+                                 update_rule=rule, per_key=per_key, **kw)
+    o, st = _check_full(case, "chunked", "bf16 chunked %s" % rule)
+    o2, st2 = gpu_forward(case, "recurrent")
+    # each side rounds o to bf16 on its own, so the two may differ by both roundings
+    assert_close(o, o2, 2 * TOL_BF16_O, "bf16 chunked vs recurrent o")
+    assert_close(st, st2, TOL_CHUNKED, "bf16 chunked vs recurrent state")
+
+
+def test_bf16_chunked_segmented():
+    """bf16 on the chunked kernels with the chain cut into segments."""
+    case = _mild(workloads.random_case(77, lengths=[64 * 30 + 5], H=1, HV=2, DK=128, DV=128, dtype="bf16",
+                                       update_rule="gated_delta"), 78)
+    say("case bf16 segmented scan")
+    o, st = gpu_forward(case, "chunked", scan_segments=4)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_BF16_O, "bf16 segmented o")
+    assert_close(st, rs, TOL_CHUNKED, "bf16 segmented state")
+
+
+def test_bf16_varlen_prefill_workload_full_chunked():
+    """The varlen prefill workload (8 requests, 29,273 tokens, H=16, HV=32)
+    with its activations on the bf16 grid: AUTO runs the chunked kernels."""
+    case = workloads.as_bf16(workloads.varlen_prefill())
+    _sampled(case, "auto", [(0, [0, 31]), (5, [20])], TOL_BF16_O, "bf16 varlen chunked", TOL_CHUNKED)
 
 
 # ------------------------------------------------------------------ sizes past 32-bit byte offsets
