@@ -614,13 +614,6 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             }
         }
     }
-    float ev[CH];  // erase gate column of a W-column thread
-    if constexpr (V2) {
-        if (tid < D128) {
-#pragma unroll
-            for (int t = 0; t < CH; ++t) ev[t] = erase_row(t)[col];
-        }
-    }
     if (tid < CH) {
         const int t = tid;
         float w = 0.f;
@@ -738,6 +731,18 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     }
     if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
 
+    // erase gate at this lane's right-hand-side fragment positions of W
+    // (tokens 32 ks + 8 lq + x, key 16 (2 wave + c) + lr), in flight during the Gram blocks
+    float ev[2][2][8];
+    if constexpr (V2) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) ev[c][ks][x] = erase_row(32 * ks + 8 * lq + x)[16 * (2 * wave + c) + lr];
+    }
+
     // ---- A and P, 16 x 16 blocks (sb <= tb) on the fp32 matrix cores; wave w
     // takes pairs w, w + 4, w + 8.  Lane (lr, lq) sums key channels 32 lq .. 32 lq + 31,
     // and the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr] without the
@@ -800,21 +805,43 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             }
         }
     }
-    // ---- right-hand side of W for key column col (threads 0-127)
-    float x[CH];
-    if (tid < D128) {
+    // ---- right-hand side of W, l o e^G, in matrix-core fragments: wave w takes
+    // key columns 32 w .. 32 w + 31 (blocks c), tokens 32 ks + 8 lq .. +7;
+    // fp32 values, so (hi, lo) fp16 planes
+    h8 bwh[2][2], bwl[2][2];
+    if constexpr (RET) {
 #pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            const float lt = (V2 ? ev[t] : sWt[t]) * sIk[t] * (float)sK[t][col];
-            x[t] = RET ? lt * ex2(sG[t][col]) : 0.f;
-        }
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int j = 16 * (2 * wave + c) + lr, s0 = 32 * ks + 8 * lq;
+                float xw[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int u = s0 + x;
+                    xw[x] = (V2 ? ev[c][ks][x] : sWt[u]) * sIk[u] * to_f32(sK[u][j]) * ex2(sG[u][j]);
+                }
+                split8(xw, bwh[c][ks], bwl[c][ks]);
+            }
     }
-    lds_barrier();  // K and Q are dead: V takes K's rows, A takes Q's
+    lds_barrier();  // K, Q and G are dead: V takes K's rows, A takes Q's, W's right-hand side G's
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
         *reinterpret_cast<a8 *>(&sK[r][c8]) = ldv[i];
+    }
+    // W's right-hand-side fragments wait in LDS (in fragment order: one
+    // 16-byte read each later), so no register holds them across the solve
+    h8 *sBw = reinterpret_cast<h8 *>(sm + 2 * SLOT);  // [plane][wave][c][ks][lane]
+    if constexpr (RET) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                sBw[((0 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane] = bwh[c][ks];
+                sBw[((1 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane] = bwl[c][ks];
+            }
     }
 #pragma unroll
     for (int slot = 0; slot < 3; ++slot) {
@@ -853,37 +880,106 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     }
     lds_barrier();
 
-    // ---- [W | U] = (I + A)^-1 [l o e^G | diag(w) V]; one column per thread
-    const bool wcol = tid < D128;
-    if (!wcol) {
+    if constexpr (!RET) {
+        // no retrieval: U = V, stored in fragment order by the row-column threads
+        if (tid >= D128) {
 #pragma unroll
-        for (int t = 0; t < CH; ++t) x[t] = (RET ? sWt[t] : 1.f) * (float)sK[t][col];
-    }
-    if constexpr (RET) {
+            for (int qd = 0; qd < CH / 4; ++qd) {
+                f4v u;
 #pragma unroll
-        for (int t = 1; t < CH; ++t) {
-            float r[4] = {x[t], 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < t; ++s) r[s & 3] = fmaf(-sA[t][s], x[s], r[s & 3]);
-            x[t] = (r[0] + r[1]) + (r[2] + r[3]);
-        }
-    }
-    if (!wcol) {
-#pragma unroll
-        for (int qd = 0; qd < CH / 4; ++qd)
-            *reinterpret_cast<f4v *>(rec + RC::U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) =
-                f4v{x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
-    }
-    if constexpr (RET) {
-        lds_barrier();  // A and G are dead: W (hi, lo) rows take their place
-        if (wcol) {
-#pragma unroll
-            for (int t = 0; t < CH; ++t) {
-                const half_t hi = (half_t)x[t];
-                sW[0][t][col] = hi;
-                sW[1][t][col] = (half_t)(x[t] - (float)hi);
+                for (int i = 0; i < 4; ++i) u[i] = to_f32(sK[4 * qd + i][col]);
+                *reinterpret_cast<f4v *>(rec + RC::U + ((uint32_t)(((qd >> 2) * 8 + (col >> 4)) * 64 + (qd & 3) * 16 + (col & 15))) * 16) = u;
             }
         }
+        return;
+    } else {
+        // ---- [W | U] = T [l o e^G | diag(w) V],  T = (I + A)^-1, as in the
+        // per-head prologue: wave 0 forms T by column substitution over A's
+        // rows, then wave w takes key columns and value rows 32 w .. 32 w + 31
+        // on the matrix cores (W: three split products, U: V is exact in the
+        // activation dtype only when that is fp16, so both operands of U get
+        // (hi, lo) planes for bf16).
+        if (wave == 0) {
+            float x[CH];
+#pragma unroll
+            for (int t = 0; t < CH; ++t) {
+                float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
+                x[t] = (r[0] + r[1]) + (r[2] + r[3]);
+                sA[t][lane] = x[t];
+            }
+        }
+        lds_barrier();  // T is complete
+        constexpr bool VX = sizeof(TA) == 2 && !__is_same(TA, bf16_t);  // V exact in fp16
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bwh[c][ks] = sBw[((0 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane];
+                bwl[c][ks] = sBw[((1 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane];
+            }
+        h8 bvh[2][2], bvl[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int cc = 16 * (2 * wave + c) + lr, s0 = 32 * ks + 8 * lq;
+                float xv[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) xv[x] = to_f32(sK[s0 + x][cc]);
+                split8(xv, bvh[c][ks], bvl[c][ks]);
+            }
+        f4v accW[4][2], accU[4][2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) accW[mb][c] = accU[mb][c] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < (mb < 2 ? 1 : 2); ++ks) {
+                const int t = 16 * mb + lr, s0 = 32 * ks + 8 * lq;
+                const f4v t0v = *reinterpret_cast<const f4v *>(&sA[t][s0]);
+                const f4v t1v = *reinterpret_cast<const f4v *>(&sA[t][s0 + 4]);
+                float tv[8], tw[8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    tv[x] = t0v[x];
+                    tv[4 + x] = t1v[x];
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) tw[x] = tv[x] * sWt[s0 + x];
+                h8 th, tl, uh, ul;
+                split8(tv, th, tl);
+                split8(tw, uh, ul);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    accW[mb][c] = mfma16(th, bwh[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(th, bwl[c][ks], accW[mb][c]);
+                    accW[mb][c] = mfma16(tl, bwh[c][ks], accW[mb][c]);
+                    accU[mb][c] = mfma16(uh, bvh[c][ks], accU[mb][c]);
+                    accU[mb][c] = mfma16(ul, bvh[c][ks], accU[mb][c]);
+                    if constexpr (!VX) accU[mb][c] = mfma16(uh, bvl[c][ks], accU[mb][c]);
+                }
+            }
+        }
+        // U: accumulator (mb, c) is block mb * 8 + 2 wave + c of the record
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                *reinterpret_cast<f4v *>(rec + RC::U + ((uint32_t)((mb * 8 + 2 * wave + c) * 64 + lane)) * 16) = accU[mb][c];
+        lds_barrier();  // T and V are read: W (hi, lo) rows take the place of A and G
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float w = accW[mb][c][i];
+                    const half_t hi = (half_t)w;
+                    sW[0][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = hi;
+                    sW[1][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = (half_t)(w - (float)hi);
+                }
         lds_barrier();
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
