@@ -512,7 +512,9 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
 // S^T <- Diag(gamma_C) S^T + Kd^T D.
 //
 // A and P are 16 x 16 blocks (s block sb <= t block tb) of fp32 matrix-core
-// products over the key channels.  Each block splits its decay at the last
+// products over the key channels.  A per-head decay broadcast over the
+// channels (the erase gate with a scalar decay, every bf16 problem) leaves
+// exp(G_t - G_s) outside the key sum and takes it per element afterwards.  Each block splits its decay at the last
 // token e = 16 sb + 15 of block sb: exp(G_t - G_s) = exp(G_t - G_e) exp(G_e - G_s).
 // For decaying channels the second factor is <= 1, and so is the first off
 // the diagonal; on the diagonal the first is >= 1 and bounded by the decay
@@ -759,7 +761,38 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             const int tb = PTB[pi], sb = PSB[pi], e = 16 * sb + 15;
             const int t = 16 * tb + lr, sr = 16 * sb + lr;
             const float *er = V2 ? erase_row(t) : nullptr;
-            if ((flags & 16) || (tb == sb && ((flags >> tb) & 1))) {
+            if constexpr (!PKG) {
+                // one decay for every key channel: exp(G_t - G_s) leaves the key sum
+                // as a scalar, so the products carry no exponentials and the factor
+                // (<= 1 for s <= t when the head decays) is applied per element after
+                f4v eb[8];
+                if constexpr (V2) {
+#pragma unroll
+                    for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
+                }
+                f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < 8; ++kq) {
+                    const int key = 32 * lq + 4 * kq;
+                    const a4 kt = *reinterpret_cast<const a4 *>(&sK[t][key]);
+                    const a4 ks = *reinterpret_cast<const a4 *>(&sK[sr][key]);
+                    const a4 qt = *reinterpret_cast<const a4 *>(&sQ[t][key]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float right = to_f32(ks[x]);
+                        if constexpr (RET)
+                            accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (V2 ? eb[kq][x] : 1.f) * to_f32(kt[x]), accA, 0, 0, 0);
+                        accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, to_f32(qt[x]), accP, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * sb + 4 * lq + i;
+                    const float f = s <= t ? ex2(sG[t][0] - sG[s][0]) : 0.f;
+                    resA[slot][i] = accA[i] * f;
+                    resP[slot][i] = accP[i] * f;
+                }
+            } else if ((flags & 16) || (tb == sb && ((flags >> tb) & 1))) {
                 // strong decay inside the block (or growth): every term with its own exponential
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
