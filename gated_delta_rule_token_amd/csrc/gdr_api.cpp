@@ -188,23 +188,27 @@ int32_t pick_algo(const gdr_problem *p)
 }
 
 // Segments of the chunked scan's chain: the caller's count, or a split of
-// long requests when few (request, head) pairs leave most CUs idle.  Each
-// segment pass then runs about 32 (request, head, segment) groups, one
-// 16-row-tile workgroup per CU (measured on MI355X, chunk scan + prologue:
-// 65,536 tokens x 16 heads 2.12 -> 1.82 ms in 3 segments; x 8 heads
-// 1.85 -> 1.10 ms in 5; 32,768 tokens x 4 heads 0.79 -> 0.47 ms in 5; with 32
-// pairs or more a split is slower, 1.41 -> 1.72 ms at 32,768 tokens x 32).
-// Segments shorter than 16 chunks are not worth the extra passes.
+// long requests when few (request, head) pairs leave most CUs idle.  The
+// count aims pass 2 at about 512 workgroups of 16 rows, two per CU (with a
+// power-of-two number of pairs every CU gets the same number; uneven counts
+// leave some CUs a workgroup more than the rest), with at most 16 segments
+// of at least 16 chunks each.  Measured on
+// MI355X (prologue + scan, one request): 65,536 tokens x 16 heads 2.0 ms in
+// one pass, 1.68 / 1.81 / 1.55 / 1.94 ms in 3 / 4 / 5 / 6 segments; x 8 heads
+// 1.71 ms, 1.01 / 0.94 ms in 5 / 9; 32,768 tokens x 4 heads 0.70 ms,
+// 0.36 / 0.41 ms in 9 / 16; 16,384 tokens x 16 heads 0.55 -> 0.47 ms in 5;
+// shorter requests gain nothing and 32 pairs or more lose (32,768 tokens x
+// 32 heads 1.35 -> 1.36 ms in 3).
 int scan_segments(const gdr_problem *p)
 {
     if (p->scan_segments > 0) return p->scan_segments;
     const int64_t pairs = (int64_t)p->batch * p->num_heads_v;
     const int64_t chunks_per_req = p->batch > 0 ? p->total_tokens / p->batch / 64 : 0;
-    if (pairs < 1 || pairs > 16 || chunks_per_req < 128) return 1;
-    int64_t n = 1 + 32 / pairs;
-    if (n > 16) n = 16;
-    if (n > chunks_per_req / 16) n = chunks_per_req / 16;
-    return n >= 3 ? (int)n : 1;
+    if (pairs < 1 || pairs > 16 || chunks_per_req < 256) return 1;
+    int64_t groups = 64 / pairs;  // (request, head, segment) groups per pair in pass 2
+    while (groups > 15) groups /= 2;
+    if (groups > chunks_per_req / 16 - 1) groups = chunks_per_req / 16 - 1;
+    return groups >= 2 ? (int)groups + 1 : 1;
 }
 
 int dk_tile(int dk) { return dk <= 32 ? 32 : dk <= 64 ? 64 : dk <= 128 ? 128 : 256; }

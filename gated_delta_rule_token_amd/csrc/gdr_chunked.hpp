@@ -1149,7 +1149,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const uint32_t offU = RC::U + (uint32_t)(tb * 8 + NVB * tile) * 1024 + l16;
         const uint32_t offKd = RC::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
         const uint32_t offGk = RC::SC + (uint32_t)(32 * wave + 4 * lq) * 4;
-        auto fetch = [&](int jj, Ops &f) {
+        // One operand set, reloaded for chunk jj right after its last use in the
+        // current chunk (stage B's operands after D is formed, stage E's after the
+        // state update), so the loads overlap the rest of the step.
+        auto fetchB = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
             if constexpr (RET) {
 #pragma unroll
@@ -1159,23 +1162,27 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 }
             }
 #pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) f.u[vb] = ld_b128<f4v>(r, offU + vb * 1024);
+            if constexpr (!PK) f.kd = ld_b128<f4v>(r, offKd);
+        };
+        auto fetchE = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+#pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl) f.kt[a][ks][pl] = ld_b128<h8>(r, offK + ((2 * a + ks) * NPL + pl) * 1024);
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) f.u[vb] = ld_b128<f4v>(r, offU + vb * 1024);
             if constexpr (PK) {
                 f.gk[0] = ld_b128<f4v>(r, offGk);
                 f.gk[1] = ld_b128<f4v>(r, offGk + 64);
             } else {
-                f.kd = ld_b128<f4v>(r, offKd);
                 f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, RC::SC + 2 * CH * 4, 0, 0));
             }
         };
-        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+        auto step = [&](int j, Ops &cur) {
             const int bf = j & 1;
+            const int jn = j + 1 < ce ? j + 1 : j;  // the last chunk re-reads itself
             // ---- A: state tile -> LDS (hi, lo), four consecutive keys per write
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -1186,11 +1193,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = hi;
                     *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = lo;
                 }
-            fetch(j + 1 < ce ? j + 1 : j, nxt);  // the last chunk re-reads itself
-            // keep the prefetch where it is: neither the optimiser nor the
-            // scheduler may move the loads past this point in either direction
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
             lds_barrier();  // 1
             // ---- B: D = U - W S^T for token block tb and every row block (D rows = tokens)
             f4v accD[NVB];
@@ -1216,22 +1218,31 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             }
             // D at (tokens 16 tb + 4 lq + i, state row 16 vb + lr): four consecutive
             // tokens per lane -> one 8-byte write per plane
+            f4v dv[NVB], dsv[NVB];
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
-                f4v d;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) d[i] = um * cur.u[vb][i] - accD[vb][i];
+                for (int i = 0; i < 4; ++i) dv[vb][i] = um * cur.u[vb][i] - accD[vb][i];
+                if constexpr (!PK) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dsv[vb][i] = cur.kd[i] * dv[vb][i];
+                }
+            }
+            // stage B's operands are used up: load chunk jn's, and keep the loads
+            // here (neither the optimiser nor the scheduler may move them)
+            fetchB(jn, cur);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
                 h4 dh, dl;
-                split4(d, dh, dl);
+                split4(dv[vb], dh, dl);
                 const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
                 *reinterpret_cast<h4 *>(&sDt[bf][0][r][c]) = dh;
                 *reinterpret_cast<h4 *>(&sDt[bf][1][r][c]) = dl;
                 if constexpr (!PK) {
-                    f4v ds;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ds[i] = cur.kd[i] * d[i];
                     h4 sh, sl;
-                    split4(ds, sh, sl);
+                    split4(dsv[vb], sh, sl);
                     *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
                     *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
                 }
@@ -1270,14 +1281,16 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     for (int rt = 0; rt < NVB; ++rt)
                         if constexpr (SEPL) Sc[a][rt] += lo4[a][rt];
             }
+            fetchE(jn, cur);  // stage E's operands are used up
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
         };
-        // two operand sets used in turn, so no register copy waits on a prefetch
-        Ops opa, opb;
-        if (ce > cb) fetch(cb, opa);
-        for (int j = cb; j < ce; j += 2) {
-            step(j, opa, opb);
-            if (j + 1 < ce) step(j + 1, opb, opa);
+        Ops op;
+        if (ce > cb) {
+            fetchB(cb, op);
+            fetchE(cb, op);
         }
+        for (int j = cb; j < ce; ++j) step(j, op);
         if (to) {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -1314,18 +1327,25 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
         const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
-        auto fetch = [&](int jj, Ops &f) {
+        // one operand set, each part reloaded for chunk jj right after its last use
+        auto fetchQ = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
+        };
+        auto fetchG = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+            if constexpr (!PK) f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
+        };
+        auto fetchP = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 f.ph[ks] = ld_b128<h8>(r, offP + ks * 2048);
                 f.pl[ks] = ld_b128<h8>(r, offP + ks * 2048 + 1024);
             }
-            if constexpr (!PK) f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
         };
         // Store the output tile of chunk jo, staged in sO, as one 16-byte write per
         // lane.  The store is unconditional: the resource spans the chunk's
@@ -1339,11 +1359,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
             __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok][8 * st_q]), ro, offO, 0, 0);
         };
-        auto step = [&](int j, const Ops &cur, Ops &nxt) {
+        auto step = [&](int j, Ops &cur) {
             const int bf = j & 1;
-            fetch(j + 1 < ce ? j + 1 : j, nxt);
-            asm volatile("" ::: "memory");  // pin the prefetch (see the chain role)
-            __builtin_amdgcn_sched_barrier(0);
+            const int jn = j + 1 < ce ? j + 1 : j;
             lds_barrier();  // 1 (also completes this wave's staging of chunk j - 1)
             store_out(j - 1);
             // ---- O1: O^T = S Q^T for row blocks 0, 1 and token block tb:
@@ -1361,6 +1379,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     acl[vb] = mfma16(slo, cur.q[kk][0], acl[vb]);
                     if constexpr (PK) acl[vb] = mfma16(shi, cur.q[kk][NPL - 1], acl[vb]);
                 }
+            fetchQ(jn, cur);  // pinned like the chain's loads
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
             lds_barrier();  // 2
             // ---- O2: O^T = gq O^T + D^T P^T; P is lower triangular (zeros above the
             // diagonal are multiplied anyway so every prefetched fragment is used)
@@ -1369,6 +1390,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 if constexpr (PK) acc[vb] = acc[vb] + acl[vb];
                 else acc[vb] = cur.gq * (acc[vb] + acl[vb]);
             }
+            fetchG(jn, cur);
             {
                 f4v p3[NVB] = {};  // the two lo products in their own chain
 #pragma unroll
@@ -1384,6 +1406,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
             }
+            fetchP(jn, cur);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
             // stage the tile as [token][row]; the next chunk (or the loop's end) stores it
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
@@ -1393,8 +1418,12 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 *reinterpret_cast<typename ActVec<TA>::v4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
             }
         };
-        Ops opa, opb;
-        if (ce > cb) fetch(cb, opa);
+        Ops op;
+        if (ce > cb) {
+            fetchQ(cb, op);
+            fetchG(cb, op);
+            fetchP(cb, op);
+        }
         {
             // a store that writes nothing (empty resource): on entry the loop
             // then sees the same outstanding pattern as in steady state (the
@@ -1403,10 +1432,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, 0x00020000);
             __builtin_amdgcn_raw_buffer_store_b128(u4v{0u, 0u, 0u, 0u}, none, 0, 0, 0);
         }
-        for (int j = cb; j < ce; j += 2) {
-            step(j, opa, opb);
-            if (j + 1 < ce) step(j + 1, opb, opa);
-        }
+        for (int j = cb; j < ce; ++j) step(j, op);
         if (ce > cb) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging has landed
             store_out(ce - 1);
