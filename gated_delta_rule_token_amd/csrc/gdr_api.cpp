@@ -189,10 +189,12 @@ int32_t pick_algo(const gdr_problem *p)
 
 // Segments of the chunked scan's chain: the caller's count, or a split of
 // long requests when few (request, head) pairs leave most CUs idle.  The
-// count aims pass 2 at about 512 workgroups of 16 rows, two per CU (with a
-// power-of-two number of pairs every CU gets the same number; uneven counts
-// leave some CUs a workgroup more than the rest), with at most 16 segments
-// of at least 16 chunks each.  Measured on
+// count gives pass 2 about 64 (request, head, segment) groups -- 256
+// workgroups, one per CU, in 32-row tiles (or 16-row tiles when there are
+// at most 32 groups) -- and pass 1 twice that; with a power-of-two number of
+// pairs every CU gets the same number of workgroups (uneven counts leave
+// some CUs one more than the rest).  At most 16 segments of at least 16
+// chunks each.  Measured on
 // MI355X (prologue + scan, one request): 65,536 tokens x 16 heads 2.0 ms in
 // one pass, 1.68 / 1.81 / 1.55 / 1.94 ms in 3 / 4 / 5 / 6 segments; x 8 heads
 // 1.71 ms, 1.01 / 0.94 ms in 5 / 9; 32,768 tokens x 4 heads 0.70 ms,

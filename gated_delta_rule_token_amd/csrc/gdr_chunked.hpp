@@ -1465,6 +1465,8 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanS
         float acc[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) acc[r] = C[(size_t)(r0 + r) * D128 + c];
+        // unrolled so that many loads of M's rows (from L2) are in flight at once
+#pragma unroll 16
         for (int j = 0; j < D128; ++j) {
             const float m = M[(size_t)j * D128 + c];
 #pragma unroll
