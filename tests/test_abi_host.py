@@ -242,6 +242,27 @@ def test_scan_segments_workspace(lib):
     assert n4.value > n1.value
 
 
+@pytest.mark.parametrize("tokens,heads,nseg", [(65536, 16, 5), (65536, 8, 9), (32768, 4, 9), (65536, 1, 9),
+                                                (16384, 16, 5), (12000, 16, 1), (65536, 32, 1)])
+def test_scan_segments_automatic_choice(lib, tokens, heads, nseg):
+    """The segment count AUTO picks for one long request over few heads,
+    read back from the workspace size (each segment adds three 64 KiB states
+    per (request, head)): pass 2 gets about 64 (request, head, segment)
+    groups, at most 16 segments, none for short requests or many pairs."""
+    p, _ = _good()
+    p.head_dim_k = p.head_dim_v = 128
+    p.act_dtype, p.gate_dtype = api.F16, api.F16
+    p.batch, p.num_heads_qk, p.num_heads_v, p.total_tokens, p.seq_len = 1, heads, heads, tokens, tokens
+    sizes = {}
+    for forced in (0, 1):
+        p.scan_segments = forced
+        n = ctypes.c_size_t(0)
+        assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
+        sizes[forced] = n.value
+    extra = sizes[0] - sizes[1]
+    assert extra == (0 if nseg == 1 else heads * 3 * nseg * 128 * 128 * 4)
+
+
 def test_gate_argument_checks(lib):
     assert lib.gdr_gate(10, 3, 0, _fake(1), _fake(2), _fake(3), None, _fake(4), None, None) \
         == api.GDR_E_INVALID  # 10 not a multiple of 3 heads
