@@ -260,8 +260,8 @@ gdr_status gdr_workspace_size(const gdr_problem *problem, size_t *bytes)
     gdr_status st = check_problem(problem);
     if (st != GDR_OK) return st;
     *bytes = pick_algo(problem) == GDR_ALGO_CHUNKED
-                 ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_v,
-                                                chunked_per_key(problem), scan_segments(problem))
+                 ? gdr::chunked_workspace_bytes(problem->total_tokens, problem->batch, problem->num_heads_qk,
+                                                problem->num_heads_v, chunked_per_key(problem), scan_segments(problem))
                  : 0;
     return GDR_OK;
 }

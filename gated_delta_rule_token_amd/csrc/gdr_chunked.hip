@@ -6,9 +6,9 @@
 
 namespace gdr {
 
-size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg)
+size_t chunked_workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int nseg)
 {
-    return f16::workspace_bytes(T, B, HV, per_key, nseg);
+    return f16::workspace_bytes(T, B, H, HV, per_key, nseg);
 }
 
 // A decay per key channel and the erase gate take the per-key form; other

@@ -74,11 +74,13 @@ constexpr int D128 = 128;       // dk = dv
 // of a wave loads at l * 16, so each wave-wide load reads 1 KB of consecutive
 // bytes (eight whole cache lines).  Per-head decay (PK = false):
 //   W   W (hi, lo) fp16, block (tb * 4 + kk) * 2 + plane: token 16 tb + lr, keys 32 kk + 8 lq .. +7
-//   KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
 //   U   U fp32,          block tb * 8 + rt:              tokens 16 tb + 4 lq .. +3, row 16 rt + lr
-//   Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
 //   P   P (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr, tokens 32 ks + 8 lq .. +7
 //   SC  fp32 scalars: kd[64], gq[64], gamma_C
+// and, once per (chunk, q/k head) -- the same for every value head of the
+// group, written by its first value head (struct KQ):
+//   KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
+//   Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
 // Decay per key channel (PK = true): the per-token weights kd and gq become
 // per-element factors, so two operands carry fp32 values and get two planes:
 //   KT  Kd^T (hi, lo),   block (mt * 2 + ks) * 2 + plane,  Kd = kn o exp(G_C - G)
@@ -88,14 +90,17 @@ template <bool PK>
 struct Rec {
     static constexpr uint32_t W = 0;
     static constexpr uint32_t KT = W + 32 * 1024;
-    static constexpr uint32_t U = KT + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t U = KT + (PK ? 32 : 0) * 1024;
     static constexpr uint32_t Q = U + 32 * 1024;
-    static constexpr uint32_t P = Q + (PK ? 32 : 16) * 1024;
+    static constexpr uint32_t P = Q + (PK ? 32 : 0) * 1024;
     static constexpr uint32_t SC = P + 16 * 1024;
     static constexpr uint32_t SIZE = SC + 1024;
 };
-constexpr uint32_t R_W = Rec<false>::W, R_KT = Rec<false>::KT, R_U = Rec<false>::U, R_Q = Rec<false>::Q,
-                   R_P = Rec<false>::P, R_SC = Rec<false>::SC, WS_REC = Rec<false>::SIZE;
+constexpr uint32_t R_W = Rec<false>::W, R_U = Rec<false>::U, R_P = Rec<false>::P, R_SC = Rec<false>::SC,
+                   WS_REC = Rec<false>::SIZE;
+struct KQ {
+    static constexpr uint32_t KT = 0, Q = 16 * 1024, SIZE = 32 * 1024;
+};
 
 __device__ __forceinline__ f4v mfma16(h8 a, h8 b, f4v c)
 {
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
 template <int RULE>
 __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int32_t *__restrict__ off,
-                                                   char *__restrict__ ws)
+                                                   char *__restrict__ ws, char *__restrict__ kqs)
 {
     constexpr bool DEC = rule_decays(RULE);
     constexpr bool RET = rule_retrieves(RULE);
@@ -248,6 +253,9 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
     char *rec = ws + ((size_t)ci * HV + h) * WS_REC;
+    // K^T and q once per (chunk, q/k head): the group's first value head writes them
+    char *kq = kqs + ((size_t)ci * H + qh) * KQ::SIZE;
+    const bool kq_writer = h % (HV / H) == 0;
 
     const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
     const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
@@ -291,19 +299,20 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
         *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
         *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
         // q in fragment order for the scan's output waves (rows past the end are zero)
-        *reinterpret_cast<h8 *>(rec + R_Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
+        if (kq_writer)
+            *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
     lds_barrier();
 
     // ---- K^T fragments (key 16 mt + lr, tokens 32 ks + 8 lq .. +7); fragment f = block * 64 + lane
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < (kq_writer ? 4 : 0); ++g) {
         const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
         const int key = 16 * (blk >> 1) + (fl & 15), tk = 32 * (blk & 1) + 8 * (fl >> 4);
         h8 col;
 #pragma unroll
         for (int x = 0; x < 8; ++x) col[x] = sK[tk + x][key];
-        *reinterpret_cast<h8 *>(rec + R_KT + (size_t)f * 16) = col;
+        *reinterpret_cast<h8 *>(kq + KQ::KT + (size_t)f * 16) = col;
     }
     // ---- inverse L2 norms of the chunk's q and k rows: 4 threads per row
     {
@@ -1056,7 +1065,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 // runs segments 1 .. nseg-1 for real from those starts.  The longest serial
 // chain shrinks from n chunk steps to about 2 n / nseg.
 template <typename TA, int RULE, int NVB, bool PK>
-__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const ScanSeg sg)
+__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const char *kqs,
+                                                   const ScanSeg sg)
 {
     using RC = Rec<PK>;
     constexpr int NPL = PK ? 2 : 1;       // fp16 planes of the K^T and q operands
@@ -1115,6 +1125,12 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         }
     }
     const int tb = wave & 3;  // token block of this wave (D rows for the chain, O columns for the output)
+    const int qh = (int)(((int64_t)h * p.H) / HV);
+    // per head: K^T and q of chunk jj come from the (chunk, q/k head) area, else from the record
+    auto kq_rsrc = [&](int jj) {
+        if constexpr (PK) return make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+        else return make_rsrc(kqs + ((size_t)(c0 + jj) * p.H + qh) * KQ::SIZE, KQ::SIZE);
+    };
 
     if (wave < 4) {
         // ================================================================ chain
@@ -1145,7 +1161,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             f4v gk[2];          // per key: gamma_C of keys 16 (2 wave + a) + 4 lq .. +3
         };
         const uint32_t offW = RC::W + (uint32_t)tb * 8 * 1024 + l16;
-        const uint32_t offK = RC::KT + (uint32_t)(2 * wave) * 2 * NPL * 1024 + l16;
+        const uint32_t offK = (PK ? RC::KT : KQ::KT) + (uint32_t)(2 * wave) * 2 * NPL * 1024 + l16;
         const uint32_t offU = RC::U + (uint32_t)(tb * 8 + NVB * tile) * 1024 + l16;
         const uint32_t offKd = RC::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
         const uint32_t offGk = RC::SC + (uint32_t)(32 * wave + 4 * lq) * 4;
@@ -1167,12 +1183,13 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         };
         auto fetchE = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+            const __amdgpu_buffer_rsrc_t rk = kq_rsrc(jj);
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl) f.kt[a][ks][pl] = ld_b128<h8>(r, offK + ((2 * a + ks) * NPL + pl) * 1024);
+                    for (int pl = 0; pl < NPL; ++pl) f.kt[a][ks][pl] = ld_b128<h8>(rk, offK + ((2 * a + ks) * NPL + pl) * 1024);
             if constexpr (PK) {
                 f.gk[0] = ld_b128<f4v>(r, offGk);
                 f.gk[1] = ld_b128<f4v>(r, offGk + 64);
@@ -1313,7 +1330,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
             float gq;         // per head: gq of this lane's token
         };
-        const uint32_t offQ = RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16;
+        const uint32_t offQ = (PK ? RC::Q : KQ::Q) + (uint32_t)tb * 4 * NPL * 1024 + l16;
         // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
         const int tok_bytes = HV * D128 * 2;
         // after the LDS transpose each lane stores 16 bytes (8 rows of a token):
@@ -1329,7 +1346,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         // one operand set, each part reloaded for chunk jj right after its last use
         auto fetchQ = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
+            const __amdgpu_buffer_rsrc_t r = kq_rsrc(jj);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -1485,17 +1502,25 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanS
 
 // ------------------------------------------------------------------ host side
 
-static size_t seg_offset(int64_t T, int B, int HV, bool per_key)
+// Workspace: chunk table | records of every (chunk, value head) | per head:
+// K^T and q of every (chunk, q/k head) | segment states
+static size_t kq_offset(int64_t T, int B, int HV, bool per_key)
 {
     const int64_t maxch = (T + CH - 1) / CH + B;
     const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
     return table + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
 }
 
-static size_t workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg)
+static size_t seg_offset(int64_t T, int B, int H, int HV, bool per_key)
+{
+    const int64_t maxch = (T + CH - 1) / CH + B;
+    return kq_offset(T, B, HV, per_key) + (per_key ? 0 : ((size_t)maxch * H * KQ::SIZE + 255) / 256 * 256);
+}
+
+static size_t workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int nseg)
 {
     const size_t segs = nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0;
-    return seg_offset(T, B, HV, per_key) + segs;
+    return seg_offset(T, B, H, HV, per_key) + segs;
 }
 
 // Row tile of the scan: 16 * NVB rows, NVB = 1 or 2 (measured on MI355X:
@@ -1503,12 +1528,13 @@ static size_t workspace_bytes(int64_t T, int B, int HV, bool per_key, int nseg)
 // by 1.7x, which loses on both the single long sequence and the batched
 // prefill).
 template <typename TA, int RULE, int NVB, bool PK>
-static void launch_scan(const Params &p, const int32_t *off, const char *rec, const ScanSeg &sg, hipStream_t s)
+static void launch_scan(const Params &p, const int32_t *off, const char *rec, const char *kq, const ScanSeg &sg,
+                        hipStream_t s)
 {
     constexpr int NTILE = D128 / (16 * NVB);
     const int64_t groups = (int64_t)p.B * p.HV * (sg.pass == 0 ? 1 : sg.nseg - 1);
     const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
-    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, sg);
+    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
 }
 
 // Scan launches.  Few (request, head) pairs leave most CUs idle with 32-row
@@ -1523,22 +1549,23 @@ static void launch_scan(const Params &p, const int32_t *off, const char *rec, co
 // then takes about twice as long (measured on MI355X, 65,536 tokens x 16
 // heads in 3 segments: 1.82 ms with 32-row pass-1 tiles, 1.89 ms with 16-row).
 template <typename TA, int RULE, bool PK>
-static void launch_scans(const Params &p, const int32_t *off, const char *rec, float *xs, int nseg, hipStream_t s)
+static void launch_scans(const Params &p, const int32_t *off, const char *rec, const char *kq, float *xs, int nseg,
+                         hipStream_t s)
 {
     const int64_t pairs = (int64_t)p.B * p.HV;
     if (nseg <= 1) {
         const ScanSeg one{1, 0, nullptr};
-        if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, one, s);
-        else launch_scan<TA, RULE, 2, PK>(p, off, rec, one, s);
+        if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, one, s);
+        else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, one, s);
         return;
     }
-    launch_scan<TA, RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 1, xs}, s);
+    launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs}, s);
     if (nseg > 2) {
         const int64_t blocks = pairs * 8;
         hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, ScanSeg{nseg, 0, xs});
     }
-    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
-    else launch_scan<TA, RULE, 2, PK>(p, off, rec, ScanSeg{nseg, 2, xs}, s);
+    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
+    else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
 }
 
 // PK: the per-key record and kernels; PKG: the gate itself is per key (else
@@ -1552,15 +1579,16 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
     char *base = static_cast<char *>(ws);
     int32_t *off = reinterpret_cast<int32_t *>(base);
     char *rec = base + table;
-    float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.HV, PK));
+    char *kq = base + kq_offset(p.T, p.B, p.HV, PK);
+    float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.H, p.HV, PK));
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
     if (maxch * p.HV > 0) {
         if constexpr (PK)
             hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
         else
-            hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
+            hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec, kq);
     }
-    launch_scans<TA, RULE, PK>(p, off, rec, xs, nseg, s);
+    launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, nseg, s);
     return hipGetLastError();
 }
 

@@ -20,8 +20,8 @@ hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hi
 // gate and every bf16 problem (per_key here: the gate itself is per key).
 // nseg > 1 cuts each request's chain of chunk steps into that many segments
 // (two scan passes and a combine step).  `ws` holds
-// chunked_workspace_bytes(T, B, HV, per-key form, nseg) bytes.
-size_t chunked_workspace_bytes(int64_t T, int B, int HV, bool per_key_form, int nseg);
+// chunked_workspace_bytes(T, B, H, HV, per-key form, nseg) bytes.
+size_t chunked_workspace_bytes(int64_t T, int B, int H, int HV, bool per_key_form, int nseg);
 hipError_t launch_chunked(const Params &p, int rule, bool per_key, int nseg, int act, void *ws, hipStream_t s);
 hipError_t launch_chunked_bf16(const Params &p, int rule, bool per_key, int nseg, void *ws, hipStream_t s);
 
