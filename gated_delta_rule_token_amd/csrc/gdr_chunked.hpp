@@ -876,6 +876,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     // W's right-hand-side fragments wait in LDS (in fragment order: one
     // 16-byte read each later), so no register holds them across the solve
     h8 *sBw = reinterpret_cast<h8 *>(sm + 2 * SLOT);  // [plane][wave][c][ks][lane]
+    static_assert(2 * 4 * 4 * 64 * sizeof(h8) <= CH * LF * 4, "W's right-hand-side fragments fit in G's slot");
     if constexpr (RET) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
