@@ -384,10 +384,14 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
             }
             h4 hi, lo;
             split4(pv, hi, lo);
-            // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane
+            // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane; the
+            // fragments of token blocks 0, 1 against tokens 32 .. 63 are all zero
+            // and are not stored (the scan reads zero past the record instead)
             const uint32_t po = R_P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
-            *reinterpret_cast<h4 *>(rec + po) = hi;
-            *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            if (tb >= 2 || sb < 2) {
+                *reinterpret_cast<h4 *>(rec + po) = hi;
+                *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            }
             if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
         }
     }
@@ -908,18 +912,16 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
         }
     }
-#pragma unroll
-    for (int zi = 0; zi < 2; ++zi) {
-        // the P blocks above the diagonal are zero (the scan multiplies them anyway)
-        constexpr int8_t ZTB[6] = {0, 0, 0, 1, 1, 2};
-        constexpr int8_t ZSB[6] = {1, 2, 3, 2, 3, 3};
-        const int z = wave + 4 * zi;
-        if (z < 6) {
-            const int tb = ZTB[z], sb = ZSB[z], s0 = 16 * sb + 4 * lq;
-            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
-            *reinterpret_cast<h4 *>(rec + po) = h4{};
-            *reinterpret_cast<h4 *>(rec + po + 1024) = h4{};
-        }
+    if (wave < 2) {
+        // the P blocks above the diagonal are zero (the scan multiplies them
+        // anyway); only the two that share a fragment with nonzero blocks are
+        // stored -- (tb, sb) = (0, 1) on wave 0, (2, 3) on wave 1 -- while the
+        // all-zero fragments of token blocks 0, 1 against tokens 32 .. 63 are
+        // read as zero past the record's end
+        const int tb = 2 * wave, sb = 2 * wave + 1, s0 = 16 * sb + 4 * lq;
+        const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+        *reinterpret_cast<h4 *>(rec + po) = h4{};
+        *reinterpret_cast<h4 *>(rec + po + 1024) = h4{};
     }
     lds_barrier();
 
@@ -1344,6 +1346,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const int st_tok = st_live ? lane / LPT : 15, st_q = lane % LPT;
         const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
         const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
+        // token blocks 0, 1 against tokens 32 .. 63: all zero, not stored; an offset
+        // past the record makes the buffer load return zero
+        const uint32_t offP1 = tb < 2 ? 0x7FFFF000u : offP + 2048;
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         // one operand set, each part reloaded for chunk jj right after its last use
         auto fetchQ = [&](int jj, Ops &f) {
@@ -1361,8 +1366,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                f.ph[ks] = ld_b128<h8>(r, offP + ks * 2048);
-                f.pl[ks] = ld_b128<h8>(r, offP + ks * 2048 + 1024);
+                f.ph[ks] = ld_b128<h8>(r, ks ? offP1 : offP);
+                f.pl[ks] = ld_b128<h8>(r, (ks ? offP1 : offP) + 1024);
             }
         };
         // Store the output tile of chunk jo, staged in sO, as one 16-byte write per
