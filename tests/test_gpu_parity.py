@@ -96,6 +96,20 @@ def test_decode_kernel_multi_token_requests():
     _check_full(case, "decode", "decode L=4 slab")
 
 
+@pytest.mark.parametrize("rule,per_key", [("gated_delta", False), ("gated_delta_v2", True)],
+                         ids=["gated_delta_qwen", "gated_delta_v2_pk"])
+def test_decode_kernel_staged_token_blocks(rule, per_key):
+    """The decode kernel forced on varlen requests of 0 to 20 tokens: the
+    token inputs go through LDS in blocks of 8, so requests cross one, two or
+    three blocks, with a ragged last block and an empty request."""
+    kw = dict(gate_activation="none" if per_key else "qwen",
+              beta_activation="none" if per_key else "sigmoid")
+    case = workloads.random_case(zlib.crc32(("stage/" + rule).encode()) % 1000,
+                                 lengths=[1, 8, 9, 0, 16, 20, 5, 17], H=2, HV=4, DK=128, DV=128,
+                                 dtype=np.float16, update_rule=rule, per_key=per_key, **kw)
+    _check_full(case, "decode", "decode staged %s" % rule)
+
+
 # ------------------------------------------------------------------ the five workloads, full size
 def test_decode_workload_full():
     case = workloads.decode_slab()
