@@ -1067,6 +1067,13 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 // M_j).  k_seg_combine then forms start_{p+1} = start_p M_p + c_p, and pass 2
 // runs segments 1 .. nseg-1 for real from those starts.  The longest serial
 // chain shrinks from n chunk steps to about 2 n / nseg.
+// Column index of a swizzled LDS row: the 16-byte chunk (8 fp16) holding
+// column x moves to chunk (x / 8) XOR f(row), with f(row) = row mod 16 for the
+// 128-column state rows and (row / 2) mod 8 for the 64-column delta rows.
+// Only the row's low four bits enter, so rows 16 apart share one pattern.
+__device__ __forceinline__ int sw_key(int row, int key) { return (((key >> 3) ^ (row & 15)) << 3) | (key & 7); }
+__device__ __forceinline__ int sw_tok(int row, int tok) { return (((tok >> 3) ^ ((row >> 1) & 7)) << 3) | (tok & 7); }
+
 template <typename TA, int RULE, int NVB, bool PK>
 __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const char *kqs,
                                                    const ScanSeg sg)
@@ -1076,14 +1083,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     constexpr bool RET = rule_retrieves(RULE);
     constexpr int TR = 16 * NVB;          // state rows of this workgroup
     constexpr int NTILE = D128 / TR;      // workgroups per head
-    constexpr int LS = D128 + 8;  // fp16 state row (272 B)
-    constexpr int LDT = CH + 8;   // fp16 row of the transposed delta (144 B)
-
-    // Row strides of 68 and 36 dwords put the 16 lanes of a 16-byte access
-    // phase on 16 distinct 4-bank groups.
-    __shared__ __align__(16) half_t sS[2][2][TR][LS];    // [buffer][hi, lo][row][key]
-    __shared__ __align__(16) half_t sDt[2][2][TR][LDT];  // [buffer][hi, lo][row][token] D^T
-    __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][LDT];  // [hi, lo][row][token] (kd D)^T, chain only
+    // Unpadded rows with their 16-byte chunks permuted per row (sw_key,
+    // sw_tok), so that the MFMA operand reads (16 bytes per lane: 16 rows x 4
+    // chunks per wave) are free of LDS bank conflicts; measured on gfx950, a
+    // ds_read_b128 pass takes lanes 0-7 with 24-31 (and 8-15 with 16-23), which
+    // padded row strides cannot serve without a 2-way conflict.
+    __shared__ __align__(16) half_t sS[2][2][TR][D128];  // [buffer][hi, lo][row][key]
+    __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token] D^T
+    __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][CH];  // [hi, lo][row][token] (kd D)^T, chain only
     __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
 
     const int HV = p.HV;
@@ -1210,8 +1217,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 for (int rt = 0; rt < NVB; ++rt) {
                     h4 hi, lo;
                     split4(Sc[a][rt], hi, lo);
-                    *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = hi;
-                    *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][16 * (2 * wave + a) + 4 * lq]) = lo;
+                    *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = hi;
+                    *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = lo;
                 }
             lds_barrier();  // 1
             // ---- B: D = U - W S^T for token block tb and every row block (D rows = tokens)
@@ -1226,8 +1233,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                         for (int vb = 0; vb < NVB; ++vb) {
-                            const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
-                            const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                            const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                            const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
                             a2[vb][0] = mfma16(cur.wh[kk], shi, a2[vb][0]);
                             a2[vb][NA - 1] = mfma16(cur.wh[kk], slo, a2[vb][NA - 1]);
                             a2[vb][0] = mfma16(cur.wl[kk], shi, a2[vb][0]);
@@ -1258,13 +1265,13 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 h4 dh, dl;
                 split4(dv[vb], dh, dl);
                 const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
-                *reinterpret_cast<h4 *>(&sDt[bf][0][r][c]) = dh;
-                *reinterpret_cast<h4 *>(&sDt[bf][1][r][c]) = dl;
+                *reinterpret_cast<h4 *>(&sDt[bf][0][r][sw_tok(lr, c)]) = dh;
+                *reinterpret_cast<h4 *>(&sDt[bf][1][r][sw_tok(lr, c)]) = dl;
                 if constexpr (!PK) {
                     h4 sh, sl;
                     split4(dsv[vb], sh, sl);
-                    *reinterpret_cast<h4 *>(&sDs[0][r][c]) = sh;
-                    *reinterpret_cast<h4 *>(&sDs[1][r][c]) = sl;
+                    *reinterpret_cast<h4 *>(&sDs[0][r][sw_tok(lr, c)]) = sh;
+                    *reinterpret_cast<h4 *>(&sDs[1][r][sw_tok(lr, c)]) = sl;
                 }
             }
             lds_barrier();  // 2
@@ -1285,8 +1292,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int rt = 0; rt < NVB; ++rt) {
-                        const h8 dhi = PK ? ld_h8(&sDt[bf][0][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[0][16 * rt + lr][32 * ks + lk]);
-                        const h8 dlo = PK ? ld_h8(&sDt[bf][1][16 * rt + lr][32 * ks + lk]) : ld_h8(&sDs[1][16 * rt + lr][32 * ks + lk]);
+                        const h8 dhi = PK ? ld_h8(&sDt[bf][0][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]) : ld_h8(&sDs[0][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]);
+                        const h8 dlo = PK ? ld_h8(&sDt[bf][1][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]) : ld_h8(&sDs[1][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]);
 #pragma unroll
                         for (int a = 0; a < 2; ++a) {
                             Sc[a][rt] = mfma16(cur.kt[a][ks][0], dhi, Sc[a][rt]);
@@ -1396,8 +1403,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) {
-                    const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][32 * kk + lk]);
-                    const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][32 * kk + lk]);
+                    const h8 shi = ld_h8(&sS[bf][0][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                    const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
                     acc[vb] = mfma16(shi, cur.q[kk][0], acc[vb]);
                     acl[vb] = mfma16(slo, cur.q[kk][0], acl[vb]);
                     if constexpr (PK) acl[vb] = mfma16(shi, cur.q[kk][NPL - 1], acl[vb]);
@@ -1420,8 +1427,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int vb = 0; vb < NVB; ++vb) {
-                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][32 * ks + lk]);
-                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][32 * ks + lk]);
+                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
                         acc[vb] = mfma16(dhi, cur.ph[ks], acc[vb]);
                         p3[vb] = mfma16(dlo, cur.ph[ks], p3[vb]);
                         p3[vb] = mfma16(dhi, cur.pl[ks], p3[vb]);
