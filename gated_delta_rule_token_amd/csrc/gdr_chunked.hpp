@@ -143,6 +143,17 @@ __device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
     }
 }
 
+// Column index of a swizzled LDS row of fp16: the 16-byte chunk (8 values)
+// holding column x moves to chunk (x / 8) XOR f(row), with f(row) = row mod 16
+// for 128-column rows and (row / 2) mod 8 for 64-column rows.  With it, the
+// matrix-core operand reads (16 bytes per lane, 16 rows x 4 chunks per wave)
+// are free of bank conflicts on gfx950, whose ds_read_b128 serves lanes 0-7
+// together with 24-31 (and 8-15 with 16-23), as a counter probe showed;
+// padded row strides leave a 2-way conflict there.  Only the row's low four
+// bits enter, so rows 16 apart share one pattern.
+__device__ __forceinline__ int sw_key(int row, int key) { return (((key >> 3) ^ (row & 15)) << 3) | (key & 7); }
+__device__ __forceinline__ int sw_tok(int row, int tok) { return (((tok >> 3) ^ ((row >> 1) & 7)) << 3) | (tok & 7); }
+
 // Segments of the scan's chain (see k_chunk_scan).  pass 0: one pass over
 // every chunk; pass 1 / 2: the two passes of an nseg-segment scan.  xs holds,
 // per (request, head), seg_slots(nseg) states of 128 x 128 fp32: the start of
@@ -236,7 +247,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
     half_t(*sV)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + SLOT);
     half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + 2 * SLOT);
     float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + 2 * SLOT);
-    half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm);  // [hi, lo][token][key], after the solve
+    half_t(*sW)[CH][D128] = reinterpret_cast<half_t(*)[CH][D128]>(sm);  // [hi, lo][token][key, swizzled], after the solve
     __shared__ float sG[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
 
     const int HV = p.HV, H = p.H;
@@ -470,9 +481,10 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
                 split8(tb8, uh, ul);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    accW[mb][c] = mfma16(th, bwh[c][ks], accW[mb][c]);
-                    accW[mb][c] = mfma16(th, bwl[c][ks], accW[mb][c]);
-                    accW[mb][c] = mfma16(tl, bwh[c][ks], accW[mb][c]);
+                    // W^T = RHS^T T^T: each lane ends with four consecutive keys of one token
+                    accW[mb][c] = mfma16(bwh[c][ks], th, accW[mb][c]);
+                    accW[mb][c] = mfma16(bwl[c][ks], th, accW[mb][c]);
+                    accW[mb][c] = mfma16(bwh[c][ks], tl, accW[mb][c]);
                     accU[mb][c] = mfma16(uh, bv[c][ks], accU[mb][c]);
                     accU[mb][c] = mfma16(ul, bv[c][ks], accU[mb][c]);
                 }
@@ -487,25 +499,24 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
                 *reinterpret_cast<f4v *>(rec + R_U + ((uint32_t)((mb * 8 + 2 * wave + c) * 64 + lane)) * 16) = accU[mb][c];
         lds_barrier();  // every wave holds its K and V fragments: W rows may overwrite them
         // W (hi, lo) rows into LDS over K and V: accumulator (mb, c) holds
-        // tokens 16 mb + 4 lq + i of key 16 (2 wave + c) + lr
+        // keys 16 (2 wave + c) + 4 lq + i of token 16 mb + lr
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float w = accW[mb][c][i];
-                    const half_t hi = (half_t)w;
-                    sW[0][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = hi;
-                    sW[1][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = (half_t)(w - (float)hi);
-                }
+            for (int c = 0; c < 2; ++c) {
+                h4 hi, lo;
+                split4(accW[mb][c], hi, lo);
+                const int key = sw_key(lr, 16 * (2 * wave + c) + 4 * lq);
+                *reinterpret_cast<h4 *>(&sW[0][16 * mb + lr][key]) = hi;
+                *reinterpret_cast<h4 *>(&sW[1][16 * mb + lr][key]) = lo;
+            }
         lds_barrier();
         // W fragments: f = block * 64 + lane, block = (tb * 4 + kk) * 2 + plane
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
             const int tb = blk >> 3, kk = (blk >> 1) & 3, pl = blk & 1;
-            *reinterpret_cast<h8 *>(rec + R_W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][32 * kk + 8 * (fl >> 4)]);
+            *reinterpret_cast<h8 *>(rec + R_W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][sw_key(fl, 32 * kk + 8 * (fl >> 4))]);
         }
     }
 }
@@ -568,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     TA(*sQ)[LD] = reinterpret_cast<TA(*)[LD]>(sm + SLOT);     // Q rows
     float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + SLOT);       // A after the Gram
     float(*sG)[LF] = reinterpret_cast<float(*)[LF]>(sm + 2 * SLOT);   // G log2(e): cumulative log2 decay
-    half_t(*sW)[CH][LD] = reinterpret_cast<half_t(*)[CH][LD]>(sm + SLOT);  // W (hi, lo) after the solve
+    half_t(*sW)[CH][D128] = reinterpret_cast<half_t(*)[CH][D128]>(sm + SLOT);  // W (hi, lo) after the solve, swizzled rows
     __shared__ float sIk[CH], sIq[CH], sWt[CH];
     __shared__ float sTot[2][D128], sPos[2][D128];
     __shared__ int sFlag;
@@ -998,9 +1009,10 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 split8(tw, uh, ul);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    accW[mb][c] = mfma16(th, bwh[c][ks], accW[mb][c]);
-                    accW[mb][c] = mfma16(th, bwl[c][ks], accW[mb][c]);
-                    accW[mb][c] = mfma16(tl, bwh[c][ks], accW[mb][c]);
+                    // W^T = RHS^T T^T: each lane ends with four consecutive keys of one token
+                    accW[mb][c] = mfma16(bwh[c][ks], th, accW[mb][c]);
+                    accW[mb][c] = mfma16(bwl[c][ks], th, accW[mb][c]);
+                    accW[mb][c] = mfma16(bwh[c][ks], tl, accW[mb][c]);
                     accU[mb][c] = mfma16(uh, bvh[c][ks], accU[mb][c]);
                     accU[mb][c] = mfma16(ul, bvh[c][ks], accU[mb][c]);
                     if constexpr (!VX) accU[mb][c] = mfma16(uh, bvl[c][ks], accU[mb][c]);
@@ -1017,20 +1029,19 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float w = accW[mb][c][i];
-                    const half_t hi = (half_t)w;
-                    sW[0][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = hi;
-                    sW[1][16 * mb + 4 * lq + i][16 * (2 * wave + c) + lr] = (half_t)(w - (float)hi);
-                }
+            for (int c = 0; c < 2; ++c) {
+                h4 hi, lo;
+                split4(accW[mb][c], hi, lo);
+                const int key = sw_key(lr, 16 * (2 * wave + c) + 4 * lq);
+                *reinterpret_cast<h4 *>(&sW[0][16 * mb + lr][key]) = hi;
+                *reinterpret_cast<h4 *>(&sW[1][16 * mb + lr][key]) = lo;
+            }
         lds_barrier();
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             const int f = tid + 256 * g, blk = f >> 6, fl = f & 63;
             const int tb = blk >> 3, kk = (blk >> 1) & 3, pl = blk & 1;
-            *reinterpret_cast<h8 *>(rec + RC::W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][32 * kk + 8 * (fl >> 4)]);
+            *reinterpret_cast<h8 *>(rec + RC::W + (size_t)f * 16) = ld_h8(&sW[pl][16 * tb + (fl & 15)][sw_key(fl, 32 * kk + 8 * (fl >> 4))]);
         }
     }
 }
@@ -1067,13 +1078,6 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 // M_j).  k_seg_combine then forms start_{p+1} = start_p M_p + c_p, and pass 2
 // runs segments 1 .. nseg-1 for real from those starts.  The longest serial
 // chain shrinks from n chunk steps to about 2 n / nseg.
-// Column index of a swizzled LDS row: the 16-byte chunk (8 fp16) holding
-// column x moves to chunk (x / 8) XOR f(row), with f(row) = row mod 16 for the
-// 128-column state rows and (row / 2) mod 8 for the 64-column delta rows.
-// Only the row's low four bits enter, so rows 16 apart share one pattern.
-__device__ __forceinline__ int sw_key(int row, int key) { return (((key >> 3) ^ (row & 15)) << 3) | (key & 7); }
-__device__ __forceinline__ int sw_tok(int row, int tok) { return (((tok >> 3) ^ ((row >> 1) & 7)) << 3) | (tok & 7); }
-
 template <typename TA, int RULE, int NVB, bool PK>
 __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const char *kqs,
                                                    const ScanSeg sg)
@@ -1083,11 +1087,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     constexpr bool RET = rule_retrieves(RULE);
     constexpr int TR = 16 * NVB;          // state rows of this workgroup
     constexpr int NTILE = D128 / TR;      // workgroups per head
-    // Unpadded rows with their 16-byte chunks permuted per row (sw_key,
-    // sw_tok), so that the MFMA operand reads (16 bytes per lane: 16 rows x 4
-    // chunks per wave) are free of LDS bank conflicts; measured on gfx950, a
-    // ds_read_b128 pass takes lanes 0-7 with 24-31 (and 8-15 with 16-23), which
-    // padded row strides cannot serve without a 2-way conflict.
+    // unpadded rows, 16-byte chunks swizzled per row (sw_key, sw_tok)
     __shared__ __align__(16) half_t sS[2][2][TR][D128];  // [buffer][hi, lo][row][key]
     __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token] D^T
     __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][CH];  // [hi, lo][row][token] (kd D)^T, chain only
