@@ -186,6 +186,34 @@ def cpu_baseline(case, total_bytes):
                       "fp64 oracle incl. input upcast, %.1f s total" % (reps, elapsed)}
 
 
+def stream_ceiling(reps=20):
+    """What plain streaming kernels reach on this device for the decode step's
+    byte count: PyTorch's own elementwise kernels reading and writing 512 MiB
+    of fp32 (in place, and into a second buffer), median over ``reps``
+    event-timed launches.  A reference for the HBM roofline, not part of the
+    engine."""
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    x = torch.ones(n, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn in (("inplace_mul_512MiB", lambda: x.mul_(1.0000001)),
+                     ("add_out_512MiB", lambda: torch.add(x, 1.0, out=y))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        out[name] = {"ms": ms, "GB/s": 2 * n * 4 / (ms * 1e-3) / 1e9}
+    del x, y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +222,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--decode-algo", default="auto")
     ap.add_argument("--prefill-algo", default="auto")
-    ap.add_argument("--only", choices=["decode", "mtp", "prefill", "varlen", "long", "perkey", "bf16"], default=None)
+    ap.add_argument("--only", choices=["decode", "mtp", "prefill", "varlen", "long", "perkey", "bf16", "ceiling"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB -> 256 MiB device copy three times, as the "
@@ -258,6 +287,8 @@ def main():
     if args.only in (None, "prefill", "bf16"):
         # the varlen workload with bf16 activations (beyond the pages' type list)
         result["prefill_bf16"] = bench_prefill(args, "varlen_bf16")
+    if args.only == "ceiling":
+        result["stream_ceiling"] = stream_ceiling()
     print(json.dumps(result), flush=True)
 
 
