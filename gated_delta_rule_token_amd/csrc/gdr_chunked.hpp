@@ -120,6 +120,17 @@ __device__ __forceinline__ void split8(const float (&x)[8], h8 &hi, h8 &lo)
 
 __device__ __forceinline__ h8 ld_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
 
+// 16x16x32 matrix product of 16-bit activations with fp32 accumulation (the
+// products of two fp16 or two bf16 values are exact in fp32)
+__device__ __forceinline__ f4v mfma16x32(ActVec<half_t>::v8 a, ActVec<half_t>::v8 b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4v mfma16x32(ActVec<bf16_t>::v8 a, ActVec<bf16_t>::v8 b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Raw buffer resource over one workspace record of `bytes` bytes (an offset
 // past it reads zero instead of faulting).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *rec, uint32_t bytes)
@@ -789,24 +800,35 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 // one decay for every key channel: exp(G_t - G_s) leaves the key sum
                 // as a scalar, so the products carry no exponentials and the factor
                 // (<= 1 for s <= t when the head decays) is applied per element after
-                f4v eb[8];
-                if constexpr (V2) {
+                f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!V2) {
+                    // plain products of the stored 16-bit values, exact in fp32: the
+                    // 16x16x32 matrix op takes 8 keys per lane and step (lane (lr, lq):
+                    // keys 32 kk + 8 lq .. +7), same accumulator layout
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int key = 32 * kk + 8 * lq;
+                        const a8 ks8 = *reinterpret_cast<const a8 *>(&sK[sr][key]);
+                        if constexpr (RET) accA = mfma16x32(ks8, *reinterpret_cast<const a8 *>(&sK[t][key]), accA);
+                        accP = mfma16x32(ks8, *reinterpret_cast<const a8 *>(&sQ[t][key]), accP);
+                    }
+                } else {
+                    // b o k is not a 16-bit value: fp32 products, 4 keys per step
+                    f4v eb[8];
 #pragma unroll
                     for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
-                }
-                f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kq = 0; kq < 8; ++kq) {
-                    const int key = 32 * lq + 4 * kq;
-                    const a4 kt = *reinterpret_cast<const a4 *>(&sK[t][key]);
-                    const a4 ks = *reinterpret_cast<const a4 *>(&sK[sr][key]);
-                    const a4 qt = *reinterpret_cast<const a4 *>(&sQ[t][key]);
+                    for (int kq = 0; kq < 8; ++kq) {
+                        const int key = 32 * lq + 4 * kq;
+                        const a4 kt = *reinterpret_cast<const a4 *>(&sK[t][key]);
+                        const a4 ks = *reinterpret_cast<const a4 *>(&sK[sr][key]);
+                        const a4 qt = *reinterpret_cast<const a4 *>(&sQ[t][key]);
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const float right = to_f32(ks[x]);
-                        if constexpr (RET)
-                            accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, (V2 ? eb[kq][x] : 1.f) * to_f32(kt[x]), accA, 0, 0, 0);
-                        accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, to_f32(qt[x]), accP, 0, 0, 0);
+                        for (int x = 0; x < 4; ++x) {
+                            const float right = to_f32(ks[x]);
+                            accA = __builtin_amdgcn_mfma_f32_16x16x4f32(right, eb[kq][x] * to_f32(kt[x]), accA, 0, 0, 0);
+                            accP = __builtin_amdgcn_mfma_f32_16x16x4f32(right, to_f32(qt[x]), accP, 0, 0, 0);
+                        }
                     }
                 }
 #pragma unroll
