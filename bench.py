@@ -117,14 +117,15 @@ def bench_decode(args, L=1):
                   gate_activation="qwen", beta_activation="sigmoid", algo=args.decode_algo)
     q, k, v = _t(case["q"]), _t(case["k"]), _t(case["v"])
     calls = [api.prepare(q, k, v, slot_ids=_t(ids), **common) for ids in (ids_a, ids_b)]
-    wall, kms = time_calls(calls, args.steps if L == 1 else max(20, args.steps // 4), args.warmup)
+    steps = args.steps if L == 1 else max(20, args.steps // 4)
+    wall, kms = time_calls(calls, steps, args.warmup)
     total_b, state_b = decode_bytes(B, H, HV, dk, dv, L)
     digest = source_digest(DECODE_SOURCES)
     traffic = committed_traffic(digest)
     achieved = total_b / (kms * 1e-3) / 1e9
     return case, {
         "wall_s": wall, "kernel_ms": kms, "bytes_per_step": total_b, "state_bytes": state_b,
-        "gbs_wall": total_b * args.steps / wall / 1e9, "gbs_kernel": achieved,
+        "gbs_wall": total_b * steps / wall / 1e9, "gbs_kernel": achieved,
         "algo": calls[0].algo, "tokens": B * L, "traffic": traffic, "digest": digest,
     }
 

@@ -204,6 +204,43 @@ def test_slots_equal_gather_scatter(algo):
     assert np.array_equal(slab[rest], case["slab"][rest].astype(np.float64))
 
 
+@pytest.mark.parametrize("tokens", [1, 3])
+def test_decode_step_replays_in_a_hip_graph(tokens):
+    """A decode step on a slot slab (updated in place), captured once in a HIP
+    graph the way a serving loop would, and replayed: after every replay the
+    output and the slab equal the same step run eagerly on a second copy, with
+    eager work and synchronisations between the replays."""
+    import torch
+    from gated_delta_rule_token_amd import api
+    case = _small(41 + tokens, rank4_batch=(6, tokens), slots=(11,))
+    d = to_dev(case)
+    common = dict(gate=d["gate"], beta=d["beta"], a_log=d["a_log"], dt_bias=d["dt_bias"],
+                  slot_ids=d["slot_ids"], update_rule=case["update_rule"],
+                  gate_activation=case["gate_activation"], beta_activation=case["beta_activation"],
+                  qk_l2_norm=case["qk_l2_norm"], scale=case["scale"], algo="decode")
+    slab_e, slab_g = d["slab"].clone(), d["slab"].clone()
+    eager = api.prepare(d["q"], d["k"], d["v"], state=slab_e, **common)
+    graphed = api.prepare(d["q"], d["k"], d["v"], state=slab_g, **common)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run()
+    torch.cuda.synchronize()
+    assert torch.equal(slab_g, d["slab"]), "capture must not run the step"
+    for i in range(4):
+        eager.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(graphed.o, eager.o), "replay %d: o differs from the eager step" % i
+        assert torch.equal(slab_g, slab_e), "replay %d: slab differs from the eager step" % i
+        if i == 0:
+            # one step from the input slab: the fp64 oracle's step
+            ro, rs = oracle_forward(case)
+            assert_close(graphed.o.double().cpu().numpy(), ro, TOL_F16, "graph replay o")
+            assert_close(slab_g.double().cpu().numpy(), rs, TOL_F16, "graph replay slab")
+
+
 def test_out_of_range_slot_is_skipped():
     case = _small(22, rank4_batch=(4, 3), slots=(9,))
     case["slot_ids"] = np.array([2, 9, -1, 5], dtype=np.int32)
