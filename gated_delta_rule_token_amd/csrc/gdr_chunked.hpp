@@ -594,6 +594,9 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     __shared__ float sIk[CH], sIq[CH], sWt[CH];
     __shared__ float sTot[2][D128], sPos[2][D128];
     __shared__ int sFlag;
+    // one decay for every key channel: per-token cumulative log2 decay G_t and
+    // the factors 2^(G_C - G_t), 2^(G_t)
+    __shared__ float sGt[PKG ? 1 : CH], sFk[PKG ? 1 : CH], sFq[PKG ? 1 : CH];
 
     const int HV = p.HV, H = p.H;
     int64_t ci;
@@ -632,24 +635,35 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             ldv[i] = *reinterpret_cast<const a8 *>(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
         }
     }
+    if constexpr (PKG) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
-        ldg[i] = f4v{0.f, 0.f, 0.f, 0.f};
-        if (r < n) {
-            const size_t th = (size_t)(t0 + r) * HV + h;
-            if constexpr (PKG) {
+        for (int i = 0; i < 8; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+            ldg[i] = f4v{0.f, 0.f, 0.f, 0.f};
+            if (r < n) {
+                const size_t th = (size_t)(t0 + r) * HV + h;
                 if (p.gate_dt == 0 && !p.gate_qwen) {
                     ldg[i] = *reinterpret_cast<const f4v *>(static_cast<const float *>(p.gate) + th * D128 + c4);
                 } else {
 #pragma unroll
                     for (int x = 0; x < 4; ++x) ldg[i][x] = log_decay_key(p, th, h, c4 + x);
                 }
-            } else {
-                const float g = DEC ? log_decay(p, th, h) : 0.f;
-                ldg[i] = f4v{g, g, g, g};
             }
         }
+    } else if (tid < CH) {
+        // one value per token: a 64-lane inclusive scan, then log2 units
+        float g = 0.f;
+        if (DEC && tid < n) g = log_decay(p, (size_t)(t0 + tid) * HV + h, h);
+#pragma unroll
+        for (int o = 1; o < CH; o <<= 1) {
+            const float y = __shfl_up(g, o, CH);
+            if (tid >= o) g += y;
+        }
+        g *= LOG2E;
+        const float gc = __shfl(g, CH - 1, CH);
+        sGt[tid] = g;
+        sFk[tid] = tid < n ? ex2(gc - g) : 0.f;
+        sFq[tid] = ex2(g);
     }
     if (tid < CH) {
         const int t = tid;
@@ -664,10 +678,12 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         *reinterpret_cast<a8 *>(&sK[r][c8]) = ldk[i];
         *reinterpret_cast<a8 *>(&sQ[r][c8]) = ldq[i];
     }
+    if constexpr (PKG) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
-        *reinterpret_cast<f4v *>(&sG[r][c4]) = ldg[i];
+        for (int i = 0; i < 8; ++i) {
+            const int idx = tid + 256 * i, r = idx >> 5, c4 = (idx & 31) * 4;
+            *reinterpret_cast<f4v *>(&sG[r][c4]) = ldg[i];
+        }
     }
     lds_barrier();
 
@@ -675,7 +691,12 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     // 32 hf .. 32 hf + 31 (bands 2 hf, 2 hf + 1), then adds the first half's total.
     // Guard sums: the decay inside each band (past its first token) bounds the
     // diagonal split factor; the total growth of the chunk bounds every other.
-    {
+    if constexpr (!PKG) {
+        // the per-token values across the row (log2 units already)
+        const int hf = tid >> 7;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) sG[32 * hf + r][col] = sGt[32 * hf + r];
+    } else {
         const int hf = tid >> 7;
         float run = 0.f, pos = 0.f, neg[2] = {0.f, 0.f};
 #pragma unroll
@@ -722,7 +743,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     }
     lds_barrier();
     // second half adds the first half's total; both convert to log2 units
-    if (tid >= D128) {
+    if constexpr (!PKG) {
+    } else if (tid >= D128) {
         const float add = sTot[0][col];
 #pragma unroll
         for (int r = 32; r < CH; ++r) sG[r][col] = (sG[r][col] + add) * LOG2E;
@@ -743,7 +765,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
             const int u = 32 * ks + 8 * l4 + x;
-            x8[x] = (float)sK[u][j] * sIk[u] * ex2(gc - sG[u][j]);
+            x8[x] = (float)sK[u][j] * sIk[u] * (PKG ? ex2(gc - sG[u][j]) : sFk[u]);
         }
         h8 hi, lo;
         split8(x8, hi, lo);
@@ -759,7 +781,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         const a8 qq = *reinterpret_cast<const a8 *>(&sQ[t][key]);
         float x8[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * ex2(sG[t][key + x]);
+        for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * (PKG ? ex2(sG[t][key + x]) : sFq[t]);
         h8 hi, lo;
         split8(x8, hi, lo);
         char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
@@ -898,7 +920,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const int u = s0 + x;
-                    xw[x] = (V2 ? ev[c][ks][x] : sWt[u]) * sIk[u] * to_f32(sK[u][j]) * ex2(sG[u][j]);
+                    xw[x] = (V2 ? ev[c][ks][x] : sWt[u]) * sIk[u] * to_f32(sK[u][j]) * (PKG ? ex2(sG[u][j]) : sFq[u]);
                 }
                 split8(xw, bwh[c][ks], bwl[c][ks]);
             }
