@@ -742,16 +742,18 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         }
     }
     lds_barrier();
-    // second half adds the first half's total; both convert to log2 units
-    if constexpr (!PKG) {
-    } else if (tid >= D128) {
-        const float add = sTot[0][col];
+    // per key: the second half adds the first half's total; both convert to
+    // log2 units (a per-token decay is final already)
+    if constexpr (PKG) {
+        if (tid >= D128) {
+            const float add = sTot[0][col];
 #pragma unroll
-        for (int r = 32; r < CH; ++r) sG[r][col] = (sG[r][col] + add) * LOG2E;
-    } else {
+            for (int r = 32; r < CH; ++r) sG[r][col] = (sG[r][col] + add) * LOG2E;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 32; ++r) sG[r][col] *= LOG2E;
-        if (sPos[0][col] + sPos[1][col] > DIAG_NATS) atomicOr(&sFlag, 16);
+            for (int r = 0; r < 32; ++r) sG[r][col] *= LOG2E;
+            if (sPos[0][col] + sPos[1][col] > DIAG_NATS) atomicOr(&sFlag, 16);
+        }
     }
     lds_barrier();
 
