@@ -266,6 +266,12 @@ def main():
             "roofline": {"bound": "hbm", "achieved": d["gbs_kernel"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": pct, "traffic": d["traffic"]},
         })
+        # the practical reference on this device: plain elementwise kernels that
+        # read and write the step's byte count (not part of the timed region)
+        ceil = stream_ceiling()
+        best = max(x["GB/s"] for x in ceil.values())
+        result["decode"]["stream_ceiling_gbs"] = best
+        result["decode"]["frac_of_stream_ceiling"] = d["gbs_kernel"] / best
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
         del case
