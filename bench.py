@@ -15,12 +15,18 @@ Also reported: prefill tokens/s on the varlen workload (8 requests of
 512..8192 tokens, H=16, HV=32, dk=dv=128, fp16, raw-gate arm, qk L2-norm,
 fp32 initial/final states), on one 65,536-token sequence (H=HV=16), on
 the per-key-decay / erase-gate workload (4 x 4096 tokens, H=8, HV=32) and on
-the varlen workload with bf16 activations, each with its algorithmic flop
-rate against the fp32 vector peak, and the fp64 CPU oracle timed on the host
-cores on the decode step (``cpu_baseline``).
+the varlen workload with bf16 activations, each with its HBM roofline
+(algorithmic bytes of the call against 8 TB/s, with the counter-measured
+bytes when the committed counter summary matches the kernel source), the
+executed matrix-core rate when known, the recurrence-equivalent flop rate
+against the fp32 vector peak, and the fp64 CPU oracle timed on a bounded
+sample of the same workload; the decode step's own oracle baseline is the
+line's ``cpu_baseline``.
 
-Per-kernel durations come from HIP events recorded on the stream the kernels
-run on (torch's current stream), around every timed launch.
+``value`` is the wall-clock rate over exactly ``steps`` launches between two
+device synchronisations; per-launch durations come from HIP events recorded
+on the stream the kernels run on (torch's current stream), around each of as
+many launches again after that region.
 """
 from __future__ import annotations
 
@@ -64,42 +70,73 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-DECODE_SOURCES = ["gated_delta_rule_token_amd/csrc/gdr_decode.hip",
-                  "gated_delta_rule_token_amd/csrc/gdr_device.hpp"]
+CSRC = "gated_delta_rule_token_amd/csrc/"
+DECODE_SOURCES = [CSRC + f for f in ("gdr_decode.hip", "gdr_device.hpp", "gdr_chunk_plan.hpp")]
+CHUNKED_SOURCES = [CSRC + f for f in ("gdr_chunked.hpp", "gdr_chunked.hip", "gdr_chunked_bf16.hip",
+                                      "gdr_recurrent.hip", "gdr_device.hpp", "gdr_chunk_plan.hpp")]
+
+
+def committed_counters(summary, digest, workload=None):
+    """Per-launch figures from a committed rocprofv3 counter summary: the
+    ``key: value`` lines of the block whose ``kernel_source_digest`` matches
+    (and, for a summary that covers several workloads, whose ``workload``
+    matches).  None when the summary is missing or was taken on other source."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    blocks = re.split(r"\n(?=kernel_source_digest:)", open(path).read())
+    for blk in blocks:
+        vals = dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", blk, re.M))
+        if vals.get("kernel_source_digest") != digest:
+            continue
+        if workload is not None and vals.get("workload") != workload:
+            continue
+        return vals
+    return None
 
 
 def committed_traffic(digest):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None when that summary is missing or was taken on other kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_hbm_counters.md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_d or not m_b or m_d.group(1) != digest:
-        return None
-    return float(m_b.group(1))
+    vals = committed_counters("decode_hbm_counters.md", digest)
+    return None if vals is None or "hbm_bytes_per_launch" not in vals else float(vals["hbm_bytes_per_launch"])
 
 
-def time_calls(calls, steps, warmup):
-    """Run ``calls`` round-robin: warmup untimed, then exactly ``steps`` timed
-    launches with an event pair around each.  Returns (wall_s, mean_kernel_ms)."""
+def time_wall(calls, steps, warmup):
+    """Run ``calls`` round-robin: ``warmup`` untimed launches, then exactly
+    ``steps`` launches bracketed by a device synchronisation on both sides
+    (nothing else in the timed region).  Returns the wall seconds."""
     import torch
     for i in range(warmup):
         calls[i % len(calls)].run()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
+        calls[i % len(calls)].run()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_events(calls, reps):
+    """Mean duration in ms of one launch, from a HIP event pair recorded on the
+    launch's own stream (torch's current stream) around each of ``reps``
+    launches, after the wall-clock region."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
         ev[i][0].record()
         calls[i % len(calls)].run()
         ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    return wall, kms
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_calls(calls, steps, warmup):
+    """Wall seconds over exactly ``steps`` launches, then the mean event-timed
+    launch duration in ms over as many launches again."""
+    wall = time_wall(calls, steps, warmup)
+    return wall, time_events(calls, steps)
 
 
 def bench_decode(args, L=1):
@@ -130,15 +167,44 @@ def bench_decode(args, L=1):
     }
 
 
+PREFILL_CASES = {
+    "varlen": lambda w: w.varlen_prefill(),
+    "long": lambda w: w.long_prefill(),
+    "perkey": lambda w: w.perkey_erase(),
+    "varlen_bf16": lambda w: w.as_bf16(w.varlen_prefill()),
+}
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix, published
+MFMA_16X16X32_FLOPS = 2 * 16 * 16 * 32
+
+
+def prefill_bytes(case):
+    """Algorithmic HBM bytes of one prefill call: q, k, v, o, the gate, beta
+    and erase rows once, the incoming state read once (when given) and the
+    final state written once."""
+    q, v = case["q"], case["v"]
+    T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
+    H, dk, HV, dv = q.shape[-2], q.shape[-1], v.shape[-2], v.shape[-1]
+    act = 2 if case["act_dtype"] in ("f16", "bf16") else 4
+    n = T * (2 * H * dk + 2 * HV * dv) * act
+    for key in ("gate", "beta", "erase"):
+        x = case.get(key)
+        if x is not None:
+            n += x.size * (act if key == "gate" and case["gate_activation"] == "qwen" else 4)
+    B = len(case["cu_seqlens"]) - 1 if case["cu_seqlens"] is not None else q.shape[0]
+    state = B * HV * dv * dk * 4
+    return n + state * (2 if case["initial_state"] is not None else 1)
+
+
 def bench_prefill(args, which):
-    """Prefill throughput on the varlen workload (8 requests, cu_seqlens, qk
-    L2-norm, raw gate, random initial states) or the long single sequence
-    (65,536 tokens, H=HV=16, log decay and update rate given directly)."""
+    """Prefill throughput on one workload: the varlen batch (8 requests,
+    cu_seqlens, qk L2-norm, raw gate, random initial states), the long single
+    sequence (65,536 tokens, H=HV=16), the per-key decay / erase-gate batch
+    (4 x 4,096 tokens) or the varlen batch in bf16.  One call is the whole hot
+    path (chunk table, prologue and scan kernels, and the recurrent kernel for
+    pairs the chunked form hands over)."""
     import torch
     from gated_delta_rule_token_amd import api, workloads
-    case = {"varlen": workloads.varlen_prefill, "long": workloads.long_prefill,
-            "perkey": workloads.perkey_erase,
-            "varlen_bf16": lambda: workloads.as_bf16(workloads.varlen_prefill())}[which]()
+    case = PREFILL_CASES[which](workloads)
     q, k, v = case["q"], case["k"], case["v"]
     T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
     dk, HV, dv = q.shape[-1], v.shape[-2], v.shape[-1]
@@ -153,16 +219,50 @@ def bench_prefill(args, which):
                        algo=args.prefill_algo)
     steps = max(1, args.prefill_steps)
     wall, kms = time_calls([call], steps, max(1, args.warmup // 2))
+    nbytes = prefill_bytes(case)
+    gbs = nbytes / (kms * 1e-3) / 1e9
     flops = 7.0 * dk * dv * HV * T  # decay, two dot products, rank-1 write per state element
     tflops = flops / (kms * 1e-3) / 1e12
+    digest = source_digest(CHUNKED_SOURCES)
+    counters = committed_counters("prefill_hbm_counters.md", digest, case["name"]) if call.algo == "chunked" else None
+    traffic = float(counters["hbm_bytes_per_call"]) if counters and "hbm_bytes_per_call" in counters else None
     out = {
         "workload": case["name"], "tokens": int(T), "algo": call.algo, "steps": steps,
         "ms_per_call": kms, "tokens_per_s": T / (kms * 1e-3), "tokens_per_s_wall": T * steps / wall,
-        "algorithmic_tflops": tflops, "frac_of_fp32_vector_peak": tflops / FP32_VECTOR_PEAK_TFLOPS,
+        # the HBM roofline of the whole call: its algorithmic bytes at 8 TB/s
+        # take longer than its executed matrix-core flops at 2.5 PFLOP/s
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "scope": "whole call"},
+        # the method's own count (7 dk dv flops per token and value head)
+        # against the fp32 vector peak: a reference figure, not the kernels' unit
+        "recurrence_equivalent": {"tflops": tflops, "frac_of_fp32_vector_peak": tflops / FP32_VECTOR_PEAK_TFLOPS},
+        "kernel_source_digest": digest,
     }
+    if counters and "mfma_16x16x32_per_call" in counters:
+        mf = float(counters["mfma_16x16x32_per_call"]) * MFMA_16X16X32_FLOPS / (kms * 1e-3) / 1e12
+        out["mfma"] = {"executed_tflops": mf, "peak": MFMA_F16_PEAK_TFLOPS, "frac": mf / MFMA_F16_PEAK_TFLOPS}
     if case["cu_seqlens"] is not None:
         out["lengths"] = np.diff(case["cu_seqlens"]).tolist()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = prefill_cpu_baseline(case)
     return out
+
+
+def prefill_cpu_baseline(case):
+    """The fp64 oracle on the whole workload (every request and value head),
+    once, on the host cores, in tokens/s."""
+    import oracle
+    from tests.gpu_helpers import oracle_forward
+    oracle.build()
+    q = case["q"]
+    T = q.shape[0] * (q.shape[1] if q.ndim == 4 else 1)
+    t0 = time.perf_counter()
+    oracle_forward(case)
+    elapsed = time.perf_counter() - t0
+    return {"value": T / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the whole workload (%d tokens, every request and value head) once, fp64 oracle "
+                      "incl. input upcast, %.1f s" % (T, elapsed)}
 
 
 def cpu_baseline(case, total_bytes):
@@ -249,6 +349,9 @@ def main():
     if args.only in (None, "decode"):
         case, d = bench_decode(args)
         pct = d["gbs_kernel"] / HBM_PEAK_GBS
+        # value: bytes of exactly `steps` launches over the wall time between two
+        # device synchronisations (launch gaps included); roofline.achieved: the
+        # same bytes over the mean event-timed duration of one launch
         result.update({
             "value": d["gbs_wall"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": d["wall_s"] * 1e3 / args.steps,
@@ -260,7 +363,10 @@ def main():
                        "update_rule": "gated_delta", "gate": "qwen raw gate + sigmoid beta",
                        "kernel": d["algo"]},
             "decode": {"kernel_ms": d["kernel_ms"], "gbs_kernel": d["gbs_kernel"],
-                       "pct_of_8tbs": 100 * pct, "tokens_per_s": d["tokens"] / (d["kernel_ms"] * 1e-3),
+                       "pct_of_8tbs": 100 * pct, "gbs_wall": d["gbs_wall"],
+                       "pct_of_8tbs_wall": 100 * d["gbs_wall"] / HBM_PEAK_GBS,
+                       "ms_per_step_wall": d["wall_s"] * 1e3 / args.steps,
+                       "tokens_per_s": d["tokens"] / (d["kernel_ms"] * 1e-3),
                        "bytes_per_step": d["bytes_per_step"], "state_bytes_per_step": d["state_bytes"],
                        "kernel_source_digest": d["digest"]},
             "roofline": {"bound": "hbm", "achieved": d["gbs_kernel"], "peak": HBM_PEAK_GBS,

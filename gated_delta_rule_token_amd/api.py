@@ -189,6 +189,48 @@ def build_problem(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_b
     return p
 
 
+def check_shapes(p: Problem, lead, shapes) -> None:
+    """Shape check of every tensor of a call against the problem (shapes only,
+    no device access).  ``lead`` is q's leading axes ((T,) or (B, L));
+    ``shapes`` maps a tensor name to its shape, or None when it is absent.
+    Raises GDRError(GDR_E_INVALID) on the first mismatch."""
+    lead = tuple(lead)
+    H, HV, dk, dv, B = p.num_heads_qk, p.num_heads_v, p.head_dim_k, p.head_dim_v, p.batch
+    state = (HV, dv, dk)
+    want = {
+        "q": [lead + (H, dk)],
+        "k": [lead + (H, dk)],
+        "v": [lead + (HV, dv)],
+        "out": [lead + (HV, dv)],
+        "gate": [lead + (HV, dk)] if p.decay_per_key else [lead + (HV,)],
+        "beta": [lead + (HV,), lead + (1,)],
+        "erase": [lead + (HV, dk)],
+        "a_log": [(HV,)],
+        "gate_scale": [(HV,)],
+        "dt_bias": [(HV, dk)] if p.decay_per_key else [(HV,)],
+        "cu_seqlens": [(B + 1,)],
+        "seq_lens": [(B,)],
+        "slot_ids": [(B,)],
+        "initial_state": [(B,) + state],
+        "final_state": [(B,) + state],
+        "state": [(p.num_slots,) + state],
+    }
+    for name, shape in shapes.items():
+        if shape is None:
+            continue
+        shape = tuple(shape)
+        ok = want.get(name)
+        if ok is None:
+            raise GDRError("GDR_E_INVALID", "unknown tensor %s" % name)
+        if shape not in ok:
+            raise GDRError("GDR_E_INVALID", "%s has shape %s, expected %s" % (
+                name, shape, " or ".join(str(w) for w in ok)))
+
+
+def _shapes(**tensors):
+    return {k: (None if t is None else tuple(t.shape)) for k, t in tensors.items()}
+
+
 def workspace_size(problem: Problem) -> int:
     n = ctypes.c_size_t(0)
     check(load_library().gdr_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
@@ -263,17 +305,26 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
         fin = _need(final_state, "final_state", torch.float32, dev)
     else:
         fin = torch.empty((p.batch, HV, dv, dk), dtype=torch.float32, device=dev)
+    check_shapes(p, lead, _shapes(q=q, k=k, v=v, out=out, gate=gate, beta=beta, erase=erase,
+                                  a_log=a_log, gate_scale=gate_scale, dt_bias=dt_bias,
+                                  cu_seqlens=cu_seqlens, seq_lens=seq_lens, slot_ids=slot_ids,
+                                  initial_state=initial_state,
+                                  final_state=None if state is not None else fin, state=state))
     ws_bytes = workspace_size(p)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = 0
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+        ws_have = workspace.numel() * workspace.element_size()
     t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(gate), beta=_ptr(beta),
                 erase=_ptr(erase), a_log=_ptr(a_log), dt_bias=_ptr(dt_bias),
                 cu_seqlens=_ptr(cu_seqlens), slot_ids=_ptr(slot_ids),
                 initial_state=_ptr(initial_state), final_state=_ptr(fin),
                 gate_scale=_ptr(gate_scale), seq_lens=_ptr(seq_lens))
     stream = torch.cuda.current_stream(dev).cuda_stream
-    check(lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), _ptr(workspace),
-                          ws_bytes if workspace is not None else 0, stream))
+    # the library checks the real size against what the problem needs
+    check(lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), _ptr(workspace), ws_have, stream))
     return out, fin
 
 
@@ -323,10 +374,16 @@ class Prepared:
             fin = kw.get("final_state")
         if fin is None:
             fin = torch.empty((p.batch, HV, dv, dk), dtype=torch.float32, device=dev)
+        g = kw.get
+        check_shapes(p, tuple(q.shape[:-2]), _shapes(
+            q=q, k=k, v=v, out=out, gate=g("gate"), beta=g("beta"), erase=g("erase"),
+            a_log=g("a_log"), gate_scale=g("gate_scale"), dt_bias=g("dt_bias"),
+            cu_seqlens=g("cu_seqlens"), seq_lens=g("seq_lens"), slot_ids=g("slot_ids"),
+            initial_state=g("initial_state"),
+            final_state=None if g("state") is not None else fin, state=g("state")))
         ws = workspace_size(p)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
         self.tensors = dict(kw, q=q, k=k, v=v, out=out, fin=fin)
-        g = kw.get
         self.t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(g("gate")),
                          beta=_ptr(g("beta")), erase=_ptr(g("erase")), a_log=_ptr(g("a_log")),
                          dt_bias=_ptr(g("dt_bias")), cu_seqlens=_ptr(g("cu_seqlens")),

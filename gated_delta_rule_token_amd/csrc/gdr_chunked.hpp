@@ -34,6 +34,8 @@
 // tiles of a head are dispatched to the same XCD so their identical
 // per-chunk reads are shared through its L2.
 
+#include <type_traits>
+
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -165,6 +167,43 @@ __device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
 __device__ __forceinline__ int sw_key(int row, int key) { return (((key >> 3) ^ (row & 15)) << 3) | (key & 7); }
 __device__ __forceinline__ int sw_tok(int row, int tok) { return (((tok >> 3) ^ ((row >> 1) & 7)) << 3) | (tok & 7); }
 
+// Magnitude of the split operands.  The recurrence is linear in (initial
+// state, v) for fixed keys, gates and update rates, so the scan may run a
+// state tile multiplied by 2^e and divide o and the final state by 2^e: a
+// power of two changes no digit.  e brings the larger of max |v| of the
+// (request, head) and max |S0| of the tile into [4, 8), where the fp16
+// (hi, lo) pairs of the state and the value updates keep ~22 bits: about
+// 2^13 of headroom above it for state growth, and entries far below it keep
+// an absolute error near 2^-25 of that maximum instead of turning into fp16
+// subnormals (inputs of size 1e-5 lost most of their digits unscaled).  Each
+// scan unit takes max |v| over its own chunks (post_vmax) and max |S0| over
+// its own tile, so units need not agree.
+__device__ __forceinline__ int tile_exponent(float m)
+{
+    if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;  // zero, or not finite
+    int e;
+    frexpf(m, &e);  // m in [2^(e-1), 2^e)
+    const int x = 3 - e;
+    return x < -100 ? -100 : (x > 100 ? 100 : x);
+}
+
+// Largest |v| of a prologue wave's chunk rows (4 vectors of 8 per thread),
+// stored as one float per wave at SC[252 + wave] of the chunk record, where
+// the scan reads it back.
+constexpr int SC_VMAX = 252;
+template <typename V8>
+__device__ __forceinline__ void post_vmax(const V8 (&x)[4], char *rec_sc)
+{
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(to_f32(x[i][e])));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) reinterpret_cast<float *>(rec_sc)[SC_VMAX + (threadIdx.x >> 6)] = m;
+}
+
 // Segments of the scan's chain (see k_chunk_scan).  pass 0: one pass over
 // every chunk; pass 1 / 2: the two passes of an nseg-segment scan.  xs holds,
 // per (request, head), seg_slots(nseg) states of 128 x 128 fp32: the start of
@@ -206,37 +245,55 @@ __device__ __forceinline__ void prep_block(int HV, int64_t &ci, int &h)
 }
 
 // ------------------------------------------------------------------ table
-__global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *off)
+// Chunk plan of gdr_chunk_plan.hpp: off[b] = first chunk of request b (B + 1
+// entries, off[B] <= budget), and redo[b * HV + h] = 1 for the pairs of the
+// requests that get no chunks although they have tokens (ranges that overlap
+// after a decreasing cu_seqlens entry); the recurrent kernel takes those.
+// Prefix sums are 64-bit: overlapping ranges can sum to B * ceil(T / 64).
+__global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *off, int32_t *redo)
 {
-    __shared__ int32_t s[256];
-    __shared__ int32_t carry;
+    __shared__ int64_t s[256];
+    __shared__ int64_t carry;
+    __shared__ unsigned long long best;  // largest granted inclusive prefix
     const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
+    const int64_t budget = chunk_budget(p.T, p.B);
+    if (tid == 0) {
+        carry = 0;
+        best = 0;
+    }
     __syncthreads();
     for (int base = 0; base < p.B; base += 256) {
         const int b = base + tid;
-        int n = 0;
+        int64_t n = 0;
         if (b < p.B) {
             int64_t st, en;
             request_range(p, b, st, en);
-            n = (int)((en - st + CH - 1) / CH);
+            n = request_chunks(st, en);
         }
         s[tid] = n;
         __syncthreads();
         for (int o = 1; o < 256; o <<= 1) {
-            const int v = tid >= o ? s[tid - o] : 0;
+            const int64_t v = tid >= o ? s[tid - o] : 0;
             __syncthreads();
             s[tid] += v;
             __syncthreads();
         }
-        if (b < p.B) off[b] = carry + s[tid] - n;
+        if (b < p.B) {
+            const int64_t excl = carry + s[tid] - n;
+            // provisional entry (capped so it fits 32 bits); the second pass caps it at best
+            off[b] = (int32_t)(excl < budget + 1 ? excl : budget + 1);
+            const int32_t denied = chunk_denied(excl, n, budget) ? 1 : 0;
+            for (int h = 0; h < p.HV; ++h) redo[(size_t)b * p.HV + h] = denied;
+            if (chunk_granted(excl, n, budget)) atomicMax(&best, (unsigned long long)(excl + n));
+        }
         __syncthreads();
         if (tid == 255) carry += s[255];
         __syncthreads();
     }
-    if (tid == 0) off[p.B] = carry;
+    const int64_t top = (int64_t)best;
+    for (int b = tid; b < p.B; b += 256) off[b] = chunk_offset(off[b], top);
+    if (tid == 0) off[p.B] = chunk_offset(carry, top);
 }
-
 
 // ------------------------------------------------------------------ phase 1
 // 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
@@ -324,6 +381,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
         if (kq_writer)
             *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
+    post_vmax(ldv, rec + R_SC);
     lds_barrier();
 
     // ---- K^T fragments (key 16 mt + lr, tokens 32 ks + 8 lq .. +7); fragment f = block * 64 + lane
@@ -934,6 +992,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
         *reinterpret_cast<a8 *>(&sK[r][c8]) = ldv[i];
     }
+    post_vmax(ldv, rec + RC::SC);
     // W's right-hand-side fragments wait in LDS (in fragment order: one
     // 16-byte read each later), so no register holds them across the solve
     h8 *sBw = reinterpret_cast<h8 *>(sm + 2 * SLOT);  // [plane][wave][c][ks][lane]
@@ -1138,6 +1197,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token] D^T
     __shared__ __align__(16) half_t sDs[2][PK ? 1 : TR][CH];  // [hi, lo][row][token] (kd D)^T, chain only
     __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
+    __shared__ float sTM[4][2];                           // per chain wave: max |S0| of its part, max |v|
 
     const int HV = p.HV;
     // A group is one (request, head) -- with segments one (request, head,
@@ -1154,6 +1214,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
     if (mode == SEG_TRANS && seg == 0) return;  // segment 0 has no transition tiles
     const int b = bh / HV, h = bh % HV;
+    if (off[p.B + 1 + bh]) return;  // the recurrent kernel takes this pair
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
     const int row0 = tile * TR;
@@ -1182,6 +1243,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     }
     const int tb = wave & 3;  // token block of this wave (D rows for the chain, O columns for the output)
     const int qh = (int)(((int64_t)h * p.H) / HV);
+    // The tile runs scaled by 2^e (tile_exponent): from max |v| over the
+    // unit's chunks (a transition tile leaves v out) and the tile's max |S0|,
+    // which the chain waves post before the first barrier.  A unit with no
+    // chunks copies its state unscaled.
+    auto scale_exp = [&]() {
+        const float ms = fmaxf(fmaxf(sTM[0][0], sTM[1][0]), fmaxf(sTM[2][0], sTM[3][0]));
+        const float mv = fmaxf(fmaxf(sTM[0][1], sTM[1][1]), fmaxf(sTM[2][1], sTM[3][1]));
+        return ce > cb ? tile_exponent(fmaxf(mode == SEG_TRANS ? 0.f : mv, ms)) : 0;
+    };
     // per head: K^T and q of chunk jj come from the (chunk, q/k head) area, else from the record
     auto kq_rsrc = [&](int jj) {
         if constexpr (PK) return make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
@@ -1190,7 +1260,13 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 
     if (wave < 4) {
         // ================================================================ chain
-        const float um = mode == SEG_TRANS ? 0.f : 1.f;  // a transition tile leaves U out
+        // max |v| over the unit's chunks, as the prologue waves posted it
+        float mv = 0.f;
+        for (int j = cb + tid; j < ce; j += 256) {
+            const f4v m4 = *reinterpret_cast<const f4v *>(ws + ((size_t)(c0 + j) * HV + h) * RC::SIZE + RC::SC +
+                                                          SC_VMAX * 4);
+            mv = fmaxf(mv, fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        }
         // Sc[a][rt][i] = S[row0 + 16 rt + lr][16 (2 wave + a) + 4 lq + i]
         f4v Sc[2][NVB];
 #pragma unroll
@@ -1208,6 +1284,32 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                     for (int i = 0; i < 4; ++i) Sc[a][rt][i] = row == col + i ? one : 0.f;
                 }
             }
+        {
+            float mx = 0.f;
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Sc[a][rt][i]));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                mx = fmaxf(mx, __shfl_xor(mx, o));
+                mv = fmaxf(mv, __shfl_xor(mv, o));
+            }
+            if (lane == 0) {
+                sTM[wave][0] = mx;
+                sTM[wave][1] = mv;
+            }
+        }
+        lds_barrier();  // 0: the tile's max |S0| is posted
+        const int sx = scale_exp();
+        const float up = ldexpf(1.f, sx), down = ldexpf(1.f, -sx);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= up;
+        const float um = mode == SEG_TRANS ? 0.f : up;  // a transition tile leaves U out
         struct Ops {
             h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
             h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
@@ -1369,11 +1471,12 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int rt = 0; rt < NVB; ++rt)
-                    *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt];
+                    *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt] * down;
         }
     } else if (mode != SEG_REAL) {
         // carry and transition tiles write no output: these waves only keep
-        // the chain's two barriers per chunk step
+        // the chain's barriers (one at the start, two per chunk step)
+        lds_barrier();  // 0
         for (int j = cb; j < ce; ++j) {
             lds_barrier();
             lds_barrier();
@@ -1381,6 +1484,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     } else {
         // ================================================================ outputs
         TA *o = static_cast<TA *>(p.o);
+        lds_barrier();  // 0: the chain waves have posted the tile's max |S0|
+        const float down = ldexpf(1.f, -scale_exp());  // o = (scaled o) / 2^e
         struct Ops {
             h8 q[4][NPL];     // q rows (per key: Qg hi, lo) of token block tb, four k-steps of 32
             h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
@@ -1490,7 +1595,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             for (int vb = 0; vb < NVB; ++vb) {
                 typename ActVec<TA>::v4 ov;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = from_f32<TA>(acc[vb][i]);
+                for (int i = 0; i < 4; ++i) ov[i] = from_f32<TA>(acc[vb][i] * down);
                 *reinterpret_cast<typename ActVec<TA>::v4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
             }
         };
@@ -1520,11 +1625,12 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 // start_{p+1} = start_p M_p + c_p for the middle segments p = 1 .. nseg - 2,
 // in order; rows are independent, so one workgroup takes 16 rows of one
 // (request, head) and keeps them in LDS from one segment to the next.
-__global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanSeg sg)
+__global__ __launch_bounds__(256) void k_seg_combine(const Params p, const int32_t *off, const ScanSeg sg)
 {
     const int64_t bh = blockIdx.x >> 3;
     const int rb = blockIdx.x & 7;
     if (bh >= (int64_t)p.B * p.HV) return;
+    if (off[p.B + 1 + bh]) return;  // the recurrent kernel takes this pair
     const float *src;
     float *dst;
     if (!state_ptrs(p, (int)(bh / p.HV), (int)(bh % p.HV), src, dst)) return;
@@ -1561,18 +1667,21 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const ScanS
 
 // ------------------------------------------------------------------ host side
 
-// Workspace: chunk table | records of every (chunk, value head) | per head:
-// K^T and q of every (chunk, q/k head) | segment states
+// Workspace: chunk table (off[B + 1], then the (B * HV) hand-over flags) |
+// records of every (chunk, value head) | per head: K^T and q of every (chunk,
+// q/k head) | segment states.  The chunk budget of gdr_chunk_plan.hpp sizes
+// the records; the table never assigns a chunk index at or past it.
+static size_t table_bytes(int B, int HV) { return ((size_t)(B + 1) * 4 + (size_t)B * HV * 4 + 255) / 256 * 256; }
+
 static size_t kq_offset(int64_t T, int B, int HV, bool per_key)
 {
-    const int64_t maxch = (T + CH - 1) / CH + B;
-    const size_t table = ((size_t)(B + 1) * 4 + 255) / 256 * 256;
-    return table + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
+    const int64_t maxch = chunk_budget(T, B);
+    return table_bytes(B, HV) + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
 }
 
 static size_t seg_offset(int64_t T, int B, int H, int HV, bool per_key)
 {
-    const int64_t maxch = (T + CH - 1) / CH + B;
+    const int64_t maxch = chunk_budget(T, B);
     return kq_offset(T, B, HV, per_key) + (per_key ? 0 : ((size_t)maxch * H * KQ::SIZE + 255) / 256 * 256);
 }
 
@@ -1621,7 +1730,7 @@ static void launch_scans(const Params &p, const int32_t *off, const char *rec, c
     launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs}, s);
     if (nseg > 2) {
         const int64_t blocks = pairs * 8;
-        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, ScanSeg{nseg, 0, xs});
+        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, off, ScanSeg{nseg, 0, xs});
     }
     if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
     else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
@@ -1633,14 +1742,14 @@ static void launch_scans(const Params &p, const int32_t *off, const char *rec, c
 template <typename TA, int RULE, bool PK, bool PKG>
 static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s)
 {
-    const int64_t maxch = (p.T + CH - 1) / CH + p.B;
-    const size_t table = ((size_t)(p.B + 1) * 4 + 255) / 256 * 256;
+    const int64_t maxch = chunk_budget(p.T, p.B);
     char *base = static_cast<char *>(ws);
     int32_t *off = reinterpret_cast<int32_t *>(base);
-    char *rec = base + table;
+    int32_t *redo = off + p.B + 1;
+    char *rec = base + table_bytes(p.B, p.HV);
     char *kq = base + kq_offset(p.T, p.B, p.HV, PK);
     float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.H, p.HV, PK));
-    hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off);
+    hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off, redo);
     if (maxch * p.HV > 0) {
         if constexpr (PK)
             hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
@@ -1648,7 +1757,17 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
             hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec, kq);
     }
     launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, nseg, s);
-    return hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // Requests whose ranges overlap an earlier one's (a decreasing cu_seqlens
+    // entry) may be left out of the chunk budget; the recurrent kernel runs
+    // exactly those pairs.  Uniform packing never overlaps.
+    if (p.cu_seqlens) {
+        Params r = p;
+        r.run_only = redo;
+        return launch_recurrent(r, RULE, PKG, std::is_same<TA, bf16_t>::value ? 2 : 1, D128, 2, s);
+    }
+    return hipSuccess;
 }
 
 }  // namespace GDR_CHUNK_NS

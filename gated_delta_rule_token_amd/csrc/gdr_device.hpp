@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdr_chunk_plan.hpp"
+
 namespace gdr {
 
 enum Rule : int { LINEAR = 0, GATED = 1, DELTA = 2, GATED_DELTA = 3, GATED_DELTA_V2 = 4 };
@@ -40,6 +42,10 @@ struct Params {
     int32_t gate_qwen, gate_dt, beta_sigmoid, qk_l2_norm;  // gate_dt: 0 fp32, 1 fp16, 2 bf16
     int32_t beta_bcast;        // 1: beta is (T, 1), one update rate per token for every head
     float scale;
+    // (B * HV) flags, or nullptr: the recurrent kernel then runs only the
+    // (request, value head) pairs whose flag is set (the chunked form's
+    // hand-over of the pairs it did not take)
+    const int32_t *run_only;
 };
 
 typedef _Float16 half_t;
@@ -150,11 +156,7 @@ __device__ __forceinline__ float update_rate(const Params &p, size_t th)
 __device__ __forceinline__ void request_range(const Params &p, int b, int64_t &s, int64_t &e)
 {
     if (p.cu_seqlens) {
-        int64_t a = p.cu_seqlens[b], z = p.cu_seqlens[b + 1];
-        a = a < 0 ? 0 : (a > p.T ? p.T : a);
-        z = z < 0 ? 0 : (z > p.T ? p.T : z);
-        s = a;
-        e = z > a ? z : a;
+        clamp_request(p.cu_seqlens[b], p.cu_seqlens[b + 1], p.T, s, e);
     } else {
         s = (int64_t)b * p.L;
         int64_t len = p.L;

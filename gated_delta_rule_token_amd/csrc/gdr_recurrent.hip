@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void k_recurrent(const Params p)
     const int qh = (int)(((int64_t)h * H) / HV);
     const bool fullk = dk == DKT;
 
+    if (p.run_only && !p.run_only[(size_t)b * HV + h]) return;
     const float *src;
     float *dst;
     if (!state_ptrs(p, b, h, src, dst)) return;

@@ -12,8 +12,10 @@ It shares no code with the HIP path.
 * ``oracle.chunked.forward_chunked`` -- the chunk-parallel form of the same
   recurrence (fp64 numpy), checked against ``forward`` by brute force.
 * ``oracle.kmajor.forward_kmajor`` -- an independent numpy transcription in
-  the K-major orientation of the ONNX issue's "What LinearAttention currently
-  does" listing, for tiny cross-checks.
+  the K-major orientation of the ONNX issue (sections "What LinearAttention
+  currently does" and "The GDN-2 recurrence"), for tiny cross-checks.
+* ``gate`` -- the standalone gate of the "com.microsoft.LinearAttentionGate"
+  README (``gdro_gate`` in ``gdr_oracle.c``).
 
 Parity pins for all three live in ``tests/test_oracle_*.py``.
 """
@@ -89,6 +91,8 @@ def _open(path):
     lib.gdro_forward.argtypes = [ctypes.POINTER(_Problem)]
     lib.gdro_forward.restype = ctypes.c_int
     lib.gdro_num_threads.restype = ctypes.c_int
+    lib.gdro_gate.argtypes = [ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 6
+    lib.gdro_gate.restype = ctypes.c_int
     return lib
 
 
@@ -242,6 +246,32 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return o.reshape(lead + (HV, DV)), state
+
+
+def gate(a, dt_bias, decay_scale, b=None, want_beta=False, lib=None):
+    """Standalone gate ("com.microsoft.LinearAttentionGate", Description), fp64:
+    decay = decay_scale * softplus(a + dt_bias), beta = sigmoid(b) if wanted.
+    The last axis of ``a`` is the head axis (dt_bias and decay_scale have one
+    entry per head).  Returns (decay, beta or None) as float64 arrays of a's
+    shape."""
+    a = _f64(a)
+    heads = a.shape[-1] if a.ndim else 1
+    dt_bias = _f64(dt_bias).reshape(-1)
+    decay_scale = _f64(decay_scale).reshape(-1)
+    if dt_bias.size != heads or decay_scale.size != heads:
+        raise ValueError("dt_bias and decay_scale need one entry per head")
+    bb = _f64(b)
+    if bb is not None and bb.shape != a.shape:
+        raise ValueError("b must have a's shape")
+    if want_beta and bb is None:
+        raise ValueError("beta requested without b")
+    decay = np.zeros(a.shape, dtype=np.float64)
+    beta = np.zeros(a.shape, dtype=np.float64) if want_beta else None
+    rc = (lib if lib is not None else _load()).gdro_gate(
+        a.size, heads, _ptr(a), _ptr(dt_bias), _ptr(decay_scale), _ptr(bb), _ptr(decay), _ptr(beta))
+    if rc != 0:
+        raise ValueError("oracle gate rejected the arguments (code %d)" % rc)
+    return decay, beta
 
 
 def max_rel_err(got, ref) -> float:

@@ -55,6 +55,9 @@
  *
  * Parallelism: OpenMP over (request, value head, block of state rows).  Rows
  * of a V-major state evolve independently, so the split changes no result.
+ *
+ * gdro_gate (at the end of the file) is the standalone gate of the
+ * "com.microsoft.LinearAttentionGate" README: decay and update rate only.
  */
 #include <math.h>
 #include <omp.h>
@@ -251,6 +254,27 @@ int gdro_forward(const gdro_problem *p)
             run_block(p, b, h, r0, r1, qn, kn, alpha);
         }
         free(scratch);
+    }
+    return 0;
+}
+
+/* Standalone gate fusion, "com.microsoft.LinearAttentionGate" README,
+ * Description and Outputs: for each of `count` elements n of a tensor whose
+ * last axis holds the `heads` heads (element n belongs to head h = n mod heads),
+ *     decay = decay_scale[h] * softplus(a + dt_bias[h])
+ *     beta  = sigmoid(b)                       (only when beta is requested)
+ * in double precision; the page narrows only on store, which the caller's
+ * comparison accounts for.  Returns 0, or a negative code on bad arguments. */
+int gdro_gate(int64_t count, int32_t heads, const double *a, const double *dt_bias,
+              const double *decay_scale, const double *b, double *decay, double *beta)
+{
+    if (count < 0 || heads < 1 || count % heads != 0) return -1;
+    if (count > 0 && (!a || !dt_bias || !decay_scale || !decay)) return -2;
+    if (beta && !b) return -3;
+    for (int64_t n = 0; n < count; ++n) {
+        const int64_t head = n % heads;
+        decay[n] = decay_scale[head] * softplus(a[n] + dt_bias[head]);
+        if (beta) beta[n] = sigmoid(b[n]);
     }
     return 0;
 }

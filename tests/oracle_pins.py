@@ -313,6 +313,26 @@ def pin_gate_arms(fwd):
     _close(st4, st5, 1e-13, "per-key qwen arm state")
 
 
+def pin_zero_vectors_normalise_to_zero(fwd):
+    """qk L2-norm with an all-zero q or k row: the epsilon under the square
+    root (README, Attributes qk_l2_norm) keeps the result finite and zero, so
+    a zero key writes nothing and a zero query reads out nothing."""
+    r = _rng(18)
+    T, H, HV, DK, DV = 4, 1, 2, 6, 3
+    q, k = r.standard_normal((T, H, DK)), r.standard_normal((T, H, DK))
+    q[1] = 0.0
+    k[2] = 0.0
+    v = r.standard_normal((T, HV, DV))
+    S0 = r.standard_normal((1, HV, DV, DK))
+    beta = r.uniform(0, 1, (T, HV))
+    o, st = fwd(q, k, v, update_rule="delta", beta=beta, qk_l2_norm=True, initial_state=S0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(st))
+    _close(o[1], np.zeros_like(o[1]), 0.0, "zero query reads out zero")
+    o2, st2 = fwd(q[:2], k[:2], v[:2], update_rule="delta", beta=beta[:2], qk_l2_norm=True, initial_state=S0)
+    _, st3 = fwd(q[:3], k[:3], v[:3], update_rule="delta", beta=beta[:3], qk_l2_norm=True, initial_state=S0)
+    _close(st3, st2, 0.0, "zero key leaves the state as it was")
+
+
 def pin_l2_norm(fwd):
     r = _rng(10)
     T, H, HV, DK, DV = 5, 2, 2, 6, 3
@@ -484,16 +504,29 @@ def pin_segment_composition(fwd):
 
 
 def pin_kmajor_cross(fwd):
+    """The V-major oracle against the independent K-major transcription: a
+    per-head decay, a decay per key dimension, and the Gated DeltaNet-2
+    key-axis erase gate with a per-key and with a per-head decay."""
     r = _rng(15)
     B, L, H, HV, DK, DV = 2, 6, 2, 4, 5, 3
     q, k = r.standard_normal((B, L, H, DK)), _unit(r.standard_normal((B, L, H, DK)))
     v = r.standard_normal((B, L, HV, DV))
     g, beta = -r.uniform(0, 1, (B, L, HV)), r.uniform(0, 1, (B, L, HV))
+    gk = -r.uniform(0, 1, (B, L, HV, DK))
+    erase = r.uniform(0, 1, (B, L, HV, DK))
     S0 = r.standard_normal((B, HV, DV, DK))
-    o, st = fwd(q, k, v, gate=g, beta=beta, initial_state=S0)
-    o2, st2 = forward_kmajor(q, k, v, g, beta, np.swapaxes(S0, 2, 3))
-    _close(o, o2, 1e-12, "K-major cross o")
-    _close(st, np.swapaxes(st2, 2, 3), 1e-12, "K-major cross state")
+    S0k = np.swapaxes(S0, 2, 3)
+    cases = [
+        ("per-head decay", dict(gate=g, beta=beta), (g, beta, None)),
+        ("per-key decay", dict(gate=gk, beta=beta), (gk, beta, None)),
+        ("erase, per-key decay", dict(update_rule="gated_delta_v2", gate=gk, erase=erase), (gk, None, erase)),
+        ("erase, per-head decay", dict(update_rule="gated_delta_v2", gate=g, erase=erase), (g, None, erase)),
+    ]
+    for name, kw, (kg, kb, ke) in cases:
+        o, st = fwd(q, k, v, initial_state=S0, **kw)
+        o2, st2 = forward_kmajor(q, k, v, kg, kb, S0k, erase=ke)
+        _close(o, o2, 1e-12, "K-major cross o (%s)" % name)
+        _close(st, np.swapaxes(st2, 2, 3), 1e-12, "K-major cross state (%s)" % name)
 
 
 def pin_row_split_invariance(fwd):
@@ -508,9 +541,60 @@ def pin_row_split_invariance(fwd):
     _close(a[1], b[1], 0.0, "row split state")
 
 
+# ---------------------------------------------------------------- standalone gate
+# ("com.microsoft.LinearAttentionGate", Description and Outputs)
+def pin_gate_closed_points(gate, fwd):
+    """softplus(0) = ln 2 and sigmoid(0) = 1/2 at every head (a = -dt_bias
+    exactly, so a wrong head index or bias sign moves the argument off zero);
+    the far tails softplus(40) = 40 + ln(1 + e^-40), softplus(-40) =
+    ln(1 + e^-40) ~ e^-40, sigmoid(+-40) = 1 / (1 + e^-+40)."""
+    import math
+    heads = 5
+    r = _rng(20)
+    dt_bias = r.uniform(-2, 2, heads)
+    dscale = -r.uniform(1, 16, heads)
+    a = np.tile(-dt_bias, (3, 1))
+    d, b = gate(a, dt_bias, dscale, b=np.zeros_like(a), want_beta=True)
+    _close(d, np.tile(dscale * math.log(2.0), (3, 1)), 1e-15, "gate at softplus(0)")
+    _close(b, np.full_like(a, 0.5), 0.0, "sigmoid(0)")
+    e40 = math.exp(-40.0)
+    a = np.array([[40.0, -40.0]])
+    d, b = gate(a, np.zeros(2), np.array([-1.0, -2.0]), b=a, want_beta=True)
+    _close(d, [[-(40.0 + math.log1p(e40)), -2.0 * e40]], 1e-15, "softplus tails")
+    assert abs(d[0, 1] / (-2.0 * e40) - 1.0) < 1e-12, "softplus(-40) keeps its relative precision"
+    _close(b, [[1.0 / (1.0 + e40), e40 / (1.0 + e40)]], 1e-15, "sigmoid tails")
+    assert abs(b[0, 1] / e40 - 1.0) < 1e-12
+
+
+def pin_gate_matches_forward(gate, fwd):
+    """The standalone gate's decay and rate drive the recurrence exactly as
+    the forward pass's fused raw-gate arm and sigmoid (README, Attributes
+    gate_activation / beta_activation): two independent code paths."""
+    r = _rng(21)
+    T, H, HV, DK, DV = 7, 1, 3, 4, 4
+    q, k = r.standard_normal((T, H, DK)), _unit(r.standard_normal((T, H, DK)))
+    v = r.standard_normal((T, HV, DV))
+    a = 3.0 * r.standard_normal((T, HV))
+    braw = 2.0 * r.standard_normal((T, HV))
+    a_log, dt_bias = np.log(r.uniform(1, 16, HV)), r.uniform(0, 1, HV)
+    decay, beta = gate(a, dt_bias, -np.exp(a_log), b=braw, want_beta=True)
+    o, st = fwd(q, k, v, gate=a, a_log=a_log, dt_bias=dt_bias, gate_activation="qwen",
+                beta=braw, beta_activation="sigmoid")
+    o2, st2 = fwd(q, k, v, gate=decay, beta=beta)
+    _close(o2, o, 1e-14, "gate output drives the recurrence like the fused arm (o)")
+    _close(st2, st, 1e-14, "gate output drives the recurrence like the fused arm (state)")
+    # an unconsumed b is allowed and changes nothing (Description)
+    d2, none = gate(a, dt_bias, -np.exp(a_log), b=braw, want_beta=False)
+    assert none is None
+    _close(d2, decay, 0.0, "decay without beta")
+
+
+GATE_PINS = [pin_gate_closed_points, pin_gate_matches_forward]
+
+
 ALL_PINS = [
     pin_golden_hand, pin_linear_closed_form, pin_gated_closed_form, pin_delta_invariant,
     pin_beta_zero, pin_orthonormal_keys, pin_gqa_mapping, pin_varlen_packing, pin_seq_lens, pin_slots,
-    pin_gate_arms, pin_l2_norm, pin_scale, pin_rule_reductions, pin_v2_reductions,
+    pin_gate_arms, pin_zero_vectors_normalise_to_zero, pin_l2_norm, pin_scale, pin_rule_reductions, pin_v2_reductions,
     pin_chunked_equivalence, pin_segment_composition, pin_kmajor_cross, pin_row_split_invariance,
 ]

@@ -270,3 +270,61 @@ def test_gate_argument_checks(lib):
         == api.GDR_E_INVALID  # beta without b
     assert lib.gdr_gate(12, 3, 9, _fake(1), _fake(2), _fake(3), None, _fake(4), None, None) \
         == api.GDR_E_INVALID  # bad dtype
+
+
+def test_forward_rejects_a_short_workspace(lib):
+    """gdr_forward compares the workspace size it is given with what the
+    problem needs and returns GDR_E_WORKSPACE before anything is enqueued."""
+    p, t = _good()
+    p.head_dim_k = p.head_dim_v = 128
+    p.total_tokens, p.act_dtype, p.gate_dtype = 4096, api.F16, api.F16
+    need = ctypes.c_size_t(0)
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(need)) == api.GDR_OK and need.value > 0
+    assert lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(_fake(11)),
+                           need.value - 1, None) == api.GDR_E_WORKSPACE
+    assert lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), None, 0, None) == api.GDR_E_WORKSPACE
+
+
+def _cpu_problem(**kw):
+    import torch
+    T, H, HV, dk, dv, B = 40, 2, 4, 32, 16, 2
+    q = torch.zeros(T, H, dk)
+    v = torch.zeros(T, HV, dv)
+    args = dict(gate=torch.zeros(T, HV), beta=torch.zeros(T, HV), a_log=torch.zeros(HV),
+                dt_bias=torch.zeros(HV), cu_seqlens=torch.zeros(B + 1, dtype=torch.int32),
+                initial_state=torch.zeros(B, HV, dv, dk), gate_activation="qwen")
+    args.update(kw)
+    p = api.build_problem(q, q, v, **args)
+    shapes = {k: (None if x is None else tuple(x.shape)) for k, x in args.items()
+              if k in ("gate", "beta", "a_log", "dt_bias", "cu_seqlens", "initial_state")}
+    return p, (T,), shapes
+
+
+def test_binding_shape_checks():
+    """The binding checks every tensor's shape against the problem before the
+    call (the kernels take raw pointers, so a short buffer would otherwise be
+    read or written out of bounds)."""
+    import torch
+    p, lead, shapes = _cpu_problem()
+    api.check_shapes(p, lead, shapes)  # consistent
+    api.check_shapes(p, lead, dict(shapes, beta=(40, 1), out=(40, 4, 16), final_state=(2, 4, 16, 32)))
+    bad = [("gate", (40, 3)), ("gate", (39, 4)), ("beta", (40, 2)), ("a_log", (3,)),
+           ("dt_bias", (4, 32)), ("cu_seqlens", (2,)), ("initial_state", (2, 4, 32, 16)),
+           ("initial_state", (1, 4, 16, 32)), ("out", (40, 4, 32)), ("final_state", (3, 4, 16, 32)),
+           ("erase", (40, 4)), ("seq_lens", (3,)), ("slot_ids", (1,)), ("gate_scale", (5,))]
+    for name, shape in bad:
+        with pytest.raises(api.GDRError, match=name):
+            api.check_shapes(p, lead, dict(shapes, **{name: shape}))
+    # a per-key gate takes (T, HV, dk) and a (HV, dk) bias
+    pk, lead, sh = _cpu_problem(gate=torch.zeros(40, 4, 32), dt_bias=torch.zeros(4, 32))
+    assert pk.decay_per_key == 1
+    api.check_shapes(pk, lead, sh)
+    with pytest.raises(api.GDRError, match="dt_bias"):
+        api.check_shapes(pk, lead, dict(sh, dt_bias=(4,)))
+    # the slab: (num_slots, HV, dv, dk)
+    ps = api.build_problem(torch.zeros(2, 1, 2, 32), torch.zeros(2, 1, 2, 32), torch.zeros(2, 1, 4, 16),
+                           state=torch.zeros(7, 4, 16, 32), slot_ids=torch.zeros(2, dtype=torch.int32),
+                           update_rule="delta", beta=torch.zeros(2, 1, 4))
+    api.check_shapes(ps, (2, 1), {"state": (7, 4, 16, 32), "slot_ids": (2,), "beta": (2, 1, 4)})
+    with pytest.raises(api.GDRError, match="state"):
+        api.check_shapes(ps, (2, 1), {"state": (7, 4, 32, 16)})

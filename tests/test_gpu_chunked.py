@@ -1,0 +1,188 @@
+"""GPU parity of the chunk-parallel prefill beyond the plain workloads:
+requests whose cu_seqlens ranges overlap (the README's decreasing entries),
+packed == separate calls, a request resumed from its own final state at and
+off chunk boundaries (the state is the checkpoint: README, Inputs
+initial_state and Outputs final_state), state magnitudes far from 1, and the
+three prefill workloads at full size with every (request, head) pair compared
+with the fp64 oracle.  Every call goes through the C ABI."""
+import json
+import os
+import zlib
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_token_amd import workloads
+from tests.gpu_helpers import (TOL_BF16_O, TOL_CHUNKED, assert_close, gpu_forward, oracle_forward, rel_err, say,
+                               sub_case, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_token_amd import api
+    api.load_library()
+
+
+def _case(seed, lengths, **kw):
+    base = dict(H=2, HV=4, DK=128, DV=128, dtype=np.float16, update_rule="gated_delta",
+                gate_activation="qwen", beta_activation="sigmoid", qk_l2_norm=1)
+    base.update(kw)
+    return workloads.random_case(seed, lengths=lengths, **base)
+
+
+def _log_errors(name, **errs):
+    """Append the measured errors of a full-size check to the file named by
+    GDR_PARITY_LOG (one JSON object per line), when set."""
+    path = os.environ.get("GDR_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(name=name, **errs)) + "\n")
+
+
+# ------------------------------------------------------------------ overlapping requests
+OVERLAP_CASES = [
+    # three full-length requests restarting at token 0: 48 chunks against a
+    # budget of 22, so requests 2 and 4 go to the recurrent kernel
+    ("restart_three_times", 1024, [0, 1024, 0, 1024, 0, 1024, 0]),
+    # two overlapping requests fit the budget; the last one, which no other
+    # request overlaps, does not
+    ("overlap_then_tail", 1100, [0, 600, 0, 600, 600, 1100, 0]),
+    # out-of-range and negative entries as well
+    ("out_of_range", 700, [-5, 300, 9999, 0, 700, 200, 700]),
+]
+
+
+@pytest.mark.parametrize("algo", ["chunked", "auto"])
+@pytest.mark.parametrize("name,T,cu", OVERLAP_CASES, ids=[c[0] for c in OVERLAP_CASES])
+def test_overlapping_requests(name, T, cu, algo):
+    """Every request's final state matches the oracle run on that request
+    alone; an output row that several requests write holds one of their
+    values (which one is unspecified), every other row the oracle's."""
+    B = len(cu) - 1
+    case = _case(zlib.crc32(name.encode()) % 1000, [T] + [0] * (B - 1))
+    case["cu_seqlens"] = np.array(cu, dtype=np.int32)
+    say("case overlapping cu_seqlens %s algo=%s" % (cu, algo))
+    d = to_dev(case)
+    sentinel = torch.full((T, 4, 128), 3.0, dtype=torch.float16, device="cuda")
+    o, st = gpu_forward(case, algo, dev=d, out=sentinel)
+    HV = 4
+    cover = [[] for _ in range(T)]
+    refs = []
+    for b in range(B):
+        sc, (s, e) = sub_case(case, b, list(range(HV)))
+        ro, rs = oracle_forward(sc)
+        refs.append((s, e, ro))
+        assert_close(st[b], rs[0], TOL_CHUNKED, "%s final state of request %d" % (name, b))
+        for t in range(s, e):
+            cover[t].append(b)
+    scale = max(float(np.max(np.abs(ro))) for _, _, ro in refs if ro.size)
+    for t in range(T):
+        if not cover[t]:
+            assert np.all(o[t] == 3.0), "row %d belongs to no request and must stay unwritten" % t
+            continue
+        err = np.min([np.abs(o[t] - refs[b][2][t - refs[b][0]]) for b in cover[t]], axis=0)
+        assert np.max(err) <= TOL_CHUNKED * scale, \
+            "row %d (requests %s): max err %.3e" % (t, cover[t], float(np.max(err)) / scale)
+
+
+# ------------------------------------------------------------------ packing and hand-off
+@pytest.mark.parametrize("per_key", [False, True], ids=["per_head", "per_key_form"])
+def test_chunked_packed_equals_separate(per_key):
+    """Each request of a packed chunked call gives, bit for bit, what the same
+    request gives alone (its chunks start at its own first token either way);
+    an empty request copies its state."""
+    kw = dict(update_rule="gated_delta_v2", per_key=True, gate_activation="none",
+              beta_activation="none") if per_key else {}
+    lengths = [300, 0, 70, 200]
+    case = _case(41 + per_key, lengths, **kw)
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    cu = case["cu_seqlens"]
+    for b in range(len(lengths)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        sc, _ = sub_case(case, b, [0, 1, 2, 3])
+        sc["q"], sc["k"] = case["q"][s:e], case["k"][s:e]  # keep the grouped q/k heads
+        ob, sb = gpu_forward(sc, "chunked", scan_segments=1)
+        assert np.array_equal(o[s:e], ob), "request %d o differs when run alone" % b
+        assert np.array_equal(st[b], sb[0]), "request %d state differs when run alone" % b
+    assert np.array_equal(st[1], case["initial_state"][1].astype(np.float64)), "empty request copies its state"
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "packed chunked o")
+    assert_close(st, rs, TOL_CHUNKED, "packed chunked state")
+
+
+@pytest.mark.parametrize("split", [64, 128, 100, 257])
+def test_chunked_resume_split(split):
+    """A request cut in two, the second call starting from the first call's
+    final state, at and off chunk boundaries: within the chunked bar of one
+    call and of the oracle.  (Each call scales its state tiles by a power of
+    two taken from its own inputs, which moves the rounding of the split
+    operands' low parts, so even a cut at a chunk boundary is not bit-exact.)"""
+    T = 300
+    case = _case(43, [T])
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    cut = lambda x, a, b: None if x is None else x[a:b]
+    first = dict(case, cu_seqlens=np.array([0, split], np.int32),
+                 **{k: cut(case[k], 0, split) for k in ("q", "k", "v", "gate", "beta")})
+    oa, sa = gpu_forward(first, "chunked", scan_segments=1)
+    second = dict(case, cu_seqlens=np.array([0, T - split], np.int32), initial_state=sa.astype(np.float32),
+                  **{k: cut(case[k], split, T) for k in ("q", "k", "v", "gate", "beta")})
+    ob, sb = gpu_forward(second, "chunked", scan_segments=1)
+    both = np.concatenate([oa, ob])
+    assert_close(both, o, TOL_CHUNKED, "resumed at %d vs one call: o" % split)
+    assert_close(sb, st, TOL_CHUNKED, "resumed at %d vs one call: state" % split)
+    ro, rs = oracle_forward(case)
+    assert_close(both, ro, TOL_CHUNKED, "resumed at %d: o" % split)
+    assert_close(sb, rs, TOL_CHUNKED, "resumed at %d: state" % split)
+
+
+# ------------------------------------------------------------------ state magnitude
+@pytest.mark.parametrize("magnitude", [1e4, 1e-5])
+@pytest.mark.parametrize("rule", ["gated_delta", "gated"])
+def test_chunked_state_magnitude(magnitude, rule):
+    """States and values far from 1 on the chunked path AUTO picks: entries
+    near 1e4 and near 1e-5 (where fp16 (hi, lo) split operands of the state
+    would turn subnormal unless the tile is scaled).  The state is fp32 and
+    keeps the 2e-3 bar; o is stored in fp16, whose spacing below 2^-14 is
+    2^-24, so o may also differ by the half spacing of that one rounding."""
+    kw = {} if rule == "gated_delta" else dict(beta_activation="none")
+    case = _case(44, [500, 300], update_rule=rule, **kw)
+    case["v"] = (case["v"].astype(np.float32) * np.float32(magnitude)).astype(np.float16)
+    case["initial_state"] = (case["initial_state"] * np.float32(magnitude * 5.0)).astype(np.float32)
+    say("case state magnitude %.0e rule %s" % (magnitude, rule))
+    o, st = gpu_forward(case, "auto")
+    ro, rs = oracle_forward(case)
+    assert float(np.max(np.abs(rs))) > 0.1 * magnitude, "the states reach the intended magnitude"
+    assert_close(st, rs, TOL_CHUNKED, "magnitude %.0e %s state" % (magnitude, rule))
+    bound = TOL_CHUNKED * float(np.max(np.abs(ro))) + 2.0 ** -25
+    worst = float(np.max(np.abs(o - ro)))
+    say("  magnitude %.0e %s o: max abs err %.3e, bound %.3e" % (magnitude, rule, worst, bound))
+    assert np.all(np.isfinite(o)) and worst <= bound
+
+
+# ------------------------------------------------------------------ the workloads, every pair
+FULL = [("varlen_prefill", lambda: workloads.varlen_prefill()),
+        ("long_prefill", lambda: workloads.long_prefill()),
+        ("perkey_erase", lambda: workloads.perkey_erase()),
+        ("varlen_prefill_bf16", lambda: workloads.as_bf16(workloads.varlen_prefill()))]
+
+
+@pytest.mark.parametrize("name,make", FULL, ids=[f[0] for f in FULL])
+def test_workload_every_pair(name, make):
+    """The prefill workload at its full size on the path AUTO runs (the
+    chunked kernels), every (request, value head) pair of o and of the final
+    state against the fp64 oracle."""
+    case = make()
+    say("case %s: AUTO path, all pairs against the oracle" % case["name"])
+    o, st = gpu_forward(case, "auto")
+    ro, rs = oracle_forward(case)
+    tol_o = TOL_BF16_O if case["act_dtype"] == "bf16" else TOL_CHUNKED
+    eo, es = rel_err(o, ro), rel_err(st, rs)
+    _log_errors(case["name"], o=eo, state=es, tol_o=tol_o, tol_state=TOL_CHUNKED)
+    assert_close(o, ro, tol_o, "%s o (all pairs)" % name)
+    assert_close(st, rs, TOL_CHUNKED, "%s state (all pairs)" % name)

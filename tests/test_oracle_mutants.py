@@ -11,7 +11,7 @@ import sys
 import pytest
 
 import oracle
-from tests.oracle_pins import ALL_PINS
+from tests.oracle_pins import ALL_PINS, GATE_PINS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -43,6 +43,15 @@ MUTANTS = [
     ("perkey_first_channel_only", "p->gate[((size_t)t * HV + h) * DK + j]",
      "p->gate[((size_t)t * HV + h) * DK]"),
     ("write_uses_query", "Si[j] += vprime * kn[j];", "Si[j] += vprime * qn[j];"),
+    # the standalone gate
+    ("gate_head_by_row", "const int64_t head = n % heads;", "const int64_t head = (n / heads) % heads;"),
+    ("gate_bias_dropped", "softplus(a[n] + dt_bias[head])", "softplus(a[n])"),
+    ("gate_bias_sign", "softplus(a[n] + dt_bias[head])", "softplus(a[n] - dt_bias[head])"),
+    ("gate_scale_dropped", "decay[n] = decay_scale[head] *", "decay[n] = -1.0 *"),
+    ("gate_beta_sign", "if (beta) beta[n] = sigmoid(b[n]);", "if (beta) beta[n] = sigmoid(-b[n]);"),
+    ("gate_beta_from_a", "if (beta) beta[n] = sigmoid(b[n]);", "if (beta) beta[n] = sigmoid(a[n]);"),
+    # the L2 norm of a zero row
+    ("l2_eps_dropped", "1.0 / sqrt(kss + 1e-12)", "1.0 / sqrt(kss)"),
 ]
 
 
@@ -50,10 +59,16 @@ def run_pins_on_variant(src_text, lib_path):
     """Compile ``src_text`` and return the names of the pins it fails."""
     lib = oracle.compile_variant(src_text, lib_path)
     fwd = functools.partial(oracle.forward, lib=lib)
+    gate = functools.partial(oracle.gate, lib=lib)
     caught = []
     for pin in ALL_PINS:
         try:
             pin(fwd)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    for pin in GATE_PINS:
+        try:
+            pin(gate, fwd)
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     return caught
