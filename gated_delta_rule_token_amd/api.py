@@ -70,7 +70,8 @@ class Tensors(ctypes.Structure):
 
 
 EXPORTS = ("gdr_abi_version", "gdr_status_str", "gdr_last_error", "gdr_validate",
-           "gdr_workspace_size", "gdr_select_algo", "gdr_forward", "gdr_gate")
+           "gdr_workspace_size", "gdr_select_algo", "gdr_forward", "gdr_forward_noalloc", "gdr_gate")
+NOALLOC_SCRATCH_BYTES = 256 << 20  # GDR_NOALLOC_SCRATCH_BYTES of include/gdr.h
 
 
 def library_path() -> str:
@@ -102,6 +103,8 @@ def load_library():
         lib.gdr_forward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Tensors), ctypes.c_void_p,
                                     ctypes.c_size_t, ctypes.c_void_p]
         lib.gdr_forward.restype = ctypes.c_int
+        lib.gdr_forward_noalloc.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Tensors), ctypes.c_void_p]
+        lib.gdr_forward_noalloc.restype = ctypes.c_int
         lib.gdr_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p]
@@ -243,30 +246,13 @@ def selected_algo(problem: Problem) -> str:
     return ALGO_NAMES[a.value]
 
 
-def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
-            cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
-            update_rule="gated_delta", gate_activation="none", beta_activation="none",
-            qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", out=None,
-            final_state=None, workspace=None, batch=None, gate_scale=None, seq_lens=None,
-            scan_segments=0):
-    """Run the gated delta rule on the GPU.
-
-    q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
-    decay, or the raw projection with gate_activation='qwen'): (...,HV) or
-    per key (...,HV,dk); beta: (...,HV) fp32, or (...,1) for one rate per
-    token; erase: (...,HV,dk) fp32.
-    Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a per-key gate, and either
-    a_log (HV,) or the folded gate_scale = -exp(a_log) (HV,).  seq_lens (B,)
-    int32 bounds each uniform-packed request to its first seq_lens[b] tokens
-    (rows past it in ``o`` are left as they are).  scan_segments: for the
-    chunked form, 0 lets the library choose, 1 runs each request's chunks in
-    one serial pass, n > 1 splits that chain into n composed segments.
-    With ``state`` (a slab (num_slots,HV,dv,dk) fp32) and ``slot_ids``, the
-    slab is updated in place and returned as the second result; otherwise a
-    final state (B,HV,dv,dk) is allocated (or ``final_state`` is filled).
-    Returns (o, final_state).
-    """
-    lib = load_library()
+def _marshal(q, k, v, gate=None, beta=None, erase=None, a_log=None, dt_bias=None,
+             cu_seqlens=None, initial_state=None, slot_ids=None, state=None,
+             update_rule="gated_delta", gate_activation="none", beta_activation="none",
+             qk_l2_norm=False, scale=0.0, chunk_size=64, algo="auto", out=None,
+             final_state=None, batch=None, gate_scale=None, seq_lens=None, scan_segments=0):
+    """Checked Problem and Tensors structs of one call, with its outputs
+    (allocated when not given)."""
     dev = q.device
     _need(q, "q", device=dev)
     _need(k, "k", q.dtype, dev)
@@ -310,21 +296,58 @@ def forward(q, k, v, *, gate=None, beta=None, erase=None, a_log=None, dt_bias=No
                                   cu_seqlens=cu_seqlens, seq_lens=seq_lens, slot_ids=slot_ids,
                                   initial_state=initial_state,
                                   final_state=None if state is not None else fin, state=state))
-    ws_bytes = workspace_size(p)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_have = 0
-    if workspace is not None:
-        _need(workspace, "workspace", device=dev)
-        ws_have = workspace.numel() * workspace.element_size()
     t = Tensors(q=_ptr(q), k=_ptr(k), v=_ptr(v), o=_ptr(out), gate=_ptr(gate), beta=_ptr(beta),
                 erase=_ptr(erase), a_log=_ptr(a_log), dt_bias=_ptr(dt_bias),
                 cu_seqlens=_ptr(cu_seqlens), slot_ids=_ptr(slot_ids),
                 initial_state=_ptr(initial_state), final_state=_ptr(fin),
                 gate_scale=_ptr(gate_scale), seq_lens=_ptr(seq_lens))
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    return p, t, out, fin
+
+
+def forward(q, k, v, *, workspace=None, **kw):
+    """Run the gated delta rule on the GPU.
+
+    q, k: (T,H,dk) or (B,L,H,dk); v: (T,HV,dv) or (B,L,HV,dv); gate (log
+    decay, or the raw projection with gate_activation='qwen'): (...,HV) or
+    per key (...,HV,dk); beta: (...,HV) fp32, or (...,1) for one rate per
+    token; erase: (...,HV,dk) fp32.
+    Raw-gate arm: dt_bias (HV,) or (HV,dk) beside a per-key gate, and either
+    a_log (HV,) or the folded gate_scale = -exp(a_log) (HV,).  seq_lens (B,)
+    int32 bounds each uniform-packed request to its first seq_lens[b] tokens
+    (rows past it in ``o`` are left as they are).  scan_segments: for the
+    chunked form, 0 lets the library choose, 1 runs each request's chunks in
+    one serial pass, n > 1 splits that chain into n composed segments.
+    With ``state`` (a slab (num_slots,HV,dv,dk) fp32) and ``slot_ids``, the
+    slab is updated in place and returned as the second result; otherwise a
+    final state (B,HV,dv,dk) is allocated (or ``final_state`` is filled).
+    ``workspace``: a uint8 device tensor for the chunked form (allocated here
+    when not given).  Returns (o, final_state).
+    """
+    lib = load_library()
+    p, t, out, fin = _marshal(q, k, v, **kw)
+    ws_bytes = workspace_size(p)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0
+    if workspace is not None:
+        _need(workspace, "workspace", device=q.device)
+        ws_have = workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
     # the library checks the real size against what the problem needs
     check(lib.gdr_forward(ctypes.byref(p), ctypes.byref(t), _ptr(workspace), ws_have, stream))
+    return out, fin
+
+
+def forward_noalloc(q, k, v, **kw):
+    """``forward`` through gdr_forward_noalloc: the library serves the
+    workspace from its own fixed device array (up to NOALLOC_SCRATCH_BYTES);
+    nothing is allocated for it.  Same arguments as ``forward`` without
+    ``workspace``; outputs are allocated here unless ``out`` / ``final_state``
+    / ``state`` are given.  Returns (o, final_state)."""
+    lib = load_library()
+    p, t, out, fin = _marshal(q, k, v, **kw)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    check(lib.gdr_forward_noalloc(ctypes.byref(p), ctypes.byref(t), stream))
     return out, fin
 
 

@@ -8,13 +8,23 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gdr_launch.hpp"
 
+// Workspace of gdr_forward_noalloc, one copy per GPU (see include/gdr.h).  In
+// host code `scratch` is only a handle: its device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
 
 gdr_status fail(gdr_status st, const char *fmt, ...)
 {
@@ -224,6 +234,27 @@ int rows_group(const gdr_problem *p)
     return p->head_dim_v <= 16 ? 1 : 2;
 }
 
+gdr_status fail(gdr_status st, const char *fmt, ...);
+
+// Device address of the current device's scratch copy, looked up once per device.
+gdr_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(GDR_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(GDR_E_UNSUPPORTED, "device ordinal %d beyond %d", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr)
+            return fail(GDR_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(err));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,18 +307,14 @@ gdr_status gdr_select_algo(const gdr_problem *problem, int32_t *algo)
     return GDR_OK;
 }
 
-gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, void *workspace,
-                       size_t workspace_bytes, void *stream)
-{
-    g_last_error.clear();
-    if (!tensors) return fail(GDR_E_INVALID, "tensors is NULL");
-    gdr_status st = gdr_validate(problem, tensors);
-    if (st != GDR_OK) return st;
-    size_t need = 0;
-    gdr_workspace_size(problem, &need);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(GDR_E_WORKSPACE, "workspace of %zu bytes required", need);
+}  // extern "C"
 
+namespace {
+
+// Enqueue every kernel of a validated call on `stream`; `workspace` holds at
+// least gdr_workspace_size bytes.
+gdr_status launch_all(const gdr_problem *problem, const gdr_tensors *tensors, void *workspace, void *stream)
+{
     const gdr_problem &p = *problem;
     const gdr_tensors &t = *tensors;
     gdr::Params k{};
@@ -335,6 +362,45 @@ gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, v
     }
     if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    if (!tensors) return fail(GDR_E_INVALID, "tensors is NULL");
+    gdr_status st = gdr_validate(problem, tensors);
+    if (st != GDR_OK) return st;
+    size_t need = 0;
+    gdr_workspace_size(problem, &need);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDR_E_WORKSPACE, "workspace of %zu bytes required", need);
+    return launch_all(problem, tensors, workspace, stream);
+}
+
+gdr_status gdr_forward_noalloc(const gdr_problem *problem, const gdr_tensors *tensors, void *stream)
+{
+    g_last_error.clear();
+    if (!tensors) return fail(GDR_E_INVALID, "tensors is NULL");
+    gdr_status st = gdr_validate(problem, tensors);
+    if (st != GDR_OK) return st;
+    size_t need = 0;
+    gdr_workspace_size(problem, &need);
+    if (need > GDR_NOALLOC_SCRATCH_BYTES)
+        return fail(GDR_E_WORKSPACE,
+                    "this problem needs %zu bytes of workspace, above the %zu bytes gdr_forward_noalloc holds; "
+                    "call gdr_forward with a workspace instead",
+                    need, (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(&ws);
+        if (st != GDR_OK) return st;
+    }
+    return launch_all(problem, tensors, ws, stream);
 }
 
 gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a, const float *dt_bias,

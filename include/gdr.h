@@ -62,7 +62,8 @@
  * contract, CLIKA "gatedDeltaUpdate"); duplicates give undefined results.
  *
  * Ownership: the caller owns every buffer; the library allocates and frees
- * nothing and keeps no state between calls.  All device work is enqueued on
+ * nothing and keeps no state between calls (gdr_forward_noalloc's workspace is
+ * a fixed array in the library's device code, see there).  All device work is enqueued on
  * the caller's stream; no call synchronises the stream or reads device
  * memory from the host.  final_state may be the same pointer as
  * initial_state (in-place update); any other overlap between an output and
@@ -128,12 +129,16 @@ typedef enum {
     GDR_ALGO_DECODE = 2,     /* one workgroup streams one (request, head) state */
     GDR_ALGO_CHUNKED = 3     /* chunk-parallel form (fp16 or bf16, dk = dv = 128).  Its products
                               * run on fp16 matrix cores with every fp32 operand split
-                              * into an fp16 (hi, lo) pair: state entries and effective
-                              * value updates must stay below 65504 in magnitude (beyond
-                              * it the result is not finite), and a state whose every
-                              * entry is below about 1e-4 loses relative precision in the
-                              * lo part (its absolute error stays near 2^-24).  Use
-                              * GDR_ALGO_RECURRENT (all fp32) outside that range. */
+                              * into an fp16 (hi, lo) pair.  Each state tile runs scaled
+                              * by a power of two that brings the larger of max |v| over
+                              * its chunks and max |S0| of the tile to [4, 8), so inputs
+                              * of any overall size keep ~22 bits; a state that grows
+                              * past about 8000 times that size (gated or linear rules
+                              * over very long requests with aligned keys) leaves the
+                              * fp16 range and the result is not finite.  Requests whose
+                              * cu_seqlens ranges overlap an earlier request's beyond the
+                              * chunk budget run on the recurrent kernel.  Use
+                              * GDR_ALGO_RECURRENT (all fp32) for such growth. */
 } gdr_algo;
 
 typedef struct {
@@ -211,6 +216,27 @@ gdr_status gdr_select_algo(const gdr_problem *problem, int32_t *algo);
  * gdr_workspace_size bytes (may be NULL when that size is 0). */
 gdr_status gdr_forward(const gdr_problem *problem, const gdr_tensors *tensors,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Largest workspace gdr_forward_noalloc can serve (256 MiB). */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* gdr_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * workspace comes from a fixed array of GDR_NOALLOC_SCRATCH_BYTES in the
+ * library's device code: each GPU the library runs on holds its own copy
+ * from the first use of the library's code there until the process ends.
+ * The first call on a device looks up that device's copy (the current
+ * device; `stream` must belong to it, as for any launch).  The call then
+ * allocates nothing and launches exactly what gdr_forward launches.
+ *
+ * Problems whose gdr_workspace_size exceeds GDR_NOALLOC_SCRATCH_BYTES are
+ * rejected with GDR_E_WORKSPACE before anything is enqueued (gdr_forward
+ * with a caller workspace serves them).  Calls on one GPU share its array:
+ * calls ordered on one stream are fine, calls that overlap in time on one GPU
+ * (different streams, or other threads) race on it.  Nothing in the array
+ * needs to start at zero: every byte a call reads is written earlier in the
+ * same call. */
+gdr_status gdr_forward_noalloc(const gdr_problem *problem, const gdr_tensors *tensors, void *stream);
 
 /* Standalone gate fusion ("com.microsoft.LinearAttentionGate", Description):
  *   decay[n] = decay_scale[h] * softplus(a[n] + dt_bias[h])
