@@ -173,8 +173,8 @@ PREFILL_CASES = {
     "perkey": lambda w: w.perkey_erase(),
     "varlen_bf16": lambda w: w.as_bf16(w.varlen_prefill()),
 }
-MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix, published
-MFMA_16X16X32_FLOPS = 2 * 16 * 16 * 32
+CLOCK_HZ = 2.4e9    # MI355X peak engine clock
+SIMDS = 256 * 4     # 256 CUs x 4 SIMDs
 
 
 def prefill_bytes(case):
@@ -239,9 +239,11 @@ def bench_prefill(args, which):
         "recurrence_equivalent": {"tflops": tflops, "frac_of_fp32_vector_peak": tflops / FP32_VECTOR_PEAK_TFLOPS},
         "kernel_source_digest": digest,
     }
-    if counters and "mfma_16x16x32_per_call" in counters:
-        mf = float(counters["mfma_16x16x32_per_call"]) * MFMA_16X16X32_FLOPS / (kms * 1e-3) / 1e12
-        out["mfma"] = {"executed_tflops": mf, "peak": MFMA_F16_PEAK_TFLOPS, "frac": mf / MFMA_F16_PEAK_TFLOPS}
+    if counters and "mfma_busy_cycles_per_call" in counters:
+        # matrix-core busy SIMD-cycles of the call's kernels (committed counter
+        # summary) over the SIMD-cycles of the call at the nominal clock
+        busy = float(counters["mfma_busy_cycles_per_call"])
+        out["mfma"] = {"busy_frac": busy / (kms * 1e-3 * CLOCK_HZ * SIMDS), "busy_cycles": busy}
     if case["cu_seqlens"] is not None:
         out["lengths"] = np.diff(case["cu_seqlens"]).tolist()
     if not args.no_cpu_baseline:

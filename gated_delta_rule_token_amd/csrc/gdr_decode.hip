@@ -73,6 +73,46 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
     int64_t s, e;
     request_range(p, b, s, e);
 
+    const TA *__restrict__ q = static_cast<const TA *>(p.q);
+    const TA *__restrict__ k = static_cast<const TA *>(p.k);
+    const TA *__restrict__ v = static_cast<const TA *>(p.v);
+    TA *__restrict__ o = static_cast<TA *>(p.o);
+
+    // Staged token inputs (STG): the raw inputs of up to TB tokens, NI
+    // elements per thread, loaded into registers and parked in LDS.  The first
+    // block is requested before the state stream, so waiting for it never
+    // waits for the state.
+    constexpr int TB = 8, NTH = 64 * WAVES, NI = TB * DK / NTH;
+    constexpr bool ER = RULE == GATED_DELTA_V2;
+    struct Raw {
+        float q[NI], k[NI], v[NI], g[VD ? NI : 1], e[ER ? NI : 1];
+        float ga, bt;  // scalar log decay and update rate (thread tid < nt: token tid)
+    };
+    auto load_block = [&](int64_t t0, int nt, Raw &r) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + NTH * j, tt = i / DK, c = i % DK;
+            const int ts = tt < nt ? tt : nt - 1;  // rows past the block repeat its last token
+            const size_t t = (size_t)(t0 + ts), th = t * HV + h;
+            r.q[j] = to_f32(q[(t * H + qh) * DK + c]);
+            r.k[j] = to_f32(k[(t * H + qh) * DK + c]);
+            r.v[j] = to_f32(v[th * DK + c]);
+            if constexpr (VD) r.g[j] = PK ? log_decay_key(p, th, h, c) : log_decay(p, th, h);
+            if constexpr (ER) r.e[j] = p.erase[th * DK + c];
+        }
+        r.ga = 0.f;
+        r.bt = 1.f;
+        if (tid < nt) {
+            const size_t th = (size_t)(t0 + tid) * HV + h;
+            if constexpr (DEC && !VD) r.ga = log_decay(p, th, h);
+            if constexpr (BETA) r.bt = update_rate(p, th);
+        }
+    };
+    Raw raw;
+    if constexpr (STG) {
+        if (e > s) load_block(s, (int)((e - s) < TB ? (e - s) : TB), raw);
+    }
+
     // lane's first element within row group g: row (wrow0 + 4*g + r4), column l16*4
     const size_t lane_off = (size_t)(wrow0 + r4) * DK + l16 * 4;
     f4 S[G][2];
@@ -87,11 +127,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
 #pragma unroll
         for (int g = 0; g < G; ++g) S[g][0] = S[g][1] = f4{0.f, 0.f, 0.f, 0.f};
     }
-
-    const TA *__restrict__ q = static_cast<const TA *>(p.q);
-    const TA *__restrict__ k = static_cast<const TA *>(p.k);
-    const TA *__restrict__ v = static_cast<const TA *>(p.v);
-    TA *__restrict__ o = static_cast<TA *>(p.o);
 
     // One token: q and k columns (l16*4 .. +3, 64 + l16*4 .. +3) of this lane,
     // v of its rows, and for a per-key decay / the erase gate their values at
@@ -202,43 +237,132 @@ __global__ __launch_bounds__(64 * WAVES) void k_decode128(const Params p)
             token(t, qv, kv, vi, ga, bt, gk, er);
         }
     } else {
-        // token inputs of up to TB tokens, widened to fp32 in LDS
-        constexpr int TB = 8, NTH = 64 * WAVES;
-        constexpr bool ER = RULE == GATED_DELTA_V2;
+        // Staged tokens.  Per block: park the raw inputs in LDS, normalise
+        // each token once for the workgroup (q and k by their L2 norms, q.k,
+        // the decay factor, and on the per-key path q o alpha and
+        // erase o alpha o k), then apply the block's tokens to the row groups
+        // in two halves.
         __shared__ float stq[TB][DK], stk[TB][DK], stv[TB][DK];
-        __shared__ float stg[VD ? TB : 1][DK], ste[ER ? TB : 1][DK];
-        __shared__ float sts[TB][2];
-        for (int64_t t0 = s; t0 < e; t0 += TB) {
-            const int nt = (int)((e - t0) < TB ? (e - t0) : TB);
-            for (int i = tid; i < nt * DK; i += NTH) {
-                const int tt = i >> 7, c = i & (DK - 1);
-                const size_t t = (size_t)(t0 + tt), th = t * HV + h;
-                stq[tt][c] = to_f32(q[(t * H + qh) * DK + c]);
-                stk[tt][c] = to_f32(k[(t * H + qh) * DK + c]);
-                stv[tt][c] = to_f32(v[th * DK + c]);
-                if constexpr (VD) stg[tt][c] = PK ? log_decay_key(p, th, h, c) : log_decay(p, th, h);
-                if constexpr (ER) ste[tt][c] = p.erase[th * DK + c];
-            }
-            if (tid < nt) {
-                const size_t th = (size_t)(t0 + tid) * HV + h;
-                float ga = 0.f;
-                if constexpr (DEC && !VD) ga = log_decay(p, th, h);
-                sts[tid][0] = ga;
-                sts[tid][1] = BETA ? update_rate(p, th) : 1.f;
-            }
-            lds_barrier();
-            for (int tt = 0; tt < nt; ++tt) {
-                float qv[C], kv[C], vi[G], gk[C] = {}, er[C] = {};
+        __shared__ float sta[VD ? TB : 1][DK], stb[VD ? TB : 1][DK];
+        __shared__ float sts[TB][4];  // q.k (normalised), decay factor, update rate
+        auto park = [&](const Raw &r, int nt) {
 #pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    qv[c] = stq[tt][col_of(c)];
-                    kv[c] = stk[tt][col_of(c)];
-                    if constexpr (VD) gk[c] = stg[tt][col_of(c)];
-                    if constexpr (ER) er[c] = ste[tt][col_of(c)];
+            for (int j = 0; j < NI; ++j) {
+                const int i = tid + NTH * j, tt = i / DK, c = i % DK;
+                stq[tt][c] = r.q[j];
+                stk[tt][c] = r.k[j];
+                stv[tt][c] = r.v[j];
+                if constexpr (VD) sta[tt][c] = r.g[j];
+                if constexpr (ER) stb[tt][c] = r.e[j];
+            }
+            if (tid < TB) {
+                sts[tid][1] = r.ga;
+                sts[tid][2] = r.bt;
+            }
+        };
+        // one wave per token, two columns per lane (c = lane, lane + 64)
+        auto prep = [&](int nt) {
+            for (int tt = wave; tt < nt; tt += WAVES) {
+                float qx[2], kx[2], qss = 0.f, kss = 0.f, qk = 0.f;
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    qx[x] = stq[tt][lane + 64 * x];
+                    kx[x] = stk[tt][lane + 64 * x];
+                    qss = fmaf(qx[x], qx[x], qss);
+                    kss = fmaf(kx[x], kx[x], kss);
+                    qk = fmaf(qx[x], kx[x], qk);
                 }
 #pragma unroll
-                for (int g = 0; g < G; ++g) vi[g] = stv[tt][wrow0 + g * 4 + r4];
-                token(t0 + tt, qv, kv, vi, sts[tt][0], sts[tt][1], gk, er);
+                for (int o2 = 32; o2 > 0; o2 >>= 1) {
+                    qss += __shfl_xor(qss, o2);
+                    kss += __shfl_xor(kss, o2);
+                    qk += __shfl_xor(qk, o2);
+                }
+                float inq = 1.f, ink = 1.f;
+                if (p.qk_l2_norm) {
+                    inq = 1.f / sqrtf(qss + 1e-12f);
+                    ink = 1.f / sqrtf(kss + 1e-12f);
+                }
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int c = lane + 64 * x;
+                    const float kn = kx[x] * ink;
+                    float qn = qx[x] * inq;
+                    if constexpr (VD) {
+                        const float av = expf(sta[tt][c]);
+                        qn *= av;
+                        stb[tt][c] = (ER ? stb[tt][c] : 1.f) * av * kn;
+                        sta[tt][c] = av;
+                    }
+                    stq[tt][c] = qn;
+                    stk[tt][c] = kn;
+                }
+                if (lane == 0) {
+                    sts[tt][0] = qk * inq * ink;
+                    if constexpr (DEC && !VD) sts[tt][1] = expf(sts[tt][1]);
+                }
+            }
+        };
+        for (int64_t t0 = s; t0 < e; t0 += TB) {
+            const int nt = (int)((e - t0) < TB ? (e - t0) : TB);
+            if (t0 != s) load_block(t0, nt, raw);
+            park(raw, nt);
+            lds_barrier();
+            prep(nt);
+            lds_barrier();
+            // two halves of the row groups: every token goes to the first half
+            // while the second half of the state is still arriving; inside a
+            // half, the row groups are independent chains
+            constexpr int GH = G / 2;
+#pragma unroll
+            for (int gh = 0; gh < 2; ++gh) {
+                for (int tt = 0; tt < nt; ++tt) {
+                    const size_t th = (size_t)(t0 + tt) * HV + h;
+                    float qv[C], kv[C], av[C], kb[C];
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        qv[c] = stq[tt][col_of(c)];
+                        kv[c] = stk[tt][col_of(c)];
+                        if constexpr (VD) {
+                            av[c] = sta[tt][col_of(c)];
+                            kb[c] = stb[tt][col_of(c)];
+                        }
+                    }
+                    const float qk = sts[tt][0], a = sts[tt][1], bb = sts[tt][2];
+#pragma unroll
+                    for (int gi = 0; gi < GH; ++gi) {
+                        const int g = gh * GH + gi;
+                        const float vi = stv[tt][wrow0 + g * 4 + r4];
+                        float sv[C];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) { sv[x] = S[g][0][x]; sv[4 + x] = S[g][1][x]; }
+                        float r = 0.f, u = 0.f;
+#pragma unroll
+                        for (int c = 0; c < C; ++c) {
+                            if constexpr (RET) r = fmaf(sv[c], VD ? kb[c] : kv[c], r);
+                            u = fmaf(sv[c], qv[c], u);
+                        }
+                        if constexpr (RET) r = sum16(r);
+                        u = sum16(u);
+                        if constexpr (DEC && !VD) {
+                            r *= a;
+                            u *= a;
+                        }
+                        float cc;
+                        if constexpr (RULE == GATED_DELTA_V2) cc = vi - r;
+                        else if constexpr (BETA) cc = bb * (vi - r);
+                        else cc = vi;
+#pragma unroll
+                        for (int c = 0; c < C; ++c) {
+                            if constexpr (VD) sv[c] = fmaf(av[c], sv[c], cc * kv[c]);
+                            else if constexpr (DEC) sv[c] = fmaf(a, sv[c], cc * kv[c]);
+                            else sv[c] = fmaf(cc, kv[c], sv[c]);
+                        }
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) { S[g][0][x] = sv[x]; S[g][1][x] = sv[4 + x]; }
+                        if (l16 == 0) o[th * DK + wrow0 + g * 4 + r4] = from_f32<TA>(p.scale * (u + qk * cc));
+                    }
+                }
             }
             lds_barrier();  // every wave is done with this block before the next one lands
         }
