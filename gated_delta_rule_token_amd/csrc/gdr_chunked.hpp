@@ -1496,12 +1496,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
         const int tok_bytes = HV * D128 * 2;
         // after the LDS transpose each lane stores 16 bytes (8 rows of a token):
         // TR / 8 lanes per token, so a 32-row tile uses every lane for its 16
-        // tokens and a 16-row tile the first 32 lanes; the others get an offset
-        // past the store's range, which the buffer store drops
-        static_assert(TR == 32 || TR == 16, "the output transpose takes 16- or 32-row tiles");
-        constexpr int LPT = TR / 8;
-        const bool st_live = lane / LPT < 16;
-        const int st_tok = st_live ? lane / LPT : 15, st_q = lane % LPT;
+        // tokens, a 64-row tile every lane twice (tokens 0-7, then 8-15) and a
+        // 16-row tile the first 32 lanes; the others get an offset past the
+        // store's range, which the buffer store drops
+        static_assert(TR == 64 || TR == 32 || TR == 16, "the output transpose takes 16-, 32- or 64-row tiles");
+        constexpr int LPT = TR / 8;                       // lanes per token
+        constexpr int NST = TR == 64 ? 2 : 1;             // stores per lane
+        constexpr int TPS = 16 / NST;                     // tokens per store pass
+        const bool st_live = lane / LPT < TPS;
+        const int st_tok = st_live ? lane / LPT : TPS - 1, st_q = lane % LPT;
         const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
         const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
         // token blocks 0, 1 against tokens 32 .. 63: all zero, not stored; an offset
@@ -1538,7 +1541,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
             TA *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
             const __amdgpu_buffer_rsrc_t ro =
                 __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
-            __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok][8 * st_q]), ro, offO, 0, 0);
+#pragma unroll
+            for (int ps = 0; ps < NST; ++ps)
+                __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok + TPS * ps][8 * st_q]), ro,
+                                                       offO + (uint32_t)(TPS * ps * tok_bytes), 0, 0);
         };
         auto step = [&](int j, Ops &cur) {
             const int bf = j & 1;
@@ -1691,10 +1697,7 @@ static size_t workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int
     return seg_offset(T, B, H, HV, per_key) + segs;
 }
 
-// Row tile of the scan: 16 * NVB rows, NVB = 1 or 2 (measured on MI355X:
-// 64-row tiles halve the per-row operand reads but lengthen each chunk step
-// by 1.7x, which loses on both the single long sequence and the batched
-// prefill).
+// Row tile of the scan: 16 * NVB rows, NVB = 1, 2 or 4 (launch_scans picks).
 template <typename TA, int RULE, int NVB, bool PK>
 static void launch_scan(const Params &p, const int32_t *off, const char *rec, const char *kq, const ScanSeg &sg,
                         hipStream_t s)
@@ -1710,7 +1713,13 @@ static void launch_scan(const Params &p, const int32_t *off, const char *rec, co
 // (measured on MI355X: one 65,536-token sequence x 16 heads 2.65 -> 2.18 ms),
 // while with many pairs the GPU is full and the larger tiles amortise the
 // operand reads (8 x 32 heads: 1.27 ms with 32-row tiles, 1.47 ms with 16-row
-// tiles).  A segmented scan runs pass 1 (carry and transition tiles: twice
+// tiles).  A chunk step is bound by the bytes of its operand reads (W, U,
+// K^T, q and P: ~84 KB per 32-row tile; skipping the reloads of W alone took
+// the varlen scan 479 -> 400 us), and W, K^T, q and P are the same for every
+// row tile of a head, so from 128 pairs on (at least two 64-row workgroups
+// per CU) the single pass takes 64-row tiles: varlen 8 x 32 heads 0.98 ->
+// 0.94 ms, 4 x 32 heads per-key 0.99 -> 0.94 ms; with fewer pairs they leave
+// CUs idle (16 heads in 4 segments: pass 2 398 -> 542 us).  A segmented scan runs pass 1 (carry and transition tiles: twice
 // the workgroups of pass 2) in 32-row tiles and pass 2 by the same rule as a
 // single pass over its (request, head, segment) groups: two workgroups of
 // this kernel on one CU share its vector-memory pipeline and each chunk step
@@ -1724,7 +1733,8 @@ static void launch_scans(const Params &p, const int32_t *off, const char *rec, c
     if (nseg <= 1) {
         const ScanSeg one{1, 0, nullptr};
         if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, one, s);
-        else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, one, s);
+        else if (pairs < 128) launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, one, s);
+        else launch_scan<TA, RULE, 4, PK>(p, off, rec, kq, one, s);
         return;
     }
     launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs}, s);

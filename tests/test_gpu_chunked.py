@@ -141,6 +141,21 @@ def test_chunked_resume_split(split):
     assert_close(sb, rs, TOL_CHUNKED, "resumed at %d: state" % split)
 
 
+@pytest.mark.parametrize("rule,per_key", [("gated_delta", False), ("gated_delta_v2", True)],
+                         ids=["per_head", "per_key_form"])
+def test_chunked_wide_tiles(rule, per_key):
+    """128 (request, head) pairs or more take 64-row state tiles in the scan
+    (and two 16-byte output stores per lane): ragged chunk tails, an empty
+    request and grouped heads on that path."""
+    kw = dict(update_rule=rule, per_key=per_key, gate_activation="none", beta_activation="none") if per_key else {}
+    case = _case(45 + per_key, [150, 0, 70, 200], H=16, HV=64, **kw)  # 4 x 64 = 256 pairs
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "64-row tiles o")
+    assert_close(st, rs, TOL_CHUNKED, "64-row tiles state")
+    assert np.array_equal(st[1], case["initial_state"][1].astype(np.float64)), "empty request copies its state"
+
+
 # ------------------------------------------------------------------ state magnitude
 @pytest.mark.parametrize("magnitude", [1e4, 1e-5])
 @pytest.mark.parametrize("rule", ["gated_delta", "gated"])
