@@ -178,6 +178,29 @@ __device__ __forceinline__ int sw_tok(int row, int tok) { return (((tok >> 3) ^ 
 // subnormals (inputs of size 1e-5 lost most of their digits unscaled).  Each
 // scan unit takes max |v| over its own chunks (post_vmax) and max |S0| over
 // its own tile, so units need not agree.
+// Magnitude past which an fp32 operand is not split into fp16 (hi, lo): the
+// hi part would round to infinity at 65520; the margin keeps the sums of the
+// products that follow finite as well.
+constexpr float SPLIT_LIMIT = 60000.f;
+
+// Largest magnitude, as the bits of |x| (so that inf and NaN rank above every
+// finite value), of the fp32 values one thread splits into fp16 (hi, lo).
+struct SplitWatch {
+    uint32_t big = 0u;
+    __device__ __forceinline__ void note(float x) { big = max(big, __float_as_uint(x) & 0x7FFFFFFFu); }
+    __device__ __forceinline__ void note(f4v x)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) note(x[i]);
+    }
+    __device__ __forceinline__ void note(const float (&x)[8])
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) note(x[i]);
+    }
+    __device__ __forceinline__ bool over() const { return big >= __float_as_uint(SPLIT_LIMIT); }
+};
+
 __device__ __forceinline__ int tile_exponent(float m)
 {
     if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;  // zero, or not finite
@@ -213,6 +236,7 @@ struct ScanSeg {
     int nseg;
     int pass;
     float *xs;
+    float *stage;  // in-place state (slab, or final == initial): final states go here first, else nullptr
 };
 enum SegMode : int { SEG_REAL = 0, SEG_CARRY = 1, SEG_TRANS = 2 };
 __host__ __device__ constexpr int seg_slots(int nseg) { return 3 * nseg; }
@@ -299,7 +323,7 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
 template <int RULE>
-__global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int32_t *__restrict__ off,
+__global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *__restrict__ off,
                                                    char *__restrict__ ws, char *__restrict__ kqs)
 {
     constexpr bool DEC = rule_decays(RULE);
@@ -335,6 +359,13 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
     // K^T and q once per (chunk, q/k head): the group's first value head writes them
     char *kq = kqs + ((size_t)ci * H + qh) * KQ::SIZE;
     const bool kq_writer = h % (HV / H) == 0;
+    // A split operand past the fp16 range hands the pair to the recurrent
+    // kernel.  Each phase watches its own operands and posts at its end, so no
+    // register stays live across the phases.
+    int32_t *const flag = off + p.B + 1 + (size_t)b * HV + h;
+    auto post = [&](const SplitWatch &w) {
+        if (w.over()) *flag = 2;
+    };
 
     const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
     const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
@@ -451,6 +482,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
         }
         lds_barrier();  // Q is dead: A takes its rows
         const int t = 16 * tb + lr;
+        SplitWatch wp;
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             const int s0 = 16 * sb + 4 * lq;
@@ -463,6 +495,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
                 av[i] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
             }
             h4 hi, lo;
+            wp.note(pv);
             split4(pv, hi, lo);
             // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane; the
             // fragments of token blocks 0, 1 against tokens 32 .. 63 are all zero
@@ -474,6 +507,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
             }
             if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
         }
+        post(wp);
     }
     lds_barrier();
 
@@ -498,6 +532,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
         // past t are read later, row t never again); zeros above the diagonal.
         if (wave == 0) {
             float x[CH];
+            SplitWatch wt;  // column `lane` of T
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
                 float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
@@ -505,7 +540,12 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
                 for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
                 x[t] = (r[0] + r[1]) + (r[2] + r[3]);
                 sA[t][lane] = x[t];
+                wt.note(x[t]);
             }
+            // the column times its weight (split beside T below) peaks where
+            // |T| does: rounding is monotone
+            wt.note(__uint_as_float(wt.big) * sBeta[lane]);
+            post(wt);
         }
         lds_barrier();  // T is complete
         // Wave w forms key columns and value rows 32 w .. 32 w + 31 on the matrix
@@ -513,6 +553,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
         // or value column; W's right-hand side is fp32 and gets (hi, lo) fp16
         // planes, V is exact in fp16.
         h8 bwh[2][2], bwl[2][2], bv[2][2];  // [column block c][token step ks]
+        SplitWatch wx, wa;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -524,8 +565,10 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
                     xw[x] = sRw[s0 + x] * (float)sK[s0 + x][cc];
                     bv[c][ks][x] = sV[s0 + x][cc];
                 }
+                wx.note(xw);
                 split8(xw, bwh[c][ks], bwl[c][ks]);
             }
+        post(wx);
         f4v accW[4][2], accU[4][2];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -574,11 +617,13 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, const int
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 h4 hi, lo;
+                wa.note(accW[mb][c]);
                 split4(accW[mb][c], hi, lo);
                 const int key = sw_key(lr, 16 * (2 * wave + c) + 4 * lq);
                 *reinterpret_cast<h4 *>(&sW[0][16 * mb + lr][key]) = hi;
                 *reinterpret_cast<h4 *>(&sW[1][16 * mb + lr][key]) = lo;
             }
+        post(wa);
         lds_barrier();
         // W fragments: f = block * 64 + lane, block = (tb * 4 + kk) * 2 + plane
 #pragma unroll
@@ -626,7 +671,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename TA, int RULE, bool PKG>
-__global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const int32_t *__restrict__ off,
+__global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_t *__restrict__ off,
                                                           char *__restrict__ ws)
 {
     using RC = Rec<true>;
@@ -671,6 +716,13 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     const int lr = lane & 15, lq = lane >> 4;
     const int col = tid & (D128 - 1);
     char *rec = ws + ((size_t)ci * HV + h) * RC::SIZE;
+    // A split operand past the fp16 range hands the pair to the recurrent
+    // kernel.  Each phase watches its own operands and posts at its end, so no
+    // register stays live across the phases.
+    int32_t *const flag = off + p.B + 1 + (size_t)b * HV + h;
+    auto post = [&](const SplitWatch &w) {
+        if (w.over()) *flag = 2;
+    };
     const TA *__restrict__ q = static_cast<const TA *>(p.q);
     const TA *__restrict__ k = static_cast<const TA *>(p.k);
     const TA *__restrict__ v = static_cast<const TA *>(p.v);
@@ -816,6 +868,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     lds_barrier();
 
     // ---- operands built from G: Kd^T and Qg fragments (4 + 4 per thread), gamma_C
+    SplitWatch wg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // Kd^T: key j, tokens 32 ks + 8 l4 .. +7
@@ -828,6 +881,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             x8[x] = (float)sK[u][j] * sIk[u] * (PKG ? ex2(gc - sG[u][j]) : sFk[u]);
         }
         h8 hi, lo;
+        wg.note(x8);
         split8(x8, hi, lo);
         char *dst = rec + RC::KT + ((uint32_t)(((j >> 4) * 2 + ks) * 2) * 64 + l4 * 16 + (j & 15)) * 16;
         *reinterpret_cast<h8 *>(dst) = hi;
@@ -843,11 +897,13 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
         for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * (PKG ? ex2(sG[t][key + x]) : sFq[t]);
         h8 hi, lo;
+        wg.note(x8);
         split8(x8, hi, lo);
         char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
         *reinterpret_cast<h8 *>(dst) = hi;
         *reinterpret_cast<h8 *>(dst + 1024) = lo;
     }
+    post(wg);
     if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
 
     // erase gate at this lane's right-hand-side fragment positions of W
@@ -971,6 +1027,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
     // fp32 values, so (hi, lo) fp16 planes
     h8 bwh[2][2], bwl[2][2];
     if constexpr (RET) {
+        SplitWatch wx;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -982,8 +1039,10 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                     const int u = s0 + x;
                     xw[x] = (V2 ? ev[c][ks][x] : sWt[u]) * sIk[u] * to_f32(sK[u][j]) * (PKG ? ex2(sG[u][j]) : sFq[u]);
                 }
+                wx.note(xw);
                 split8(xw, bwh[c][ks], bwl[c][ks]);
             }
+        post(wx);
     }
     lds_barrier();  // K, Q and G are dead: V takes K's rows, A takes Q's, W's right-hand side G's
 
@@ -1006,6 +1065,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 sBw[((1 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane] = bwl[c][ks];
             }
     }
+    SplitWatch wp;
 #pragma unroll
     for (int slot = 0; slot < 3; ++slot) {
         const int pi = wave + 4 * slot;
@@ -1021,6 +1081,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 av[i] = s < t ? at * sIk[s] * resA[slot][i] : 0.f;
             }
             h4 hi, lo;
+            wp.note(pv);
             split4(pv, hi, lo);
             const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
             *reinterpret_cast<h4 *>(rec + po) = hi;
@@ -1028,6 +1089,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
             if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
         }
     }
+    post(wp);
     if (wave < 2) {
         // the P blocks above the diagonal are zero (the scan multiplies them
         // anyway); only the two that share a fragment with nonzero blocks are
@@ -1062,6 +1124,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
         // (hi, lo) planes for bf16).
         if (wave == 0) {
             float x[CH];
+            SplitWatch wt;  // column `lane` of T
 #pragma unroll
             for (int t = 0; t < CH; ++t) {
                 float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
@@ -1069,7 +1132,12 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
                 x[t] = (r[0] + r[1]) + (r[2] + r[3]);
                 sA[t][lane] = x[t];
+                wt.note(x[t]);
             }
+            // the column times its weight (split beside T below) peaks where
+            // |T| does: rounding is monotone
+            wt.note(__uint_as_float(wt.big) * sWt[lane]);
+            post(wt);
         }
         lds_barrier();  // T is complete
         constexpr bool VX = sizeof(TA) == 2 && !__is_same(TA, bf16_t);  // V exact in fp16
@@ -1081,6 +1149,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 bwl[c][ks] = sBw[((1 * 4 + wave) * 4 + c * 2 + ks) * 64 + lane];
             }
         h8 bvh[2][2], bvl[2][2];
+        SplitWatch wv, wa;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -1089,8 +1158,10 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
                 float xv[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) xv[x] = to_f32(sK[s0 + x][cc]);
+                wv.note(xv);
                 split8(xv, bvh[c][ks], bvl[c][ks]);
             }
+        post(wv);
         f4v accW[4][2], accU[4][2];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -1136,11 +1207,13 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 h4 hi, lo;
+                wa.note(accW[mb][c]);
                 split4(accW[mb][c], hi, lo);
                 const int key = sw_key(lr, 16 * (2 * wave + c) + 4 * lq);
                 *reinterpret_cast<h4 *>(&sW[0][16 * mb + lr][key]) = hi;
                 *reinterpret_cast<h4 *>(&sW[1][16 * mb + lr][key]) = lo;
             }
+        post(wa);
         lds_barrier();
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
@@ -1184,7 +1257,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, const 
 // runs segments 1 .. nseg-1 for real from those starts.  The longest serial
 // chain shrinks from n chunk steps to about 2 n / nseg.
 template <typename TA, int RULE, int NVB, bool PK>
-__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_t *off, const char *ws, const char *kqs,
+__global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off, const char *ws, const char *kqs,
                                                    const ScanSeg sg)
 {
     using RC = Rec<PK>;
@@ -1230,12 +1303,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
     const int ns = sg.pass == 0 ? 1 : sg.nseg;
     const int cb = (int)((int64_t)seg * nch / ns), ce = (int)((int64_t)(seg + 1) * nch / ns);
     const float *from = src;
-    float *to = dst;
+    // an in-place final state is staged (the commit kernel copies it back unless
+    // the pair is handed to the recurrent kernel, which then reads the intact state)
+    float *const fin = sg.stage ? sg.stage + (size_t)bh * (D128 * D128) : dst;
+    float *to = fin;
     if (sg.pass != 0) {
         float *xs = sg.xs + (size_t)bh * seg_slots(ns) * (D128 * D128);
         if (mode == SEG_REAL) {
             from = seg == 0 ? src : xs + (size_t)seg_start(seg) * (D128 * D128);
-            to = seg == ns - 1 ? dst : seg == 0 ? xs + (size_t)seg_start(1) * (D128 * D128) : nullptr;
+            to = seg == ns - 1 ? fin : seg == 0 ? xs + (size_t)seg_start(1) * (D128 * D128) : nullptr;
         } else {
             from = nullptr;
             to = xs + (size_t)(mode == SEG_CARRY ? seg_carry(ns, seg) : seg_trans(ns, seg)) * (D128 * D128);
@@ -1310,6 +1386,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
             for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= up;
         const float um = mode == SEG_TRANS ? 0.f : up;  // a transition tile leaves U out
+        SplitWatch sw;
         struct Ops {
             h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
             h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
@@ -1364,6 +1441,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
                 for (int rt = 0; rt < NVB; ++rt) {
                     h4 hi, lo;
+                    sw.note(Sc[a][rt]);
                     split4(Sc[a][rt], hi, lo);
                     *reinterpret_cast<h4 *>(&sS[bf][0][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = hi;
                     *reinterpret_cast<h4 *>(&sS[bf][1][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = lo;
@@ -1411,12 +1489,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
                 h4 dh, dl;
+                sw.note(dv[vb]);
                 split4(dv[vb], dh, dl);
                 const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
                 *reinterpret_cast<h4 *>(&sDt[bf][0][r][sw_tok(lr, c)]) = dh;
                 *reinterpret_cast<h4 *>(&sDt[bf][1][r][sw_tok(lr, c)]) = dl;
                 if constexpr (!PK) {
                     h4 sh, sl;
+                    sw.note(dsv[vb]);
                     split4(dsv[vb], sh, sl);
                     *reinterpret_cast<h4 *>(&sDs[0][r][sw_tok(lr, c)]) = sh;
                     *reinterpret_cast<h4 *>(&sDs[1][r][sw_tok(lr, c)]) = sl;
@@ -1473,6 +1553,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, const int32_
                 for (int rt = 0; rt < NVB; ++rt)
                     *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt] * down;
         }
+        // A split operand at or past SPLIT_LIMIT (or not finite) leaves the fp16
+        // range of its hi part: the pair goes to the recurrent kernel, which
+        // recomputes it in fp32 (its o rows and its final state).
+        if (sw.over()) off[p.B + 1 + bh] = 2;
     } else if (mode != SEG_REAL) {
         // carry and transition tiles write no output: these waves only keep
         // the chain's barriers (one at the start, two per chunk step)
@@ -1671,6 +1755,23 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const int32
     }
 }
 
+// ------------------------------------------------------------------ commit
+// In-place states (a slab, or final == initial): copy each pair's staged final
+// state to its place unless the pair went to the recurrent kernel (which
+// wrote it from the intact incoming state).  One workgroup per pair.
+__global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int32_t *off, const float *stage)
+{
+    const int64_t bh = blockIdx.x;
+    if (bh >= (int64_t)p.B * p.HV || off[p.B + 1 + bh]) return;
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, (int)(bh / p.HV), (int)(bh % p.HV), src, dst)) return;
+    const f4v *from = reinterpret_cast<const f4v *>(stage + (size_t)bh * (D128 * D128));
+    f4v *to = reinterpret_cast<f4v *>(dst);
+#pragma unroll 4
+    for (int i = threadIdx.x; i < D128 * D128 / 4; i += 256) to[i] = from[i];
+}
+
 // ------------------------------------------------------------------ host side
 
 // Workspace: chunk table (off[B + 1], then the (B * HV) hand-over flags) |
@@ -1691,15 +1792,21 @@ static size_t seg_offset(int64_t T, int B, int H, int HV, bool per_key)
     return kq_offset(T, B, HV, per_key) + (per_key ? 0 : ((size_t)maxch * H * KQ::SIZE + 255) / 256 * 256);
 }
 
-static size_t workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int nseg)
+static size_t stage_offset(int64_t T, int B, int H, int HV, bool per_key, int nseg)
 {
     const size_t segs = nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0;
     return seg_offset(T, B, H, HV, per_key) + segs;
 }
 
+// ... | staging for in-place final states (one 128 x 128 fp32 state per pair)
+static size_t workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int nseg)
+{
+    return stage_offset(T, B, H, HV, per_key, nseg) + (size_t)B * HV * D128 * D128 * 4;
+}
+
 // Row tile of the scan: 16 * NVB rows, NVB = 1, 2 or 4 (launch_scans picks).
 template <typename TA, int RULE, int NVB, bool PK>
-static void launch_scan(const Params &p, const int32_t *off, const char *rec, const char *kq, const ScanSeg &sg,
+static void launch_scan(const Params &p, int32_t *off, const char *rec, const char *kq, const ScanSeg &sg,
                         hipStream_t s)
 {
     constexpr int NTILE = D128 / (16 * NVB);
@@ -1726,24 +1833,24 @@ static void launch_scan(const Params &p, const int32_t *off, const char *rec, co
 // then takes about twice as long (measured on MI355X, 65,536 tokens x 16
 // heads in 3 segments: 1.82 ms with 32-row pass-1 tiles, 1.89 ms with 16-row).
 template <typename TA, int RULE, bool PK>
-static void launch_scans(const Params &p, const int32_t *off, const char *rec, const char *kq, float *xs, int nseg,
-                         hipStream_t s)
+static void launch_scans(const Params &p, int32_t *off, const char *rec, const char *kq, float *xs, float *stage,
+                         int nseg, hipStream_t s)
 {
     const int64_t pairs = (int64_t)p.B * p.HV;
     if (nseg <= 1) {
-        const ScanSeg one{1, 0, nullptr};
+        const ScanSeg one{1, 0, nullptr, stage};
         if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, one, s);
         else if (pairs < 128) launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, one, s);
         else launch_scan<TA, RULE, 4, PK>(p, off, rec, kq, one, s);
         return;
     }
-    launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs}, s);
+    launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
     if (nseg > 2) {
         const int64_t blocks = pairs * 8;
-        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, off, ScanSeg{nseg, 0, xs});
+        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, off, ScanSeg{nseg, 0, xs, stage});
     }
-    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
-    else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs}, s);
+    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
+    else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
 }
 
 // PK: the per-key record and kernels; PKG: the gate itself is per key (else
@@ -1759,6 +1866,9 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
     char *rec = base + table_bytes(p.B, p.HV);
     char *kq = base + kq_offset(p.T, p.B, p.HV, PK);
     float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.H, p.HV, PK));
+    // the incoming state is overwritten in place: stage the final states
+    const bool in_place = p.num_slots > 0 || (p.init != nullptr && p.init == p.state);
+    float *stage = in_place ? reinterpret_cast<float *>(base + stage_offset(p.T, p.B, p.H, p.HV, PK, nseg)) : nullptr;
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off, redo);
     if (maxch * p.HV > 0) {
         if constexpr (PK)
@@ -1766,18 +1876,20 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
         else
             hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec, kq);
     }
-    launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, nseg, s);
+    launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, stage, nseg, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // Requests whose ranges overlap an earlier one's (a decreasing cu_seqlens
-    // entry) may be left out of the chunk budget; the recurrent kernel runs
-    // exactly those pairs.  Uniform packing never overlaps.
-    if (p.cu_seqlens) {
-        Params r = p;
-        r.run_only = redo;
-        return launch_recurrent(r, RULE, PKG, std::is_same<TA, bf16_t>::value ? 2 : 1, D128, 2, s);
-    }
-    return hipSuccess;
+    // The recurrent kernel runs exactly the flagged pairs: requests the chunk
+    // plan left out (ranges that overlap after a decreasing cu_seqlens entry)
+    // and pairs whose split operands left the fp16 range.  With no flag set
+    // its workgroups return at once.
+    Params r = p;
+    r.run_only = redo;
+    err = launch_recurrent(r, RULE, PKG, std::is_same<TA, bf16_t>::value ? 2 : 1, D128, 2, s);
+    if (err != hipSuccess) return err;
+    if (stage && p.B * p.HV > 0)
+        hipLaunchKernelGGL(k_chunk_commit, dim3((unsigned)(p.B * p.HV)), dim3(256), 0, s, p, off, stage);
+    return hipGetLastError();
 }
 
 }  // namespace GDR_CHUNK_NS

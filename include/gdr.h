@@ -132,13 +132,15 @@ typedef enum {
                               * into an fp16 (hi, lo) pair.  Each state tile runs scaled
                               * by a power of two that brings the larger of max |v| over
                               * its chunks and max |S0| of the tile to [4, 8), so inputs
-                              * of any overall size keep ~22 bits; a state that grows
-                              * past about 8000 times that size (gated or linear rules
-                              * over very long requests with aligned keys) leaves the
-                              * fp16 range and the result is not finite.  Requests whose
-                              * cu_seqlens ranges overlap an earlier request's beyond the
-                              * chunk budget run on the recurrent kernel.  Use
-                              * GDR_ALGO_RECURRENT (all fp32) for such growth. */
+                              * of any overall size keep ~22 bits.  A (request, head)
+                              * pair whose split operands reach 60000 (a state grown
+                              * about 8000 times past that size, or inputs such as
+                              * unnormalised keys that push the chunk's own operands
+                              * there) is recomputed on the recurrent kernel in fp32, as
+                              * are requests whose cu_seqlens ranges overlap an earlier
+                              * request's beyond the chunk budget.  In-place final states
+                              * (a slab, or final == initial) are staged in the workspace
+                              * and copied back for the pairs not recomputed. */
 } gdr_algo;
 
 typedef struct {

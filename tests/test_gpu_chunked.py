@@ -180,6 +180,77 @@ def test_chunked_state_magnitude(magnitude, rule):
     assert np.all(np.isfinite(o)) and worst <= bound
 
 
+# ------------------------------------------------------------------ operands past the fp16 range
+GROWTH = [("plain", None, 1, 16384), ("slab", (5,), 1, 16384), ("segmented", None, 2, 32768)]
+
+
+@pytest.mark.parametrize("name,slots,segs,T0", GROWTH, ids=[g[0] for g in GROWTH])
+def test_chunked_state_growth_hand_over(name, slots, segs, T0):
+    """A state that grows past what the scan's fp16 (hi, lo) operands hold: the
+    linear rule (README, update rules: no decay, no erase) with one key
+    repeated for T0 tokens and v = 1 builds a state column of T0 times the
+    value, 2^14 times max |v| or more (with two segments, each segment's own
+    carry grows that far).  The scan flags those (request, head) pairs and the
+    recurrent kernel recomputes them in fp32; the second request stays on the
+    chunked path.  In slab mode the final states of the unflagged pairs go
+    through the staging area and the flagged ones are recomputed from the
+    intact slab."""
+    case = _case(47, [T0, 300], update_rule="linear", gate_activation="none", beta_activation="none",
+                 slots=slots)
+    key = np.zeros(128, np.float16)
+    key[5] = 1.0
+    case["k"][:T0] = key
+    case["v"][:T0] = np.float16(1.0)
+    say("case state growth %s segments=%d" % (name, segs))
+    o, st = gpu_forward(case, "chunked", scan_segments=segs)
+    ro, rs = oracle_forward(case)
+    assert float(np.max(np.abs(rs))) > 16000.0, "the state reaches the intended size"
+    if slots is not None:
+        st = st[case["slot_ids"]]
+        rs = rs[case["slot_ids"]]
+    assert_close(o[:T0], ro[:T0], TOL_CHUNKED, "%s grown request o" % name)
+    assert_close(st[0], rs[0], TOL_CHUNKED, "%s grown request state" % name)
+    assert_close(o[T0:], ro[T0:], TOL_CHUNKED, "%s chunked request o" % name)
+    assert_close(st[1], rs[1], TOL_CHUNKED, "%s chunked request state" % name)
+
+
+PROLOGUE = ["per_head_scores", "per_key_bf16_values"]
+
+
+@pytest.mark.parametrize("form", PROLOGUE)
+def test_chunked_prologue_hand_over(form):
+    """Operands the prologue splits into fp16 (hi, lo) past the fp16 range:
+    scores scale q.k of unnormalised keys near 1e5 (per-head form, gated
+    rule), and bf16 values near 5e5 (per-key form, Gated DeltaNet-2 rule).
+    The prologue flags the request's pairs and the recurrent kernel computes
+    them; the other request stays on the chunked path."""
+    T0 = 400
+    if form == "per_head_scores":
+        case = _case(48, [T0, 200], update_rule="gated", gate_activation="none", beta_activation="none",
+                     qk_l2_norm=0)
+        rng = np.random.default_rng(48)
+        for hq in range(2):
+            u = rng.standard_normal(128)
+            u = 1000.0 * u / np.linalg.norm(u)
+            case["q"][:T0, hq] = u.astype(np.float16)
+            case["k"][:T0, hq] = u.astype(np.float16)
+        case["v"][:T0] = (case["v"][:T0].astype(np.float32) * np.float32(1e-3)).astype(np.float16)
+        assert float((case["scale"] or 128 ** -0.5) * 1000.0 ** 2) > 65504.0
+    else:
+        case = _case(49, [T0, 200], dtype="bf16", update_rule="gated_delta_v2", per_key=True,
+                     gate_activation="none", beta_activation="none")
+        case["v"][:T0] = case["v"][:T0] * np.float32(2.0 ** 17)  # stays on the bf16 grid
+        assert float(np.max(np.abs(case["v"][:T0]))) > 65504.0
+    say("case prologue hand-over %s" % form)
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    ro, rs = oracle_forward(case)
+    tol_o = TOL_BF16_O if case["act_dtype"] == "bf16" else TOL_CHUNKED
+    assert_close(o[:T0], ro[:T0], tol_o, "%s flagged request o" % form)
+    assert_close(st[0], rs[0], TOL_CHUNKED, "%s flagged request state" % form)
+    assert_close(o[T0:], ro[T0:], tol_o, "%s chunked request o" % form)
+    assert_close(st[1], rs[1], TOL_CHUNKED, "%s chunked request state" % form)
+
+
 # ------------------------------------------------------------------ the workloads, every pair
 FULL = [("varlen_prefill", lambda: workloads.varlen_prefill()),
         ("long_prefill", lambda: workloads.long_prefill()),
