@@ -100,6 +100,27 @@ struct Rec {
 };
 constexpr uint32_t R_W = Rec<false>::W, R_U = Rec<false>::U, R_P = Rec<false>::P, R_SC = Rec<false>::SC,
                    WS_REC = Rec<false>::SIZE;
+
+// Record of one (chunk, value head) in the T form (per-head decay, fp16
+// activations): the scan forms W S^T and U itself as T (beta V - w K S^T)
+// from the raw k and v rows, so the record holds only what needs the whole
+// chunk at once:
+//   T   T = (I + A)^-1 (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr,
+//       tokens 32 ks + 8 lq .. +7 (blocks tb < 2, ks = 1 lie above the diagonal: not stored)
+//   P   as in Rec<false>
+//   SC  fp32: kd[64], gq[64], gamma_C, max |v| at SC_VMAX, beta[64] at SCT_BETA,
+//       w[64] at SCT_RW (w = beta gamma / |k|, the row weight of K in W)
+// plus, once per (chunk, q/k head), K^T in fragment order as KQ::KT below
+// (16 KB: the state update's left operand, which the k rows give only
+// through a transpose).
+struct RecT {
+    static constexpr uint32_t T = 0;
+    static constexpr uint32_t P = 16 * 1024;
+    static constexpr uint32_t SC = 32 * 1024;
+    static constexpr uint32_t SIZE = SC + 1536;
+    static constexpr uint32_t KT_SIZE = 16 * 1024;
+};
+constexpr int SCT_BETA = 256, SCT_RW = 320;
 struct KQ {
     static constexpr uint32_t KT = 0, Q = 16 * 1024, SIZE = 32 * 1024;
 };
@@ -322,7 +343,9 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // ------------------------------------------------------------------ phase 1
 // 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
-template <int RULE>
+// TF: the T form (RecT: T, P and the scalars; no W, U, K^T or q), else Rec<false>
+// plus the K^T and q area.
+template <int RULE, bool TF>
 __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *__restrict__ off,
                                                    char *__restrict__ ws, char *__restrict__ kqs)
 {
@@ -355,9 +378,10 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
     const int qh = (int)(((int64_t)h * H) / HV);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
-    char *rec = ws + ((size_t)ci * HV + h) * WS_REC;
+    constexpr uint32_t OP = TF ? RecT::P : R_P, OSC = TF ? RecT::SC : R_SC;
+    char *rec = ws + ((size_t)ci * HV + h) * (TF ? RecT::SIZE : WS_REC);
     // K^T and q once per (chunk, q/k head): the group's first value head writes them
-    char *kq = kqs + ((size_t)ci * H + qh) * KQ::SIZE;
+    char *kq = kqs + ((size_t)ci * H + qh) * (TF ? RecT::KT_SIZE : KQ::SIZE);
     const bool kq_writer = h % (HV / H) == 0;
     // A split operand past the fp16 range hands the pair to the recurrent
     // kernel.  Each phase watches its own operands and posts at its end, so no
@@ -407,12 +431,12 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
         const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
         *reinterpret_cast<h8 *>(&sK[r][c8]) = ldk[i];
         *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
-        *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
+        if constexpr (!TF) *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
         // q in fragment order for the scan's output waves (rows past the end are zero)
-        if (kq_writer)
+        if (!TF && kq_writer)
             *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
-    post_vmax(ldv, rec + R_SC);
+    post_vmax(ldv, rec + OSC);
     lds_barrier();
 
     // ---- K^T fragments (key 16 mt + lr, tokens 32 ks + 8 lq .. +7); fragment f = block * 64 + lane
@@ -457,10 +481,14 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
         const int t = tid;
         const float gl = sG[n - 1];
         sRw[t] = sBeta[t] * expf(sG[t]) * sIk[t];  // row scale of K in W's right-hand side
-        float *sc = reinterpret_cast<float *>(rec + R_SC);
+        float *sc = reinterpret_cast<float *>(rec + OSC);
         sc[t] = t < n ? expf(gl - sG[t]) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
         sc[CH + t] = scale * sIq[t] * expf(sG[t]);        // gq: read-out weight of the incoming state
         if (t == 0) sc[2 * CH] = DEC ? expf(gl) : 1.f;    // gamma_C
+        if constexpr (TF) {
+            sc[SCT_BETA + t] = sBeta[t];  // zero past the request's end, like w
+            sc[SCT_RW + t] = sRw[t];
+        }
     }
 
     // ---- K Q^T and K K^T, 16 x 16 tiles (wave = token block tb, tiles sb <= tb);
@@ -500,7 +528,7 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
             // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane; the
             // fragments of token blocks 0, 1 against tokens 32 .. 63 are all zero
             // and are not stored (the scan reads zero past the record instead)
-            const uint32_t po = R_P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            const uint32_t po = OP + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
             if (tb >= 2 || sb < 2) {
                 *reinterpret_cast<h4 *>(rec + po) = hi;
                 *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
@@ -513,8 +541,9 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
 
     if constexpr (!RET) {
         // no retrieval: U = V, stored in fragment order by the row-column threads
+        // (the T form reads v itself)
         const int col = tid & (D128 - 1);
-        if (tid >= D128) {
+        if (!TF && tid >= D128) {
 #pragma unroll
             for (int qd = 0; qd < CH / 4; ++qd) {
                 f4v u;
@@ -548,6 +577,33 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
             post(wt);
         }
         lds_barrier();  // T is complete
+        if constexpr (TF) {
+            // T fragments (hi, lo) in the order the scan's chain waves load them:
+            // blocks (tb, ks) on or below the diagonal, 64 fragments of 8 tokens each
+            SplitWatch wtf;
+            for (int it = tid; it < 6 * 64; it += 256) {
+                const int blk = it >> 6, fl = it & 63;
+                // (tb, ks) = (0, 0) (1, 0) (2, 0) (2, 1) (3, 0) (3, 1)
+                const int tb = blk < 2 ? blk : 2 + ((blk - 2) >> 1), ks = blk < 2 ? 0 : (blk - 2) & 1;
+                const int t = 16 * tb + (fl & 15), s0 = 32 * ks + 8 * (fl >> 4);
+                const f4v a0 = *reinterpret_cast<const f4v *>(&sA[t][s0]);
+                const f4v a1 = *reinterpret_cast<const f4v *>(&sA[t][s0 + 4]);
+                float x8[8];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    x8[x] = a0[x];
+                    x8[4 + x] = a1[x];
+                }
+                wtf.note(x8);
+                h8 hi, lo;
+                split8(x8, hi, lo);
+                char *dst = rec + RecT::T + (uint32_t)((tb * 2 + ks) * 2) * 1024 + (uint32_t)fl * 16;
+                *reinterpret_cast<h8 *>(dst) = hi;
+                *reinterpret_cast<h8 *>(dst + 1024) = lo;
+            }
+            post(wtf);
+            return;
+        }
         // Wave w forms key columns and value rows 32 w .. 32 w + 31 on the matrix
         // cores.  Right-hand-side fragments hold 8 consecutive tokens of one key
         // or value column; W's right-hand side is fp32 and gets (hi, lo) fp16
@@ -1711,6 +1767,472 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
     }
 }
 
+// ------------------------------------------------------------------ phase 2, T form
+// Per-head decay, fp16 activations.  The chain forms the chunk's value
+// updates from the raw rows instead of loading W and U: with the key rows
+// against the incoming state, Y = K S^T, and Z = diag(beta) V - diag(w) Y,
+//   D = U - W S^T = T Z,
+// since U = T diag(beta) V and W = T diag(w) K (w = beta gamma / |k|).  The
+// record holds T, P and the per-token scalars, the (chunk, q/k head) area
+// K^T; k, v and q are read from the activations.  A chunk step
+// has three barriers: the state tile is in LDS (1), Z is (1.5, retrieving
+// rules only), D is (2).  Workgroup layout, segments, tile scaling and the
+// output path follow k_chunk_scan.
+template <int RULE, int NVB>
+__global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *off, const char *ws, const char *kts,
+                                                     const ScanSeg sg)
+{
+    constexpr bool RET = rule_retrieves(RULE);
+    constexpr int TR = 16 * NVB;          // state rows of this workgroup
+    constexpr int NTILE = D128 / TR;      // workgroups per head
+    // [hi, lo][row][key]: one buffer suffices, since every read of chunk j's
+    // planes (B1, O1) precedes barrier 1.5 (or 2), which precedes their rewrite
+    __shared__ __align__(16) half_t sS[2][TR][D128];
+    __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token]: D^T of chunk j in j & 1, Z^T in the other
+    __shared__ __align__(16) half_t sDs[2][TR][CH];      // [hi, lo][row][token] (kd D)^T
+    __shared__ __align__(16) half_t sO[4][16][TR + 8];   // per output wave: [token][row] staging for the store
+    __shared__ float sTM[4][2];                           // per chain wave: max |S0| of its part, max |v|
+
+    const int HV = p.HV;
+    const int NU = (sg.pass == 1 ? 2 : 1) * NTILE;
+    const int nsg = sg.pass == 0 ? 1 : sg.nseg - 1;
+    const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
+    const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
+    if (gi >= (int64_t)p.B * HV * nsg) return;
+    const int bh = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    const int tile = unit % NTILE;
+    const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
+    if (mode == SEG_TRANS && seg == 0) return;
+    const int b = bh / HV, h = bh % HV;
+    if (off[p.B + 1 + bh]) return;  // the recurrent kernel takes this pair
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
+    const int row0 = tile * TR;
+    const uint32_t l16 = (uint32_t)lane * 16;
+
+    const float *src;
+    float *dst;
+    if (!state_ptrs(p, b, h, src, dst)) return;
+    int64_t rs, re;
+    request_range(p, b, rs, re);
+    const int c0 = off[b], nch = off[b + 1] - off[b];
+    const int ns = sg.pass == 0 ? 1 : sg.nseg;
+    const int cb = (int)((int64_t)seg * nch / ns), ce = (int)((int64_t)(seg + 1) * nch / ns);
+    const float *from = src;
+    float *const fin = sg.stage ? sg.stage + (size_t)bh * (D128 * D128) : dst;
+    float *to = fin;
+    if (sg.pass != 0) {
+        float *xs = sg.xs + (size_t)bh * seg_slots(ns) * (D128 * D128);
+        if (mode == SEG_REAL) {
+            from = seg == 0 ? src : xs + (size_t)seg_start(seg) * (D128 * D128);
+            to = seg == ns - 1 ? fin : seg == 0 ? xs + (size_t)seg_start(1) * (D128 * D128) : nullptr;
+        } else {
+            from = nullptr;
+            to = xs + (size_t)(mode == SEG_CARRY ? seg_carry(ns, seg) : seg_trans(ns, seg)) * (D128 * D128);
+        }
+    }
+    const int tb = wave & 3;
+    const int qh = (int)(((int64_t)h * p.H) / HV);
+    auto scale_exp = [&]() {
+        const float ms = fmaxf(fmaxf(sTM[0][0], sTM[1][0]), fmaxf(sTM[2][0], sTM[3][0]));
+        const float mv = fmaxf(fmaxf(sTM[0][1], sTM[1][1]), fmaxf(sTM[2][1], sTM[3][1]));
+        return ce > cb ? tile_exponent(fmaxf(mode == SEG_TRANS ? 0.f : mv, ms)) : 0;
+    };
+    auto rec_of = [&](int jj) { return ws + ((size_t)(c0 + jj) * HV + h) * RecT::SIZE; };
+    // chunk jj's rows of an activation with `heads` heads (head hh, columns c0 ..):
+    // a resource over its valid tokens only, so rows past the request's end read zero
+    const int tok_k = p.H * D128 * 2, tok_v = HV * D128 * 2;  // bytes from one token to the next
+    auto act_rsrc = [&](const void *x, int heads, int hh, int col, int tok_bytes, int row_bytes, int jj) {
+        const int64_t t0 = rs + (int64_t)jj * CH;
+        const int n = (int)((re - t0) < CH ? (re - t0) : CH);
+        const half_t *base = static_cast<const half_t *>(x) + ((size_t)t0 * heads + hh) * D128 + col;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t *>(base), 0, (n - 1) * tok_bytes + row_bytes,
+                                                 0x00020000);
+    };
+
+    if (wave < 4) {
+        // ================================================================ chain
+        float mv = 0.f;
+        for (int j = cb + tid; j < ce; j += 256) {
+            const f4v m4 = *reinterpret_cast<const f4v *>(rec_of(j) + RecT::SC + SC_VMAX * 4);
+            mv = fmaxf(mv, fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        }
+        // Sc[a][rt][i] = S[row0 + 16 rt + lr][16 (2 wave + a) + 4 lq + i]
+        f4v Sc[2][NVB];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rt = 0; rt < NVB; ++rt) {
+                const int row = row0 + 16 * rt + lr, col = 16 * (2 * wave + a) + 4 * lq;
+                if (from) {
+                    Sc[a][rt] = *reinterpret_cast<const f4v *>(from + (size_t)row * D128 + col);
+                } else {
+                    const float one = mode == SEG_TRANS ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Sc[a][rt][i] = row == col + i ? one : 0.f;
+                }
+            }
+        {
+            float mx = 0.f;
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(Sc[a][rt][i]));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                mx = fmaxf(mx, __shfl_xor(mx, o));
+                mv = fmaxf(mv, __shfl_xor(mv, o));
+            }
+            if (lane == 0) {
+                sTM[wave][0] = mx;
+                sTM[wave][1] = mv;
+            }
+        }
+        lds_barrier();  // 0: the tile's max |S0| is posted
+        const int sx = scale_exp();
+        const float up = ldexpf(1.f, sx), down = ldexpf(1.f, -sx);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= up;
+        const float um = mode == SEG_TRANS ? 0.f : up;  // a transition tile leaves V out
+        SplitWatch sw;
+        struct Ops {
+            h8 k[4];        // k row 16 tb + lr, keys 32 kk + 8 lq .. +7
+            h4 v[NVB];      // v at (tokens 16 tb + 4 lq + i, row 16 vb + lr)
+            h8 kt[2][2];    // K^T fragments: key tiles 2 wave + a, token steps ks
+            h8 th[2], tl[2];  // T (hi, lo): token 16 tb + lr, tokens 32 ks + 8 lq .. +7
+            f4v kd, bt, rw;   // kd, beta and w of this lane's four D tokens 16 tb + 4 lq + i
+            float gc;         // gamma_C
+        };
+        const uint32_t offK = (uint32_t)((16 * tb + lr) * tok_k + 2 * lk);
+        const uint32_t offSc = RecT::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
+        auto fetchK = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = act_rsrc(p.k, p.H, qh, 0, tok_k, D128 * 2, jj);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.k[kk] = ld_b128<h8>(r, offK + 64 * kk);
+        };
+        // v in the layout of D's accumulators: four tokens of one row per lane
+        auto fetchV = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = act_rsrc(p.v, HV, h, row0, tok_v, TR * 2, jj);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f.v[vb][i] = __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(
+                                                                r, (uint32_t)((16 * tb + 4 * lq + i) * tok_v + 2 * (16 * vb + lr)), 0, 0));
+        };
+        const uint32_t offKt = (uint32_t)(2 * wave) * 2 * 1024 + l16;
+        auto fetchKt = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(kts + ((size_t)(c0 + jj) * p.H + qh) * RecT::KT_SIZE, RecT::KT_SIZE);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = ld_b128<h8>(r, offKt + (2 * a + ks) * 1024);
+        };
+        auto fetchT = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // blocks above the diagonal are not stored: an offset past the record reads zero
+                const uint32_t o = (tb < 2 && ks == 1) ? 0x7FFFF000u : RecT::T + (uint32_t)((tb * 2 + ks) * 2) * 1024 + l16;
+                f.th[ks] = ld_b128<h8>(r, o);
+                f.tl[ks] = ld_b128<h8>(r, o + 1024);
+            }
+        };
+        auto fetchS = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
+            f.kd = ld_b128<f4v>(r, offSc);
+            if constexpr (RET) {
+                f.bt = ld_b128<f4v>(r, offSc + SCT_BETA * 4);
+                f.rw = ld_b128<f4v>(r, offSc + SCT_RW * 4);
+            }
+            f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, RecT::SC + 2 * CH * 4, 0, 0));
+        };
+        // D at (tokens 16 bt + 4 lq + i, state row 16 vb + lr) -> D^T and (kd D)^T
+        auto put_d = [&](int bf, f4v dv, f4v kd, int bt, int vb) {
+            f4v dsv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsv[i] = kd[i] * dv[i];
+            const int r = 16 * vb + lr, c = 16 * bt + 4 * lq;
+            h4 dh, dl, sh, sl;
+            sw.note(dv);
+            split4(dv, dh, dl);
+            *reinterpret_cast<h4 *>(&sDt[bf][0][r][sw_tok(lr, c)]) = dh;
+            *reinterpret_cast<h4 *>(&sDt[bf][1][r][sw_tok(lr, c)]) = dl;
+            sw.note(dsv);
+            split4(dsv, sh, sl);
+            *reinterpret_cast<h4 *>(&sDs[0][r][sw_tok(lr, c)]) = sh;
+            *reinterpret_cast<h4 *>(&sDs[1][r][sw_tok(lr, c)]) = sl;
+        };
+        auto step = [&](int j, Ops &cur) {
+            const int bf = j & 1;
+            const int jn = j + 1 < ce ? j + 1 : j;  // the last chunk re-reads itself
+            // ---- A: state tile -> LDS (hi, lo)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt) {
+                    h4 hi, lo;
+                    sw.note(Sc[a][rt]);
+                    split4(Sc[a][rt], hi, lo);
+                    *reinterpret_cast<h4 *>(&sS[0][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = hi;
+                    *reinterpret_cast<h4 *>(&sS[1][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = lo;
+                }
+            lds_barrier();  // 1
+            if constexpr (RET) {
+                // ---- B1: Y = K S^T at (tokens 16 tb + 4 lq + i, rows 16 vb + lr), then
+                // Z = um beta V - w Y as Z^T into the free D buffer
+                f4v y[NVB], yl[NVB];
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) y[vb] = yl[vb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const h8 shi = ld_h8(&sS[0][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                        const h8 slo = ld_h8(&sS[1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                        y[vb] = mfma16(cur.k[kk], shi, y[vb]);
+                        yl[vb] = mfma16(cur.k[kk], slo, yl[vb]);
+                    }
+                fetchK(jn, cur);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    f4v z;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[i] = um * cur.bt[i] * (float)cur.v[vb][i] - cur.rw[i] * (y[vb][i] + yl[vb][i]);
+                    h4 zh, zl;
+                    sw.note(z);
+                    split4(z, zh, zl);
+                    const int r = 16 * vb + lr, c = 16 * tb + 4 * lq;
+                    *reinterpret_cast<h4 *>(&sDt[bf ^ 1][0][r][sw_tok(lr, c)]) = zh;
+                    *reinterpret_cast<h4 *>(&sDt[bf ^ 1][1][r][sw_tok(lr, c)]) = zl;
+                }
+                fetchV(jn, cur);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();  // 1.5
+                // ---- B2: D = T Z; T is lower triangular, so token block tb reads
+                // Z tokens 0 .. 16 tb + 15 (one token step for tb < 2)
+                f4v d[NVB], dl[NVB];
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) d[vb] = dl[vb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks == 1 && tb < 2) break;
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const h8 zhi = ld_h8(&sDt[bf ^ 1][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                        const h8 zlo = ld_h8(&sDt[bf ^ 1][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                        d[vb] = mfma16(cur.th[ks], zhi, d[vb]);
+                        dl[vb] = mfma16(cur.th[ks], zlo, dl[vb]);
+                        dl[vb] = mfma16(cur.tl[ks], zhi, dl[vb]);
+                    }
+                }
+                fetchT(jn, cur);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) put_d(bf, d[vb] + dl[vb], cur.kd, tb, vb);
+            } else {
+                // no retrieval: D = V
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    f4v dv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dv[i] = um * (float)cur.v[vb][i];
+                    put_d(bf, dv, cur.kd, tb, vb);
+                }
+                fetchV(jn, cur);
+            }
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();  // 2
+            // ---- E: S^T <- gamma_C S^T + K^T (kd D) for key tiles 2 wave + a, row blocks rt
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= cur.gc;
+            {
+                constexpr bool SEPL = NVB < 4;
+                f4v lo4[2][NVB] = {};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int rt = 0; rt < NVB; ++rt) {
+                        const h8 dhi = ld_h8(&sDs[0][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]);
+                        const h8 dlo = ld_h8(&sDs[1][16 * rt + lr][sw_tok(lr, 32 * ks + lk)]);
+#pragma unroll
+                        for (int a = 0; a < 2; ++a) {
+                            Sc[a][rt] = mfma16(cur.kt[a][ks], dhi, Sc[a][rt]);
+                            if constexpr (SEPL) lo4[a][rt] = mfma16(cur.kt[a][ks], dlo, lo4[a][rt]);
+                            else Sc[a][rt] = mfma16(cur.kt[a][ks], dlo, Sc[a][rt]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int rt = 0; rt < NVB; ++rt)
+                        if constexpr (SEPL) Sc[a][rt] += lo4[a][rt];
+            }
+            fetchS(jn, cur);
+            fetchKt(jn, cur);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        Ops op;
+        if (ce > cb) {
+            if constexpr (RET) {
+                fetchK(cb, op);
+                fetchT(cb, op);
+            }
+            fetchV(cb, op);
+            fetchS(cb, op);
+            fetchKt(cb, op);
+        }
+        for (int j = cb; j < ce; ++j) step(j, op);
+        if (to) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int rt = 0; rt < NVB; ++rt)
+                    *reinterpret_cast<f4v *>(to + (size_t)(row0 + 16 * rt + lr) * D128 + 16 * (2 * wave + a) + 4 * lq) = Sc[a][rt] * down;
+        }
+        // a split operand at or past SPLIT_LIMIT hands the pair to the recurrent kernel
+        if (sw.over()) off[p.B + 1 + bh] = 2;
+    } else if (mode != SEG_REAL) {
+        // carry and transition tiles write no output: these waves only keep
+        // the chain's barriers (one at the start, two or three per chunk step)
+        lds_barrier();  // 0
+        for (int j = cb; j < ce; ++j) {
+            lds_barrier();
+            if constexpr (RET) lds_barrier();
+            lds_barrier();
+        }
+    } else {
+        // ================================================================ outputs
+        half_t *o = static_cast<half_t *>(p.o);
+        lds_barrier();  // 0
+        const float down = ldexpf(1.f, -scale_exp());
+        struct Ops {
+            h8 q[4];          // q row 16 tb + lr, keys 32 kk + 8 lq .. +7
+            h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
+            float gq;         // gq of this lane's token
+        };
+        const uint32_t offQ = (uint32_t)((16 * tb + lr) * tok_k + 2 * lk);
+        const int tok_bytes = HV * D128 * 2;
+        static_assert(TR == 64 || TR == 32 || TR == 16, "the output transpose takes 16-, 32- or 64-row tiles");
+        constexpr int LPT = TR / 8;
+        constexpr int NST = TR == 64 ? 2 : 1;
+        constexpr int TPS = 16 / NST;
+        const bool st_live = lane / LPT < TPS;
+        const int st_tok = st_live ? lane / LPT : TPS - 1, st_q = lane % LPT;
+        const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
+        const uint32_t offP = RecT::P + (uint32_t)tb * 4 * 1024 + l16;
+        const uint32_t offP1 = tb < 2 ? 0x7FFFF000u : offP + 2048;
+        const uint32_t offG = RecT::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
+        auto fetchQ = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = act_rsrc(p.q, p.H, qh, 0, tok_k, D128 * 2, jj);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.q[kk] = ld_b128<h8>(r, offQ + 64 * kk);
+        };
+        auto fetchG = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
+            f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
+        };
+        auto fetchP = [&](int jj, Ops &f) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f.ph[ks] = ld_b128<h8>(r, ks ? offP1 : offP);
+                f.pl[ks] = ld_b128<h8>(r, (ks ? offP1 : offP) + 1024);
+            }
+        };
+        auto store_out = [&](int jo) {
+            const int64_t t0 = rs + (int64_t)jo * CH;
+            const int n = jo >= cb ? (int)((re - t0) < CH ? (re - t0) : CH) : 0;
+            half_t *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
+            const __amdgpu_buffer_rsrc_t ro =
+                __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
+#pragma unroll
+            for (int ps = 0; ps < NST; ++ps)
+                __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok + TPS * ps][8 * st_q]), ro,
+                                                       offO + (uint32_t)(TPS * ps * tok_bytes), 0, 0);
+        };
+        auto step = [&](int j, Ops &cur) {
+            const int bf = j & 1;
+            const int jn = j + 1 < ce ? j + 1 : j;
+            lds_barrier();  // 1
+            store_out(j - 1);
+            // ---- O1: O^T = S Q^T at (rows 16 vb + 4 lq + i, token 16 tb + lr)
+            f4v acc[NVB], acl[NVB];
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = acl[vb] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const h8 shi = ld_h8(&sS[0][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                    const h8 slo = ld_h8(&sS[1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
+                    acc[vb] = mfma16(shi, cur.q[kk], acc[vb]);
+                    acl[vb] = mfma16(slo, cur.q[kk], acl[vb]);
+                }
+            fetchQ(jn, cur);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (RET) lds_barrier();  // 1.5
+            lds_barrier();  // 2
+            // ---- O2: O^T = gq O^T + D^T P^T
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = cur.gq * (acc[vb] + acl[vb]);
+            fetchG(jn, cur);
+            {
+                f4v p3[NVB] = {};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) {
+                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                        acc[vb] = mfma16(dhi, cur.ph[ks], acc[vb]);
+                        p3[vb] = mfma16(dlo, cur.ph[ks], p3[vb]);
+                        p3[vb] = mfma16(dhi, cur.pl[ks], p3[vb]);
+                    }
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
+            }
+            fetchP(jn, cur);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                h4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = (half_t)(acc[vb][i] * down);
+                *reinterpret_cast<h4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
+            }
+        };
+        Ops op;
+        if (ce > cb) {
+            fetchQ(cb, op);
+            fetchG(cb, op);
+            fetchP(cb, op);
+        }
+        {
+            const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(u4v{0u, 0u, 0u, 0u}, none, 0, 0, 0);
+        }
+        for (int j = cb; j < ce; ++j) step(j, op);
+        if (ce > cb) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            store_out(ce - 1);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ segment starts
 // start_{p+1} = start_p M_p + c_p for the middle segments p = 1 .. nseg - 2,
 // in order; rows are independent, so one workgroup takes 16 rows of one
@@ -1774,45 +2296,62 @@ __global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int3
 
 // ------------------------------------------------------------------ host side
 
+// The per-head form has two variants.  With a single-pass scan over 128 or
+// more (request, head) pairs it takes the T form (k_chunk_prep<RULE, true>,
+// k_chunk_scan_t): records of 34 KB per (chunk, value head) instead of 81 KB
+// plus 32 KB of K^T and q per (chunk, q/k head), at the price of one more
+// product on the scan's serial chain per chunk.  Measured on MI355X in one
+// session: the varlen workload (8 requests, 32 heads) 0.974 -> 0.924 ms; the
+// 65,536-token sequence (16 heads, 5 scan segments) 1.53 -> 1.65 ms, so
+// segmented and few-pair scans keep W and U in the records.
+static bool t_form(bool per_key, int B, int HV, int nseg) { return !per_key && nseg <= 1 && (int64_t)B * HV >= 128; }
+
 // Workspace: chunk table (off[B + 1], then the (B * HV) hand-over flags) |
-// records of every (chunk, value head) | per head: K^T and q of every (chunk,
-// q/k head) | segment states.  The chunk budget of gdr_chunk_plan.hpp sizes
-// the records; the table never assigns a chunk index at or past it.
+// records of every (chunk, value head) (Rec<true>, Rec<false> or RecT) |
+// per-head form: K^T and q (T form: K^T only) of every (chunk, q/k head) |
+// segment states | staging for in-place final states (one 128 x 128 fp32
+// state per pair).  The chunk budget of gdr_chunk_plan.hpp sizes the
+// records; the table never assigns a chunk index at or past it.
+struct Layout {
+    size_t kq, seg, stage, total;
+};
 static size_t table_bytes(int B, int HV) { return ((size_t)(B + 1) * 4 + (size_t)B * HV * 4 + 255) / 256 * 256; }
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-static size_t kq_offset(int64_t T, int B, int HV, bool per_key)
+static Layout layout(int64_t T, int B, int H, int HV, bool per_key, int nseg)
 {
     const int64_t maxch = chunk_budget(T, B);
-    return table_bytes(B, HV) + ((size_t)maxch * HV * (per_key ? Rec<true>::SIZE : Rec<false>::SIZE) + 255) / 256 * 256;
+    const bool tf = t_form(per_key, B, HV, nseg);
+    const size_t rec = per_key ? Rec<true>::SIZE : tf ? RecT::SIZE : Rec<false>::SIZE;
+    const size_t kq = per_key ? 0 : tf ? RecT::KT_SIZE : KQ::SIZE;
+    Layout l;
+    l.kq = table_bytes(B, HV) + round256((size_t)maxch * HV * rec);
+    l.seg = l.kq + round256((size_t)maxch * H * kq);
+    l.stage = l.seg + (nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0);
+    l.total = l.stage + (size_t)B * HV * D128 * D128 * 4;
+    return l;
 }
 
-static size_t seg_offset(int64_t T, int B, int H, int HV, bool per_key)
-{
-    const int64_t maxch = chunk_budget(T, B);
-    return kq_offset(T, B, HV, per_key) + (per_key ? 0 : ((size_t)maxch * H * KQ::SIZE + 255) / 256 * 256);
-}
-
-static size_t stage_offset(int64_t T, int B, int H, int HV, bool per_key, int nseg)
-{
-    const size_t segs = nseg > 1 ? (size_t)B * HV * seg_slots(nseg) * D128 * D128 * 4 : 0;
-    return seg_offset(T, B, H, HV, per_key) + segs;
-}
-
-// ... | staging for in-place final states (one 128 x 128 fp32 state per pair)
 static size_t workspace_bytes(int64_t T, int B, int H, int HV, bool per_key, int nseg)
 {
-    return stage_offset(T, B, H, HV, per_key, nseg) + (size_t)B * HV * D128 * D128 * 4;
+    return layout(T, B, H, HV, per_key, nseg).total;
 }
 
 // Row tile of the scan: 16 * NVB rows, NVB = 1, 2 or 4 (launch_scans picks).
-template <typename TA, int RULE, int NVB, bool PK>
+// TF: the per-head T form (fp16 activations).
+template <typename TA, int RULE, int NVB, bool PK, bool TF>
 static void launch_scan(const Params &p, int32_t *off, const char *rec, const char *kq, const ScanSeg &sg,
                         hipStream_t s)
 {
     constexpr int NTILE = D128 / (16 * NVB);
     const int64_t groups = (int64_t)p.B * p.HV * (sg.pass == 0 ? 1 : sg.nseg - 1);
     const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
-    if (blocks > 0) hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
+    if (blocks <= 0) return;
+    if constexpr (TF)
+        hipLaunchKernelGGL((k_chunk_scan_t<RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
+    else
+        hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq,
+                           sg);
 }
 
 // Scan launches.  Few (request, head) pairs leave most CUs idle with 32-row
@@ -1839,18 +2378,19 @@ static void launch_scans(const Params &p, int32_t *off, const char *rec, const c
     const int64_t pairs = (int64_t)p.B * p.HV;
     if (nseg <= 1) {
         const ScanSeg one{1, 0, nullptr, stage};
-        if (pairs <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, one, s);
-        else if (pairs < 128) launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, one, s);
-        else launch_scan<TA, RULE, 4, PK>(p, off, rec, kq, one, s);
+        if (pairs <= 32) launch_scan<TA, RULE, 1, PK, false>(p, off, rec, kq, one, s);
+        else if (pairs < 128) launch_scan<TA, RULE, 2, PK, false>(p, off, rec, kq, one, s);
+        else if constexpr (PK) launch_scan<TA, RULE, 4, PK, false>(p, off, rec, kq, one, s);
+        else launch_scan<TA, RULE, 4, PK, true>(p, off, rec, kq, one, s);  // the T form (t_form)
         return;
     }
-    launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
+    launch_scan<TA, RULE, 2, PK, false>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
     if (nseg > 2) {
         const int64_t blocks = pairs * 8;
         hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, off, ScanSeg{nseg, 0, xs, stage});
     }
-    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
-    else launch_scan<TA, RULE, 2, PK>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
+    if (pairs * (nseg - 1) <= 32) launch_scan<TA, RULE, 1, PK, false>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
+    else launch_scan<TA, RULE, 2, PK, false>(p, off, rec, kq, ScanSeg{nseg, 2, xs, stage}, s);
 }
 
 // PK: the per-key record and kernels; PKG: the gate itself is per key (else
@@ -1863,18 +2403,22 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
     char *base = static_cast<char *>(ws);
     int32_t *off = reinterpret_cast<int32_t *>(base);
     int32_t *redo = off + p.B + 1;
+    const Layout l = layout(p.T, p.B, p.H, p.HV, PK, nseg);
     char *rec = base + table_bytes(p.B, p.HV);
-    char *kq = base + kq_offset(p.T, p.B, p.HV, PK);
-    float *xs = reinterpret_cast<float *>(base + seg_offset(p.T, p.B, p.H, p.HV, PK));
+    char *kq = base + l.kq;
+    float *xs = reinterpret_cast<float *>(base + l.seg);
     // the incoming state is overwritten in place: stage the final states
     const bool in_place = p.num_slots > 0 || (p.init != nullptr && p.init == p.state);
-    float *stage = in_place ? reinterpret_cast<float *>(base + stage_offset(p.T, p.B, p.H, p.HV, PK, nseg)) : nullptr;
+    float *stage = in_place ? reinterpret_cast<float *>(base + l.stage) : nullptr;
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, s, p, off, redo);
     if (maxch * p.HV > 0) {
+        const dim3 grid((unsigned)((maxch + 7) / 8 * 8 * p.HV));
         if constexpr (PK)
-            hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec);
+            hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), grid, dim3(256), 0, s, p, off, rec);
+        else if (t_form(PK, p.B, p.HV, nseg))
+            hipLaunchKernelGGL((k_chunk_prep<RULE, true>), grid, dim3(256), 0, s, p, off, rec, kq);
         else
-            hipLaunchKernelGGL((k_chunk_prep<RULE>), dim3((unsigned)((maxch + 7) / 8 * 8 * p.HV)), dim3(256), 0, s, p, off, rec, kq);
+            hipLaunchKernelGGL((k_chunk_prep<RULE, false>), grid, dim3(256), 0, s, p, off, rec, kq);
     }
     launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, stage, nseg, s);
     hipError_t err = hipGetLastError();

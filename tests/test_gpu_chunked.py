@@ -181,11 +181,28 @@ def test_chunked_state_magnitude(magnitude, rule):
 
 
 # ------------------------------------------------------------------ operands past the fp16 range
-GROWTH = [("plain", None, 1, 16384), ("slab", (5,), 1, 16384), ("segmented", None, 2, 32768)]
+def _check_heads(case, o, st, heads, tol_o, what):
+    """o and the final state of every request on value heads ``heads``
+    against the oracle run on those heads alone (requests and heads evolve
+    independently)."""
+    if case["slab"] is not None:
+        st = st[case["slot_ids"]]
+    for b in range(len(case["cu_seqlens"]) - 1):
+        sc, (s, e) = sub_case(case, b, heads)
+        ro, rs = oracle_forward(sc)
+        assert_close(o[s:e][:, heads], ro, tol_o, "%s request %d o" % (what, b))
+        assert_close(st[b][heads], rs[0], TOL_CHUNKED, "%s request %d state" % (what, b))
+        yield rs
 
 
-@pytest.mark.parametrize("name,slots,segs,T0", GROWTH, ids=[g[0] for g in GROWTH])
-def test_chunked_state_growth_hand_over(name, slots, segs, T0):
+# (name, slots, scan segments, grown request's tokens, q/k heads, value heads):
+# 8 pairs take the form with W and U in the records; 128 pairs the T form
+GROWTH = [("plain", None, 1, 16384, 2, 4), ("slab", (5,), 1, 16384, 2, 4), ("segmented", None, 2, 32768, 2, 4),
+          ("t_form", None, 1, 16384, 16, 64), ("t_form_slab", (5,), 1, 16384, 16, 64)]
+
+
+@pytest.mark.parametrize("name,slots,segs,T0,H,HV", GROWTH, ids=[g[0] for g in GROWTH])
+def test_chunked_state_growth_hand_over(name, slots, segs, T0, H, HV):
     """A state that grows past what the scan's fp16 (hi, lo) operands hold: the
     linear rule (README, update rules: no decay, no erase) with one key
     repeated for T0 tokens and v = 1 builds a state column of T0 times the
@@ -196,40 +213,36 @@ def test_chunked_state_growth_hand_over(name, slots, segs, T0):
     through the staging area and the flagged ones are recomputed from the
     intact slab."""
     case = _case(47, [T0, 300], update_rule="linear", gate_activation="none", beta_activation="none",
-                 slots=slots)
+                 slots=slots, H=H, HV=HV)
     key = np.zeros(128, np.float16)
     key[5] = 1.0
     case["k"][:T0] = key
     case["v"][:T0] = np.float16(1.0)
-    say("case state growth %s segments=%d" % (name, segs))
+    say("case state growth %s segments=%d pairs=%d" % (name, segs, 2 * HV))
     o, st = gpu_forward(case, "chunked", scan_segments=segs)
-    ro, rs = oracle_forward(case)
-    assert float(np.max(np.abs(rs))) > 16000.0, "the state reaches the intended size"
-    if slots is not None:
-        st = st[case["slot_ids"]]
-        rs = rs[case["slot_ids"]]
-    assert_close(o[:T0], ro[:T0], TOL_CHUNKED, "%s grown request o" % name)
-    assert_close(st[0], rs[0], TOL_CHUNKED, "%s grown request state" % name)
-    assert_close(o[T0:], ro[T0:], TOL_CHUNKED, "%s chunked request o" % name)
-    assert_close(st[1], rs[1], TOL_CHUNKED, "%s chunked request state" % name)
+    heads = [0, 1, HV - 1]
+    states = list(_check_heads(case, o, st, heads, TOL_CHUNKED, name))
+    assert float(np.max(np.abs(states[0]))) > 16000.0, "the state reaches the intended size"
 
 
-PROLOGUE = ["per_head_scores", "per_key_bf16_values"]
+# (form, q/k heads, value heads)
+PROLOGUE = [("per_head_scores", 2, 4), ("t_form_scores", 16, 64), ("per_key_bf16_values", 2, 4)]
 
 
-@pytest.mark.parametrize("form", PROLOGUE)
-def test_chunked_prologue_hand_over(form):
+@pytest.mark.parametrize("form,H,HV", PROLOGUE, ids=[f[0] for f in PROLOGUE])
+def test_chunked_prologue_hand_over(form, H, HV):
     """Operands the prologue splits into fp16 (hi, lo) past the fp16 range:
     scores scale q.k of unnormalised keys near 1e5 (per-head form, gated
-    rule), and bf16 values near 5e5 (per-key form, Gated DeltaNet-2 rule).
-    The prologue flags the request's pairs and the recurrent kernel computes
-    them; the other request stays on the chunked path."""
+    rule; 8 pairs with W and U in the records, 128 pairs in the T form), and
+    bf16 values near 5e5 (per-key form, Gated DeltaNet-2 rule).  The prologue
+    flags the request's pairs and the recurrent kernel computes them; the
+    other request stays on the chunked path."""
     T0 = 400
-    if form == "per_head_scores":
+    if form != "per_key_bf16_values":
         case = _case(48, [T0, 200], update_rule="gated", gate_activation="none", beta_activation="none",
-                     qk_l2_norm=0)
+                     qk_l2_norm=0, H=H, HV=HV)
         rng = np.random.default_rng(48)
-        for hq in range(2):
+        for hq in range(H):
             u = rng.standard_normal(128)
             u = 1000.0 * u / np.linalg.norm(u)
             case["q"][:T0, hq] = u.astype(np.float16)
@@ -241,14 +254,10 @@ def test_chunked_prologue_hand_over(form):
                      gate_activation="none", beta_activation="none")
         case["v"][:T0] = case["v"][:T0] * np.float32(2.0 ** 17)  # stays on the bf16 grid
         assert float(np.max(np.abs(case["v"][:T0]))) > 65504.0
-    say("case prologue hand-over %s" % form)
+    say("case prologue hand-over %s pairs=%d" % (form, 2 * HV))
     o, st = gpu_forward(case, "chunked", scan_segments=1)
-    ro, rs = oracle_forward(case)
     tol_o = TOL_BF16_O if case["act_dtype"] == "bf16" else TOL_CHUNKED
-    assert_close(o[:T0], ro[:T0], tol_o, "%s flagged request o" % form)
-    assert_close(st[0], rs[0], TOL_CHUNKED, "%s flagged request state" % form)
-    assert_close(o[T0:], ro[T0:], tol_o, "%s chunked request o" % form)
-    assert_close(st[1], rs[1], TOL_CHUNKED, "%s chunked request state" % form)
+    list(_check_heads(case, o, st, [0, 1, HV - 1], tol_o, form))
 
 
 # ------------------------------------------------------------------ the workloads, every pair

@@ -69,7 +69,7 @@ def test_noalloc_equals_forward_on_consecutive_calls():
 
 def test_noalloc_refuses_a_workspace_beyond_its_array():
     from gated_delta_rule_token_amd import api
-    T, H = 16384, 16
+    T, H = 32768, 16  # records of 34 KB per (chunk, head): ~300 MB of workspace
     q = torch.zeros((T, H, 128), dtype=torch.float16, device="cuda")
     v = torch.zeros((T, H, 128), dtype=torch.float16, device="cuda")
     g = torch.zeros((T, H), dtype=torch.float32, device="cuda")
