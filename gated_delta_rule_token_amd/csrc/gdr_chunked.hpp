@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // TF: the T form (RecT: T, P and the scalars; no W, U, K^T or q), else Rec<false>
 // plus the K^T and q area.
 template <int RULE, bool TF>
-__global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *__restrict__ off,
-                                                   char *__restrict__ ws, char *__restrict__ kqs)
+__global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, int32_t *__restrict__ off,
+                                                              char *__restrict__ ws, char *__restrict__ kqs)
 {
     constexpr bool DEC = rule_decays(RULE);
     constexpr bool RET = rule_retrieves(RULE);
@@ -357,11 +357,12 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
     constexpr int SLOT = CH * LD * 2;
     static_assert(CH * LA * 4 == SLOT, "Q rows and A rows share one LDS footprint");
 
-    __shared__ __align__(16) char sm[3 * SLOT];
+    // the T form keeps no V rows: K and Q (then A) only, so four workgroups fit a CU
+    __shared__ __align__(16) char sm[(TF ? 2 : 3) * SLOT];
     half_t(*sK)[LD] = reinterpret_cast<half_t(*)[LD]>(sm);
     half_t(*sV)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + SLOT);
-    half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + 2 * SLOT);
-    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + 2 * SLOT);
+    half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + (TF ? 1 : 2) * SLOT);
+    float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + (TF ? 1 : 2) * SLOT);
     half_t(*sW)[CH][D128] = reinterpret_cast<half_t(*)[CH][D128]>(sm);  // [hi, lo][token][key, swizzled], after the solve
     __shared__ float sG[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
 
@@ -569,12 +570,14 @@ __global__ __launch_bounds__(256, 3) void k_chunk_prep(const Params p, int32_t *
                 for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
                 x[t] = (r[0] + r[1]) + (r[2] + r[3]);
                 sA[t][lane] = x[t];
-                wt.note(x[t]);
+                if constexpr (!TF) wt.note(x[t]);
             }
             // the column times its weight (split beside T below) peaks where
-            // |T| does: rounding is monotone
-            wt.note(__uint_as_float(wt.big) * sBeta[lane]);
-            post(wt);
+            // |T| does: rounding is monotone (the T form watches T as it exports it)
+            if constexpr (!TF) {
+                wt.note(__uint_as_float(wt.big) * sBeta[lane]);
+                post(wt);
+            }
         }
         lds_barrier();  // T is complete
         if constexpr (TF) {
