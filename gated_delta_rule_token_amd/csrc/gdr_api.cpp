@@ -55,7 +55,7 @@ int64_t state_rows(const gdr_problem *p) { return p->num_slots > 0 ? p->num_slot
 // and the erase gate take the per-key form).
 bool chunked_per_key(const gdr_problem *p)
 {
-    return p->decay_per_key != 0 || p->update_rule == GDR_RULE_GATED_DELTA_V2 || p->act_dtype == GDR_BF16;
+    return p->decay_per_key != 0 || p->update_rule == GDR_RULE_GATED_DELTA_V2;
 }
 
 bool chunked_ok(const gdr_problem *p)

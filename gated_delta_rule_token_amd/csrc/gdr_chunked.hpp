@@ -143,6 +143,27 @@ __device__ __forceinline__ void split8(const float (&x)[8], h8 &hi, h8 &lo)
 
 __device__ __forceinline__ h8 ld_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
 
+// Eight 16-bit activations as fp16.  bf16 values convert exactly when they
+// lie in fp16's range with no more than its precision (every bf16 value of
+// magnitude 2^-17 to 65504); `exact` is cleared for any other (and for NaN).
+__device__ __forceinline__ h8 to_h8(h8 x, bool &) { return x; }
+__device__ __forceinline__ h8 to_h8(ActVec<bf16_t>::v8 x, bool &exact)
+{
+    h8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float f = (float)x[e];
+        r[e] = (half_t)f;
+        exact = exact && (float)r[e] == f;
+    }
+    return r;
+}
+template <typename TI>
+__device__ __forceinline__ h8 ld_as_h8(const TI *p, bool &exact)
+{
+    return to_h8(*reinterpret_cast<const typename ActVec<TI>::v8 *>(p), exact);
+}
+
 // 16x16x32 matrix product of 16-bit activations with fp32 accumulation (the
 // products of two fp16 or two bf16 values are exact in fp32)
 __device__ __forceinline__ f4v mfma16x32(ActVec<half_t>::v8 a, ActVec<half_t>::v8 b, f4v c)
@@ -345,7 +366,9 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
 // TF: the T form (RecT: T, P and the scalars; no W, U, K^T or q), else Rec<false>
 // plus the K^T and q area.
-template <int RULE, bool TF>
+// TI: the activations' dtype (bf16 rows are converted to fp16 as they load;
+// a pair with a value fp16 cannot hold exactly goes to the recurrent kernel).
+template <typename TI, int RULE, bool TF>
 __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, int32_t *__restrict__ off,
                                                               char *__restrict__ ws, char *__restrict__ kqs)
 {
@@ -392,22 +415,23 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         if (w.over()) *flag = 2;
     };
 
-    const half_t *__restrict__ q = static_cast<const half_t *>(p.q);
-    const half_t *__restrict__ k = static_cast<const half_t *>(p.k);
-    const half_t *__restrict__ v = static_cast<const half_t *>(p.v);
+    const TI *__restrict__ q = static_cast<const TI *>(p.q);
+    const TI *__restrict__ k = static_cast<const TI *>(p.k);
+    const TI *__restrict__ v = static_cast<const TI *>(p.v);
 
     // ---- chunk rows of K, Q (head qh) and V (head h): issue the loads first,
     // compute the gates while they are in flight, then park them in LDS
     h8 ldk[4], ldq[4], ldv[4];
+    bool exact = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
         ldk[i] = ldq[i] = ldv[i] = h8{};
         if (r < n) {
             const size_t tq = ((size_t)(t0 + r) * H + qh) * D128 + c8;
-            ldk[i] = ld_h8(k + tq);
-            ldq[i] = ld_h8(q + tq);
-            ldv[i] = ld_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8);
+            ldk[i] = ld_as_h8(k + tq, exact);
+            ldq[i] = ld_as_h8(q + tq, exact);
+            ldv[i] = ld_as_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8, exact);
         }
     }
     // ---- per-token log decay (cumulated over the chunk by a 64-lane scan) and update rate
@@ -438,6 +462,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
             *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
     post_vmax(ldv, rec + OSC);
+    if (!exact) *flag = 2;  // a bf16 value fp16 cannot hold: the recurrent kernel takes the pair
     lds_barrier();
 
     // ---- K^T fragments (key 16 mt + lr, tokens 32 ks + 8 lq .. +7); fragment f = block * 64 + lane
@@ -1771,7 +1796,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 }
 
 // ------------------------------------------------------------------ phase 2, T form
-// Per-head decay, fp16 activations.  The chain forms the chunk's value
+// Per-head decay; fp16 activations, or bf16 converted to fp16 as they load
+// (the prologue has handed pairs with values fp16 cannot hold to the
+// recurrent kernel).  The chain forms the chunk's value
 // updates from the raw rows instead of loading W and U: with the key rows
 // against the incoming state, Y = K S^T, and Z = diag(beta) V - diag(w) Y,
 //   D = U - W S^T = T Z,
@@ -1781,7 +1808,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 // has three barriers: the state tile is in LDS (1), Z is (1.5, retrieving
 // rules only), D is (2).  Workgroup layout, segments, tile scaling and the
 // output path follow k_chunk_scan.
-template <int RULE, int NVB>
+template <typename TA, int RULE, int NVB>
 __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *off, const char *ws, const char *kts,
                                                      const ScanSeg sg)
 {
@@ -1793,7 +1820,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
     __shared__ __align__(16) half_t sS[2][TR][D128];
     __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token]: D^T of chunk j in j & 1, Z^T in the other
     __shared__ __align__(16) half_t sDs[2][TR][CH];      // [hi, lo][row][token] (kd D)^T
-    __shared__ __align__(16) half_t sO[4][16][TR + 8];   // per output wave: [token][row] staging for the store
+    __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
     __shared__ float sTM[4][2];                           // per chain wave: max |S0| of its part, max |v|
 
     const int HV = p.HV;
@@ -1914,8 +1941,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         const uint32_t offSc = RecT::SC + (uint32_t)(16 * tb + 4 * lq) * 4;
         auto fetchK = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = act_rsrc(p.k, p.H, qh, 0, tok_k, D128 * 2, jj);
+            bool ok = true;  // exactness was checked by the prologue
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.k[kk] = ld_b128<h8>(r, offK + 64 * kk);
+            for (int kk = 0; kk < 4; ++kk) f.k[kk] = to_h8(ld_b128<typename ActVec<TA>::v8>(r, offK + 64 * kk), ok);
         };
         // v in the layout of D's accumulators: four tokens of one row per lane
         auto fetchV = [&](int jj, Ops &f) {
@@ -1924,8 +1952,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    f.v[vb][i] = __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(
-                                                                r, (uint32_t)((16 * tb + 4 * lq + i) * tok_v + 2 * (16 * vb + lr)), 0, 0));
+                    f.v[vb][i] = (half_t)to_f32(__builtin_bit_cast(TA, __builtin_amdgcn_raw_buffer_load_b16(
+                                     r, (uint32_t)((16 * tb + 4 * lq + i) * tok_v + 2 * (16 * vb + lr)), 0, 0)));
         };
         const uint32_t offKt = (uint32_t)(2 * wave) * 2 * 1024 + l16;
         auto fetchKt = [&](int jj, Ops &f) {
@@ -2117,7 +2145,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         }
     } else {
         // ================================================================ outputs
-        half_t *o = static_cast<half_t *>(p.o);
+        TA *o = static_cast<TA *>(p.o);
         lds_barrier();  // 0
         const float down = ldexpf(1.f, -scale_exp());
         struct Ops {
@@ -2139,8 +2167,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         const uint32_t offG = RecT::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         auto fetchQ = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = act_rsrc(p.q, p.H, qh, 0, tok_k, D128 * 2, jj);
+            bool ok = true;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.q[kk] = ld_b128<h8>(r, offQ + 64 * kk);
+            for (int kk = 0; kk < 4; ++kk) f.q[kk] = to_h8(ld_b128<typename ActVec<TA>::v8>(r, offQ + 64 * kk), ok);
         };
         auto fetchG = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
@@ -2157,7 +2186,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         auto store_out = [&](int jo) {
             const int64_t t0 = rs + (int64_t)jo * CH;
             const int n = jo >= cb ? (int)((re - t0) < CH ? (re - t0) : CH) : 0;
-            half_t *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
+            TA *base = jo >= cb ? o + ((size_t)t0 * HV + h) * D128 + row0 : o;
             const __amdgpu_buffer_rsrc_t ro =
                 __builtin_amdgcn_make_buffer_rsrc(base, 0, n > 0 ? (int)((n - 1) * tok_bytes + TR * 2) : 0, 0x00020000);
 #pragma unroll
@@ -2212,10 +2241,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
-                h4 ov;
+                typename ActVec<TA>::v4 ov;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = (half_t)(acc[vb][i] * down);
-                *reinterpret_cast<h4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
+                for (int i = 0; i < 4; ++i) ov[i] = from_f32<TA>(acc[vb][i] * down);
+                *reinterpret_cast<typename ActVec<TA>::v4 *>(&sO[tb][lr][16 * vb + 4 * lq]) = ov;
             }
         };
         Ops op;
@@ -2351,7 +2380,7 @@ static void launch_scan(const Params &p, int32_t *off, const char *rec, const ch
     const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
     if (blocks <= 0) return;
     if constexpr (TF)
-        hipLaunchKernelGGL((k_chunk_scan_t<RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
+        hipLaunchKernelGGL((k_chunk_scan_t<TA, RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
     else
         hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq,
                            sg);
@@ -2397,8 +2426,10 @@ static void launch_scans(const Params &p, int32_t *off, const char *rec, const c
 }
 
 // PK: the per-key record and kernels; PKG: the gate itself is per key (else
-// a per-head gate broadcast over the key channels).  The per-head record and
-// prologue (PK = false) take fp16 activations only.
+// a per-head gate broadcast over the key channels).  The per-head form
+// (PK = false) reads bf16 activations as fp16 (exact for values of magnitude
+// 2^-17 to 65504; its prologue hands pairs with any other value to the
+// recurrent kernel) and stores o in the activations' dtype.
 template <typename TA, int RULE, bool PK, bool PKG>
 static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s)
 {
@@ -2419,9 +2450,9 @@ static hipError_t launch_rule(const Params &p, int nseg, void *ws, hipStream_t s
         if constexpr (PK)
             hipLaunchKernelGGL((k_chunk_prep_pk<TA, RULE, PKG>), grid, dim3(256), 0, s, p, off, rec);
         else if (t_form(PK, p.B, p.HV, nseg))
-            hipLaunchKernelGGL((k_chunk_prep<RULE, true>), grid, dim3(256), 0, s, p, off, rec, kq);
+            hipLaunchKernelGGL((k_chunk_prep<TA, RULE, true>), grid, dim3(256), 0, s, p, off, rec, kq);
         else
-            hipLaunchKernelGGL((k_chunk_prep<RULE, false>), grid, dim3(256), 0, s, p, off, rec, kq);
+            hipLaunchKernelGGL((k_chunk_prep<TA, RULE, false>), grid, dim3(256), 0, s, p, off, rec, kq);
     }
     launch_scans<TA, RULE, PK>(p, off, rec, kq, xs, stage, nseg, s);
     hipError_t err = hipGetLastError();

@@ -16,8 +16,8 @@ hipError_t launch_recurrent(const Params &p, int rule, bool per_key, int act, in
 hipError_t launch_decode128(const Params &p, int rule, bool per_key, int act, hipStream_t s);
 
 // Chunk-parallel prefill (chunk 64, dk = dv = 128, fp16 or bf16 activations,
-// act = 1 or 2); the per-key form serves a decay per key channel, the erase
-// gate and every bf16 problem (per_key here: the gate itself is per key).
+// act = 1 or 2); the per-key form serves a decay per key channel and the
+// erase gate (per_key here: the gate itself is per key).
 // nseg > 1 cuts each request's chain of chunk steps into that many segments
 // (two scan passes and a combine step).  `ws` holds
 // chunked_workspace_bytes(T, B, H, HV, per-key form, nseg) bytes.

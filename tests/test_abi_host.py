@@ -205,12 +205,17 @@ def test_workspace_and_algo_selection(lib):
     assert api.selected_algo(p) == "recurrent"
     p.total_tokens, p.act_dtype = 4096, api.F32
     assert api.selected_algo(p) == "recurrent"
-    # bf16 takes the per-key chunked form for every rule (per-key record size)
+    # bf16 with a per-head decay takes the per-head chunked form (the fp16
+    # problem's layout); the erase gate takes the per-key form
     p.decay_per_key, p.gate_activation, p.gate_dtype, p.update_rule = 0, 0, api.F32, api.RULES["gated_delta"]
     p.act_dtype = api.BF16
     assert api.selected_algo(p) == "chunked"
     assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
+    assert n.value == n_head
+    p.update_rule = api.RULES["gated_delta_v2"]
+    assert lib.gdr_workspace_size(ctypes.byref(p), ctypes.byref(n)) == api.GDR_OK
     assert n.value > n_head
+    p.update_rule = api.RULES["gated_delta"]
     p.act_dtype = api.F32
     p.algo = api.ALGOS["chunked"]
     assert lib.gdr_validate(ctypes.byref(p), None) == api.GDR_E_UNSUPPORTED

@@ -226,7 +226,8 @@ def test_chunked_state_growth_hand_over(name, slots, segs, T0, H, HV):
 
 
 # (form, q/k heads, value heads)
-PROLOGUE = [("per_head_scores", 2, 4), ("t_form_scores", 16, 64), ("per_key_bf16_values", 2, 4)]
+PROLOGUE = [("per_head_scores", 2, 4), ("t_form_scores", 16, 64), ("per_key_bf16_values", 2, 4),
+            ("per_head_bf16_values", 2, 4), ("t_form_bf16_tiny_keys", 16, 64)]
 
 
 @pytest.mark.parametrize("form,H,HV", PROLOGUE, ids=[f[0] for f in PROLOGUE])
@@ -234,11 +235,22 @@ def test_chunked_prologue_hand_over(form, H, HV):
     """Operands the prologue splits into fp16 (hi, lo) past the fp16 range:
     scores scale q.k of unnormalised keys near 1e5 (per-head form, gated
     rule; 8 pairs with W and U in the records, 128 pairs in the T form), and
-    bf16 values near 5e5 (per-key form, Gated DeltaNet-2 rule).  The prologue
-    flags the request's pairs and the recurrent kernel computes them; the
-    other request stays on the chunked path."""
+    bf16 values near 5e5 (per-key form, Gated DeltaNet-2 rule).  And bf16
+    activations the per-head form cannot read as fp16 exactly: values near
+    5e5, keys near 1e-7 (below fp16's exact range; L2-normalised, so the
+    method itself is indifferent to their size).  The prologue flags the
+    request's pairs and the recurrent kernel computes them; the other request
+    stays on the chunked path."""
     T0 = 400
-    if form != "per_key_bf16_values":
+    if form == "per_head_bf16_values":
+        case = _case(50, [T0, 200], dtype="bf16", H=H, HV=HV)
+        case["v"][:T0] = case["v"][:T0] * np.float32(2.0 ** 17)  # stays on the bf16 grid
+        assert float(np.max(np.abs(case["v"][:T0]))) > 65504.0
+    elif form == "t_form_bf16_tiny_keys":
+        case = _case(51, [T0, 200], dtype="bf16", H=H, HV=HV)
+        case["k"][:T0] = case["k"][:T0] * np.float32(2.0 ** -23)  # stays on the bf16 grid
+        assert float(np.max(np.abs(case["k"][:T0]))) < 2.0 ** -17
+    elif form != "per_key_bf16_values":
         case = _case(48, [T0, 200], update_rule="gated", gate_activation="none", beta_activation="none",
                      qk_l2_norm=0, H=H, HV=HV)
         rng = np.random.default_rng(48)
