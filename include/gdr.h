@@ -98,8 +98,11 @@ typedef enum {
 
 /* Activation dtypes.  bf16 goes beyond the pages' type list (fp32, fp16;
  * README, Type constraints): the loads widen it exactly to fp32 and the
- * output is rounded to nearest even on store; on the chunked kernels bf16
- * takes the per-key form, whose prologue works on fp32 values. */
+ * output is rounded to nearest even on store.  The chunked kernels read it
+ * as fp16 when the decay is per head (a (request, head) pair holding a
+ * value fp16 cannot represent exactly, outside magnitudes 2^-17 to 65504,
+ * is computed by the recurrent kernel instead) and widen it to fp32 in the
+ * per-key form. */
 typedef enum { GDR_F32 = 0, GDR_F16 = 1, GDR_BF16 = 2 } gdr_dtype;
 
 typedef enum {
