@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_token_amd import workloads
-from tests.gpu_helpers import (TOL_BF16_O, TOL_CHUNKED, TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward, say,
-                               sub_case, to_dev)
+from tests.gpu_helpers import (TOL_BF16_O, TOL_CHUNKED, TOL_F16, TOL_F32, assert_close, gpu_forward, oracle_forward,
+                               rel_err, say, sub_case, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -745,3 +745,33 @@ def test_chunked_workspace_beyond_4gib():
     offsets) and 1 GiB q/k/v; the oracle checks sampled heads."""
     case = workloads.long_prefill(T=262144)
     _sampled(case, "chunked", [(0, [0]), (0, [15])], TOL_CHUNKED, "chunked 262k tokens")
+
+
+@pytest.mark.parametrize("algo", ["recurrent", "decode"])
+def test_l2_norm_epsilon_placement(algo):
+    """qk L2-norm of rows whose squared norm is the size of the epsilon
+    (README, Attributes qk_l2_norm: epsilon 1e-12).  The kernels follow the
+    oracle's reading x / sqrt(sum x^2 + 1e-12): a key or query scaled to
+    squared norm 1e-12 normalises to length 1/sqrt(2).  x / max(|x|, 1e-12)
+    would give length 1 here; the check below shows that this case tells the
+    two readings apart by far more than the bar."""
+    lengths = [1] * 8 if algo == "decode" else [40, 23]
+    case = _small(60, lengths=lengths, dtype=np.float32)
+    T = case["q"].shape[0]
+    tiny = [0, T - 1]
+    for arr in ("k", "q"):
+        x = case[arr][tiny].astype(np.float64)
+        case[arr][tiny] = (x / np.linalg.norm(x, axis=-1, keepdims=True) * 1e-6).astype(np.float32)
+    say("case l2-norm epsilon placement algo=%s" % algo)
+    o, st = gpu_forward(case, algo)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_F32, "epsilon placement o")
+    assert_close(st, rs, TOL_F32, "epsilon placement state")
+    # the other reading: those rows at full length
+    alt = dict(case)
+    for arr in ("k", "q"):
+        alt[arr] = case[arr].copy()
+        x = alt[arr][tiny].astype(np.float64)
+        alt[arr][tiny] = (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
+    ao, ast = oracle_forward(alt)
+    assert max(rel_err(ao, ro), rel_err(ast, rs)) > 100 * TOL_F32, "the case separates the two readings"
