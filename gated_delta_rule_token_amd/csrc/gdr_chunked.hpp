@@ -316,9 +316,11 @@ __device__ __forceinline__ void prep_block(int HV, int64_t &ci, int &h)
 // requests that get no chunks although they have tokens (ranges that overlap
 // after a decreasing cu_seqlens entry); the recurrent kernel takes those.
 // Prefix sums are 64-bit: overlapping ranges can sum to B * ceil(T / 64).
+constexpr int ORDER_MAX = 1024;
 __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *off, int32_t *redo)
 {
     __shared__ int64_t s[256];
+    __shared__ int32_t s_cnt[ORDER_MAX];
     __shared__ int64_t carry;
     __shared__ unsigned long long best;  // largest granted inclusive prefix
     const int tid = threadIdx.x;
@@ -359,6 +361,28 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
     const int64_t top = (int64_t)best;
     for (int b = tid; b < p.B; b += 256) off[b] = chunk_offset(off[b], top);
     if (tid == 0) off[p.B] = chunk_offset(carry, top);
+    __syncthreads();
+    // The scans take the requests longest first (order[i] = the request of
+    // rank i by granted chunks, ties by index): with one workgroup per CU a
+    // long request placed late in the batch would start only when an early
+    // one ends and finish last.  Rank by counting, up to ORDER_MAX requests;
+    // past that, batch order.
+    int32_t *order = redo + (size_t)p.B * p.HV;
+    if (p.B <= ORDER_MAX) {
+        for (int b = tid; b < p.B; b += 256) s_cnt[b] = off[b + 1] - off[b];
+        __syncthreads();
+        for (int b = tid; b < p.B; b += 256) {
+            const int c = s_cnt[b];
+            int rank = 0;
+            for (int x = 0; x < p.B; ++x) {
+                const int cx = s_cnt[x];
+                rank += (cx > c || (cx == c && x < b)) ? 1 : 0;
+            }
+            order[rank] = b;
+        }
+    } else {
+        for (int b = tid; b < p.B; b += 256) order[b] = b;
+    }
 }
 
 // ------------------------------------------------------------------ phase 1
@@ -1366,7 +1390,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
     const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
     const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
     if (gi >= (int64_t)p.B * HV * nsg) return;
-    const int bh = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    // group -> (request, head): requests longest first (k_chunk_table's order)
+    const int pr = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    const int bh = off[p.B + 1 + (size_t)p.B * HV + pr / HV] * HV + pr % HV;
     const int tile = unit % NTILE;
     const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
     if (mode == SEG_TRANS && seg == 0) return;  // segment 0 has no transition tiles
@@ -1829,7 +1855,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
     const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
     const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
     if (gi >= (int64_t)p.B * HV * nsg) return;
-    const int bh = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    // group -> (request, head): requests longest first (k_chunk_table's order)
+    const int pr = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
+    const int bh = off[p.B + 1 + (size_t)p.B * HV + pr / HV] * HV + pr % HV;
     const int tile = unit % NTILE;
     const int mode = sg.pass != 1 ? SEG_REAL : unit < NTILE ? (seg == 0 ? SEG_REAL : SEG_CARRY) : SEG_TRANS;
     if (mode == SEG_TRANS && seg == 0) return;
@@ -2338,7 +2366,8 @@ __global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int3
 // segmented and few-pair scans keep W and U in the records.
 static bool t_form(bool per_key, int B, int HV, int nseg) { return !per_key && nseg <= 1 && (int64_t)B * HV >= 128; }
 
-// Workspace: chunk table (off[B + 1], then the (B * HV) hand-over flags) |
+// Workspace: chunk table (off[B + 1], the (B * HV) hand-over flags, the scan
+// order of the B requests) |
 // records of every (chunk, value head) (Rec<true>, Rec<false> or RecT) |
 // per-head form: K^T and q (T form: K^T only) of every (chunk, q/k head) |
 // segment states | staging for in-place final states (one 128 x 128 fp32
@@ -2347,7 +2376,7 @@ static bool t_form(bool per_key, int B, int HV, int nseg) { return !per_key && n
 struct Layout {
     size_t kq, seg, stage, total;
 };
-static size_t table_bytes(int B, int HV) { return ((size_t)(B + 1) * 4 + (size_t)B * HV * 4 + 255) / 256 * 256; }
+static size_t table_bytes(int B, int HV) { return ((size_t)(B + 1) * 4 + (size_t)B * HV * 4 + (size_t)B * 4 + 255) / 256 * 256; }
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 static Layout layout(int64_t T, int B, int H, int HV, bool per_key, int nseg)
