@@ -91,6 +91,24 @@ def test_overlapping_requests(name, T, cu, algo):
             "row %d (requests %s): max err %.3e" % (t, cover[t], float(np.max(err)) / scale)
 
 
+# ------------------------------------------------------------------ request order
+@pytest.mark.parametrize("B", [900, 1100], ids=["ranked", "batch_order"])
+def test_many_requests_any_order(B):
+    """The scans take requests longest first (ranked by chunk count, ties by
+    index) up to 1,024 requests and in batch order past that: ragged lengths
+    0-300 with many ties, empty requests included; every request's o rows
+    and final state against the oracle."""
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(0, 301, size=B)
+    lengths[rng.integers(0, B, size=B // 10)] = 0
+    case = _case(52 + B, lengths.tolist(), H=1, HV=2)
+    say("case %d requests, %d tokens" % (B, int(lengths.sum())))
+    o, st = gpu_forward(case, "chunked")
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "%d requests o" % B)
+    assert_close(st, rs, TOL_CHUNKED, "%d requests state" % B)
+
+
 # ------------------------------------------------------------------ packing and hand-off
 @pytest.mark.parametrize("per_key", [False, True], ids=["per_head", "per_key_form"])
 def test_chunked_packed_equals_separate(per_key):
