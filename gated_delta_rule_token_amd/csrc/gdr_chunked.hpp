@@ -20,7 +20,7 @@
 //                  K Q^T and K K^T on 16x16x32 f16 MFMA (q/k are fp16, so the
 //                  products are exact up to fp32 accumulation), the unit
 //                  lower-triangular solve for [W | U] by fp32 forward
-//                  substitution (one column per thread), the per-token
+//                  substitution (four lanes per column), the per-token
 //                  scalars, and every operand of the scan written in the
 //                  order the scan's lanes load it.
 //   k_chunk_scan   one workgroup per (request, head, 32 state rows), chunks
@@ -242,6 +242,56 @@ struct SplitWatch {
     }
     __device__ __forceinline__ bool over() const { return big >= __float_as_uint(SPLIT_LIMIT); }
 };
+
+// T = (I + A)^-1 of a chunk's strictly lower triangular 64 x 64 matrix A
+// (rows of LA floats) by forward substitution down the rows,
+//   T_tc = [t == c] - sum_{s<t} A_ts T_sc,
+// on the four waves of a 256-thread workgroup: wave w takes the columns
+// 16 w .. 16 w + 15 with four lanes each, lane q of a column the terms
+// s = q (mod 4) of every row, and a quad reduction completes the row.  The
+// caller stores A with each row permuted, entry s at a_pos(s) = 16 (s mod 4)
+// + s / 4, so that a lane reads its terms as 16-byte vectors; it must store
+// the diagonal 4 x 4 groups of A in full (zeros on and above the diagonal),
+// the only entries at or above the diagonal that the substitution reads.
+// T is written over A in natural order after a barrier (zeros above the
+// diagonal); each lane watches its column's entries and, scaled by the
+// column's weight `wc`, the products the caller forms from them.
+__device__ __forceinline__ int a_pos(int s) { return 16 * (s & 3) + (s >> 2); }
+
+template <int LA>
+__device__ __forceinline__ void solve_unit_lower(float (*sA)[LA], int tid, float wc, SplitWatch &wt)
+{
+    const int lane = tid & 63, c = 16 * (tid >> 6) + (lane >> 2), q = lane & 3;
+    float x[CH / 4];  // x[i] = T_{4 i + q, c}
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) x[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+        // terms i < ceil(t / 4): s = 4 i + q < t, or s in t's group (A_ts = 0, x = 0 yet)
+        const int nt = (t + 3) >> 2;
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < nt; j += 4) {
+            const f4v a = *reinterpret_cast<const f4v *>(&sA[t][16 * q + j]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (j + u < nt) {
+                    if (u & 1) r1 = fmaf(a[u], x[j + u], r1);
+                    else r0 = fmaf(a[u], x[j + u], r0);
+                }
+        }
+        float r = r0 + r1;
+        r += dpp_mov<0xB1>(r);  // the quad's four partial sums
+        r += dpp_mov<0x4E>(r);
+        const float xt = (t == c ? 1.f : 0.f) - r;
+        if ((t & 3) == q) x[t >> 2] = xt;
+        wt.note(xt);
+    }
+    wt.note(__uint_as_float(wt.big) * wc);
+    lds_barrier();  // every wave has read A
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) sA[4 * i + q][c] = x[i];
+}
 
 __device__ __forceinline__ int tile_exponent(float m)
 {
@@ -583,7 +633,10 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
                 *reinterpret_cast<h4 *>(rec + po) = hi;
                 *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
             }
-            if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
+            if constexpr (RET) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sA[t][a_pos(s0 + i)] = av[i];
+            }
         }
         post(wp);
     }
@@ -604,29 +657,14 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         }
         return;
     } else {
-        // ---- [W | U] = T [diag(beta gamma / |k|) K | diag(beta) V],  T = (I + A)^-1.
-        // T by column substitution on wave 0 (lane j = column j):
-        //   T_tj = [t == j] - sum_{s<t} A_ts T_sj,
-        // T's row t is written over A's row t once every lane has read it (rows
-        // past t are read later, row t never again); zeros above the diagonal.
-        if (wave == 0) {
-            float x[CH];
-            SplitWatch wt;  // column `lane` of T
-#pragma unroll
-            for (int t = 0; t < CH; ++t) {
-                float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
-                x[t] = (r[0] + r[1]) + (r[2] + r[3]);
-                sA[t][lane] = x[t];
-                if constexpr (!TF) wt.note(x[t]);
-            }
-            // the column times its weight (split beside T below) peaks where
-            // |T| does: rounding is monotone (the T form watches T as it exports it)
-            if constexpr (!TF) {
-                wt.note(__uint_as_float(wt.big) * sBeta[lane]);
-                post(wt);
-            }
+        // ---- [W | U] = T [diag(beta gamma / |k|) K | diag(beta) V],  T = (I + A)^-1,
+        // on all four waves.  The column times its weight (split beside T below)
+        // peaks where |T| does: rounding is monotone (the T form watches T as it
+        // exports it).
+        {
+            SplitWatch wt;
+            solve_unit_lower(sA, tid, sBeta[16 * wave + (lane >> 2)], wt);
+            if constexpr (!TF) post(wt);
         }
         lds_barrier();  // T is complete
         if constexpr (TF) {
@@ -1194,7 +1232,10 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
             const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
             *reinterpret_cast<h4 *>(rec + po) = hi;
             *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
-            if constexpr (RET) *reinterpret_cast<f4v *>(&sA[t][s0]) = av;
+            if constexpr (RET) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sA[t][a_pos(s0 + i)] = av[i];
+            }
         }
     }
     post(wp);
@@ -1225,26 +1266,16 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
         return;
     } else {
         // ---- [W | U] = T [l o e^G | diag(w) V],  T = (I + A)^-1, as in the
-        // per-head prologue: wave 0 forms T by column substitution over A's
-        // rows, then wave w takes key columns and value rows 32 w .. 32 w + 31
+        // per-head prologue: the four waves form T by forward substitution,
+        // then wave w takes key columns and value rows 32 w .. 32 w + 31
         // on the matrix cores (W: three split products, U: V is exact in the
         // activation dtype only when that is fp16, so both operands of U get
         // (hi, lo) planes for bf16).
-        if (wave == 0) {
-            float x[CH];
-            SplitWatch wt;  // column `lane` of T
-#pragma unroll
-            for (int t = 0; t < CH; ++t) {
-                float r[4] = {t == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s2 = 0; s2 < t; ++s2) r[s2 & 3] = fmaf(-sA[t][s2], x[s2], r[s2 & 3]);
-                x[t] = (r[0] + r[1]) + (r[2] + r[3]);
-                sA[t][lane] = x[t];
-                wt.note(x[t]);
-            }
+        {
             // the column times its weight (split beside T below) peaks where
             // |T| does: rounding is monotone
-            wt.note(__uint_as_float(wt.big) * sWt[lane]);
+            SplitWatch wt;
+            solve_unit_lower(sA, tid, sWt[16 * wave + (lane >> 2)], wt);
             post(wt);
         }
         lds_barrier();  // T is complete
@@ -2426,12 +2457,18 @@ static void launch_scan(const Params &p, int32_t *off, const char *rec, const ch
 // row tile of a head, so from 128 pairs on (at least two 64-row workgroups
 // per CU) the single pass takes 64-row tiles: varlen 8 x 32 heads 0.98 ->
 // 0.94 ms, 4 x 32 heads per-key 0.99 -> 0.94 ms; with fewer pairs they leave
-// CUs idle (16 heads in 4 segments: pass 2 398 -> 542 us).  A segmented scan runs pass 1 (carry and transition tiles: twice
-// the workgroups of pass 2) in 32-row tiles and pass 2 by the same rule as a
-// single pass over its (request, head, segment) groups: two workgroups of
-// this kernel on one CU share its vector-memory pipeline and each chunk step
-// then takes about twice as long (measured on MI355X, 65,536 tokens x 16
-// heads in 3 segments: 1.82 ms with 32-row pass-1 tiles, 1.89 ms with 16-row).
+// CUs idle (16 heads in 4 segments: pass 2 398 -> 542 us).  A segmented scan
+// runs pass 1 (carry and transition tiles: twice the workgroups of pass 2) in
+// 32-row tiles and pass 2 by the same rule as a single pass over its
+// (request, head, segment) groups: two workgroups of this kernel on one CU
+// share its vector-memory pipeline and each chunk step then takes about twice
+// as long (measured on MI355X, 65,536 tokens x 16 heads in 3 segments: 1.82 ms
+// with 32-row pass-1 tiles, 1.89 ms with 16-row).  Pass 1 takes 64-row tiles
+// when that gives 192 to 256 workgroups (one per CU on 3/4 of the chip or
+// more), which then read each chunk's operands half as often: 65,536 tokens
+// x 16 heads in 4 segments 1.75 -> 1.69 ms, in 5 segments 1.51 -> 1.50 ms;
+// fewer (3 segments, 128 workgroups: 1.64 -> 1.97 ms) or more (6 segments,
+// 320: 1.91 -> 2.07 ms) lose.
 template <typename TA, int RULE, bool PK>
 static void launch_scans(const Params &p, int32_t *off, const char *rec, const char *kq, float *xs, float *stage,
                          int nseg, hipStream_t s)
@@ -2445,7 +2482,11 @@ static void launch_scans(const Params &p, int32_t *off, const char *rec, const c
         else launch_scan<TA, RULE, 4, PK, true>(p, off, rec, kq, one, s);  // the T form (t_form)
         return;
     }
-    launch_scan<TA, RULE, 2, PK, false>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
+    const int64_t pass1_64 = pairs * (nseg - 1) * 4;  // pass-1 workgroups in 64-row tiles
+    if (pass1_64 >= 192 && pass1_64 <= 256)
+        launch_scan<TA, RULE, 4, PK, false>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
+    else
+        launch_scan<TA, RULE, 2, PK, false>(p, off, rec, kq, ScanSeg{nseg, 1, xs, stage}, s);
     if (nseg > 2) {
         const int64_t blocks = pairs * 8;
         hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)blocks), dim3(256), 0, s, p, off, ScanSeg{nseg, 0, xs, stage});

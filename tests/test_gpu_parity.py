@@ -452,6 +452,24 @@ def test_chunked_segmented_scan(nseg):
     assert np.array_equal(gpu_forward(case, "chunked", scan_segments=nseg)[1], st), "deterministic"
 
 
+@pytest.mark.parametrize("nseg,per_key", [(4, False), (5, False), (5, True)])
+def test_chunked_segmented_wide_pass1(nseg, per_key):
+    """16 (request, head) pairs in 4 or 5 segments: pass 1 then runs in 64-row
+    tiles (192 or 256 workgroups), per head and per key, against the oracle
+    and the one-pass scan."""
+    rule = "gated_delta_v2" if per_key else "gated_delta"
+    case = _mild(workloads.random_case(80 + nseg + 2 * per_key, lengths=[64 * 26 + 41], H=4, HV=16, DK=128,
+                                       DV=128, dtype=np.float16, update_rule=rule, per_key=per_key),
+                 86, per_key=per_key)
+    say("case segmented scan, 64-row pass 1: nseg=%d per_key=%s" % (nseg, per_key))
+    o, st = gpu_forward(case, "chunked", scan_segments=nseg)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "wide pass 1 o")
+    assert_close(st, rs, TOL_CHUNKED, "wide pass 1 state")
+    o1, st1 = gpu_forward(case, "chunked", scan_segments=1)
+    assert_close(st, st1, TOL_CHUNKED, "wide pass 1 vs one pass state")
+
+
 @pytest.mark.parametrize("rule", ["linear", "gated", "delta", "gated_delta"])
 def test_chunked_segmented_varlen_slab(rule):
     """Segmented scans over varlen requests in a slot slab: requests shorter
