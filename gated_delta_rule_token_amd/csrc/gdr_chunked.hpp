@@ -103,24 +103,25 @@ constexpr uint32_t R_W = Rec<false>::W, R_U = Rec<false>::U, R_P = Rec<false>::P
 
 // Record of one (chunk, value head) in the T form (per-head decay, fp16
 // activations): the scan forms W S^T and U itself as T (beta V - w K S^T)
-// from the raw k and v rows, so the record holds only what needs the whole
-// chunk at once:
+// from the raw k and v rows, and P from the raw q and k rows, so the record
+// holds only what needs the whole chunk at once:
 //   T   T = (I + A)^-1 (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr,
 //       tokens 32 ks + 8 lq .. +7 (blocks tb < 2, ks = 1 lie above the diagonal: not stored)
-//   P   as in Rec<false>
 //   SC  fp32: kd[64], gq[64], gamma_C, max |v| at SC_VMAX, beta[64] at SCT_BETA,
-//       w[64] at SCT_RW (w = beta gamma / |k|, the row weight of K in W)
+//       w[64] at SCT_RW (w = beta gamma / |k|, the row weight of K in W), and
+//       P's per-token factors: G[64] at SCT_G (cumulative log decay in log2
+//       units) with its rounding error at SCT_GL, 1 / |k| [64] at SCT_IK,
+//       scale / |q| [64] at SCT_QS
 // plus, once per (chunk, q/k head), K^T in fragment order as KQ::KT below
 // (16 KB: the state update's left operand, which the k rows give only
 // through a transpose).
 struct RecT {
     static constexpr uint32_t T = 0;
-    static constexpr uint32_t P = 16 * 1024;
-    static constexpr uint32_t SC = 32 * 1024;
-    static constexpr uint32_t SIZE = SC + 1536;
+    static constexpr uint32_t SC = 16 * 1024;
+    static constexpr uint32_t SIZE = SC + 2560;
     static constexpr uint32_t KT_SIZE = 16 * 1024;
 };
-constexpr int SCT_BETA = 256, SCT_RW = 320;
+constexpr int SCT_BETA = 256, SCT_RW = 320, SCT_G = 384, SCT_IK = 448, SCT_QS = 512, SCT_GL = 576;
 struct KQ {
     static constexpr uint32_t KT = 0, Q = 16 * 1024, SIZE = 32 * 1024;
 };
@@ -130,15 +131,37 @@ __device__ __forceinline__ f4v mfma16(h8 a, h8 b, f4v c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// fp32 -> (hi, lo) fp16 pair with hi + lo ~ x to about 22 bits
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr double LOG2E_D = 1.4426950408889634;
+
+// 2^x on the transcendental unit (one instruction; results below the normal
+// range flush toward zero, which only ever drops terms smaller than 1e-38)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> (hi, lo) fp16 pairs with hi + lo ~ x to about 22 bits: hi = fp16(x)
+// (nearest), lo = fp16(x - hi), where x - hi is exact in fp32.  Two values at
+// a time, in three instructions: one packed conversion gives both hi, then
+// v_fma_mix{lo,hi}_f16 forms each lo from its hi half and x.  The three are
+// one asm block that takes x as fp32 registers: left to itself, contraction
+// fuses the product or sum that feeds a split into the conversion of one part
+// and not of the other, and within half an fp32 unit of an fp16 rounding
+// midpoint the two parts then disagree by a unit in the last fp16 place
+// (measured: one state entry in error by 5e-4 of itself).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    asm("v_cvt_pk_f16_f32 %0, %2, %3\n\t"
+        "v_fma_mixlo_f16 %1, %0, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %1, %0, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(hi), "=&v"(lo)
+        : "v"(x0), "v"(x1));
+}
 __device__ __forceinline__ void split8(const float (&x)[8], h8 &hi, h8 &lo)
 {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const half_t h = (half_t)x[i];
-        hi[i] = h;
-        lo[i] = (half_t)(x[i] - (float)h);
-    }
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    hi = __builtin_bit_cast(h8, u4v{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(h8, u4v{l[0], l[1], l[2], l[3]});
 }
 
 __device__ __forceinline__ h8 ld_h8(const half_t *p) { return *reinterpret_cast<const h8 *>(p); }
@@ -191,11 +214,11 @@ __device__ __forceinline__ T ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // four fp32 -> (hi, lo) fp16 quads
 __device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
 {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (half_t)x[i];
-        lo[i] = (half_t)(x[i] - (float)hi[i]);
-    }
+    uint32_t h0, h1, l0, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    hi = __builtin_bit_cast(h4, u2v{h0, h1});
+    lo = __builtin_bit_cast(h4, u2v{l0, l1});
 }
 
 // Column index of a swizzled LDS row of fp16: the 16-byte chunk (8 values)
@@ -438,7 +461,7 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // ------------------------------------------------------------------ phase 1
 // 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
-// TF: the T form (RecT: T, P and the scalars; no W, U, K^T or q), else Rec<false>
+// TF: the T form (RecT: T and the scalars; no W, U, P or q), else Rec<false>
 // plus the K^T and q area.
 // TI: the activations' dtype (bf16 rows are converted to fp16 as they load;
 // a pair with a value fp16 cannot hold exactly goes to the recurrent kernel).
@@ -461,7 +484,10 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     half_t(*sQ)[LD] = reinterpret_cast<half_t(*)[LD]>(sm + (TF ? 1 : 2) * SLOT);
     float(*sA)[LA] = reinterpret_cast<float(*)[LA]>(sm + (TF ? 1 : 2) * SLOT);
     half_t(*sW)[CH][D128] = reinterpret_cast<half_t(*)[CH][D128]>(sm);  // [hi, lo][token][key, swizzled], after the solve
-    __shared__ float sG[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
+    // G_t = sG + sGl (the cumulative log decay and its fp32 rounding error).
+    // LDS per workgroup: 53,760 bytes at most for three workgroups per CU
+    // (measured on MI355X: 512 bytes more cost the W/U form's prologue 18 %).
+    __shared__ float sG[CH], sGl[CH], sBeta[CH], sIk[CH], sIq[CH], sRw[CH];
 
     const int HV = p.HV, H = p.H;
     int64_t ci;
@@ -476,7 +502,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     const int qh = (int)(((int64_t)h * H) / HV);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
-    constexpr uint32_t OP = TF ? RecT::P : R_P, OSC = TF ? RecT::SC : R_SC;
+    constexpr uint32_t OSC = TF ? RecT::SC : R_SC;
     char *rec = ws + ((size_t)ci * HV + h) * (TF ? RecT::SIZE : WS_REC);
     // K^T and q once per (chunk, q/k head): the group's first value head writes them
     char *kq = kqs + ((size_t)ci * H + qh) * (TF ? RecT::KT_SIZE : KQ::SIZE);
@@ -508,21 +534,33 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
             ldv[i] = ld_as_h8(v + ((size_t)(t0 + r) * HV + h) * D128 + c8, exact);
         }
     }
-    // ---- per-token log decay (cumulated over the chunk by a 64-lane scan) and update rate
+    // ---- per-token log decay (cumulated over the chunk by a 64-lane scan) and
+    // update rate.  The sums run in fp64: in a strongly decaying chunk two
+    // prefix sums of hundreds of nats differ by a few late in the chunk, and
+    // their fp32 roundings alone would put relative errors of 1e-5 .. 1e-4
+    // into the decay factors between them (kd, A, P).  G_t is kept as fp32
+    // (hi, lo), so that (hi_t - hi_s) + (lo_t - lo_s) -- the first difference
+    // exact whenever it is small against the sums -- recovers G_t - G_s.
+    float gend = 0.f;  // G_end - G_t of this thread's token t = tid < CH (kd below)
     if (tid < CH) {
         const int t = tid;
-        float g = 0.f, bt = 0.f;
+        float gt = 0.f, bt = 0.f;
         if (t < n) {
             const size_t th = (size_t)(t0 + t) * HV + h;
-            if constexpr (DEC) g = log_decay(p, th, h);
+            if constexpr (DEC) gt = log_decay(p, th, h);
             bt = BETA ? update_rate(p, th) : 1.f;
         }
+        double g = gt;
 #pragma unroll
         for (int o = 1; o < CH; o <<= 1) {
-            const float y = __shfl_up(g, o, CH);
+            const double y = __shfl_up(g, o, CH);
             if (t >= o) g += y;
         }
-        sG[t] = g;  // inclusive cumulative log decay inside the chunk
+        const double ge = __shfl(g, n - 1, CH);
+        const float gh = (float)g;
+        sG[t] = gh;  // inclusive cumulative log decay inside the chunk
+        sGl[t] = (float)(g - (double)gh);
+        gend = (float)(ge - g);
         sBeta[t] = bt;
     }
 #pragma unroll
@@ -582,17 +620,23 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         const float gl = sG[n - 1];
         sRw[t] = sBeta[t] * expf(sG[t]) * sIk[t];  // row scale of K in W's right-hand side
         float *sc = reinterpret_cast<float *>(rec + OSC);
-        sc[t] = t < n ? expf(gl - sG[t]) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
+        sc[t] = t < n ? expf(gend) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
         sc[CH + t] = scale * sIq[t] * expf(sG[t]);        // gq: read-out weight of the incoming state
         if (t == 0) sc[2 * CH] = DEC ? expf(gl) : 1.f;    // gamma_C
         if constexpr (TF) {
             sc[SCT_BETA + t] = sBeta[t];  // zero past the request's end, like w
             sc[SCT_RW + t] = sRw[t];
+            const double g2 = ((double)sG[t] + (double)sGl[t]) * LOG2E_D;
+            sc[SCT_G + t] = (float)g2;
+            sc[SCT_GL + t] = (float)(g2 - (double)(float)g2);
+            sc[SCT_IK + t] = sIk[t];
+            sc[SCT_QS + t] = scale * sIq[t];
         }
     }
 
-    // ---- K Q^T and K K^T, 16 x 16 tiles (wave = token block tb, tiles sb <= tb);
-    // the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr]
+    // ---- K Q^T (not in the T form: its scan forms P) and K K^T, 16 x 16 tiles
+    // (wave = token block tb, tiles sb <= tb); the accumulators hold
+    // [s = 16 sb + 4 lq + i][t = 16 tb + lr]
     {
         const int tb = wave;
         f4v accq[4], acck[4];
@@ -603,7 +647,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
 #pragma unroll
                 for (int kk = 0; kk < D128; kk += 32) {
                     const h8 ak = ld_h8(&sK[16 * sb + lr][kk + lk]);
-                    accq[sb] = mfma16(ak, ld_h8(&sQ[16 * tb + lr][kk + lk]), accq[sb]);
+                    if constexpr (!TF) accq[sb] = mfma16(ak, ld_h8(&sQ[16 * tb + lr][kk + lk]), accq[sb]);
                     if constexpr (RET) acck[sb] = mfma16(ak, ld_h8(&sK[16 * tb + lr][kk + lk]), acck[sb]);
                 }
             }
@@ -618,18 +662,18 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + i;
-                const float dg = (s <= t) ? expf(sG[t] - sG[s]) : 0.f;
+                const float dg = (s <= t) ? expf((sG[t] - sG[s]) + (sGl[t] - sGl[s])) : 0.f;
                 pv[i] = scale * sIq[t] * sIk[s] * dg * accq[sb][i];
                 av[i] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
             }
-            h4 hi, lo;
-            wp.note(pv);
-            split4(pv, hi, lo);
             // P rows in fragment order: block (tb * 2 + s0 / 32) * 2 + plane; the
             // fragments of token blocks 0, 1 against tokens 32 .. 63 are all zero
             // and are not stored (the scan reads zero past the record instead)
-            const uint32_t po = OP + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
-            if (tb >= 2 || sb < 2) {
+            if (!TF && (tb >= 2 || sb < 2)) {
+                h4 hi, lo;
+                wp.note(pv);
+                split4(pv, hi, lo);
+                const uint32_t po = R_P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
                 *reinterpret_cast<h4 *>(rec + po) = hi;
                 *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
             }
@@ -810,11 +854,6 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
 // after the Gram products A takes Q's rows and V takes K's, and after the
 // solve the W (hi, lo) rows take Q's and G's.
 constexpr float DIAG_NATS = 80.f;
-constexpr float LOG2E = 1.4426950408889634f;
-
-// 2^x on the transcendental unit (one instruction; results below the normal
-// range flush toward zero, which only ever drops terms smaller than 1e-38)
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename TA, int RULE, bool PKG>
 __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_t *__restrict__ off,
@@ -1013,6 +1052,23 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
     }
     lds_barrier();
 
+    // A and P come in 16 x 16 blocks (sb <= tb); wave w takes pairs w, w + 4,
+    // w + 8 (slots 0, 1, 2).  The erase gate rows of a slot's left operands
+    // (token 16 tb + lr, key channels 32 lq .. 32 lq + 31) are loaded one slot
+    // ahead, slot 0's while the operands below are built.
+    constexpr int8_t PTB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int8_t PSB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    f4v ebuf[2][8];
+    auto load_eb = [&](int slot, f4v(&e)[8]) {
+        const int pi = wave + 4 * slot;
+        if (pi < 10) {
+            const float *er = erase_row(16 * PTB[pi] + lr);
+#pragma unroll
+            for (int kq = 0; kq < 8; ++kq) e[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
+        }
+    };
+    if constexpr (V2) load_eb(0, ebuf[0]);
+
     // ---- operands built from G: Kd^T and Qg fragments (4 + 4 per thread), gamma_C
     SplitWatch wg;
 #pragma unroll
@@ -1064,16 +1120,18 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
                 for (int x = 0; x < 8; ++x) ev[c][ks][x] = erase_row(32 * ks + 8 * lq + x)[16 * (2 * wave + c) + lr];
     }
 
-    // ---- A and P, 16 x 16 blocks (sb <= tb) on the fp32 matrix cores; wave w
-    // takes pairs w, w + 4, w + 8.  Lane (lr, lq) sums key channels 32 lq .. 32 lq + 31,
-    // and the accumulators hold [s = 16 sb + 4 lq + i][t = 16 tb + lr] without the
-    // per-token factors (applied below).
-    constexpr int8_t PTB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int8_t PSB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    // ---- A and P blocks on the fp32 matrix cores.  Lane (lr, lq) sums key
+    // channels 32 lq .. 32 lq + 31, and the accumulators hold
+    // [s = 16 sb + 4 lq + i][t = 16 tb + lr] without the per-token factors
+    // (applied below).
     const int flags = sFlag;
     f4v resA[3], resP[3];
 #pragma unroll
     for (int slot = 0; slot < 3; ++slot) {
+        if constexpr (V2) {
+            if (slot + 1 < 3) load_eb(slot + 1, ebuf[(slot + 1) & 1]);
+        }
+        const f4v(&eb)[8] = ebuf[slot & 1];
         const int pi = wave + 4 * slot;
         resA[slot] = resP[slot] = f4v{0.f, 0.f, 0.f, 0.f};
         if (pi < 10) {
@@ -1098,9 +1156,6 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
                     }
                 } else {
                     // b o k is not a 16-bit value: fp32 products, 4 keys per step
-                    f4v eb[8];
-#pragma unroll
-                    for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
 #pragma unroll
                     for (int kq = 0; kq < 8; ++kq) {
                         const int key = 32 * lq + 4 * kq;
@@ -1139,11 +1194,6 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
                     resP[slot][i] = pq;
                 }
             } else {
-                f4v eb[8];
-                if constexpr (V2) {
-#pragma unroll
-                    for (int kq = 0; kq < 8; ++kq) eb[kq] = *reinterpret_cast<const f4v *>(er + 32 * lq + 4 * kq);
-                }
                 f4v accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kq = 0; kq < 8; ++kq) {
@@ -1860,11 +1910,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 // against the incoming state, Y = K S^T, and Z = diag(beta) V - diag(w) Y,
 //   D = U - W S^T = T Z,
 // since U = T diag(beta) V and W = T diag(w) K (w = beta gamma / |k|).  The
-// record holds T, P and the per-token scalars, the (chunk, q/k head) area
-// K^T; k, v and q are read from the activations.  A chunk step
-// has three barriers: the state tile is in LDS (1), Z is (1.5, retrieving
-// rules only), D is (2).  Workgroup layout, segments, tile scaling and the
-// output path follow k_chunk_scan.
+// output waves form P from the q rows and the k rows that the chain waves
+// park in LDS with the state tile (fp16 products, exact in fp32, scaled per
+// element as the prologue of the W/U form scales them).  The record holds T
+// and the per-token scalars, the (chunk, q/k head) area K^T; k, v and q are
+// read from the activations.  A chunk step has three barriers: the state
+// tile and the k rows are in LDS (1), Z is (1.5, retrieving rules only), D is
+// (2).  Workgroup layout, segments, tile scaling and the output path follow
+// k_chunk_scan.
 template <typename TA, int RULE, int NVB>
 __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *off, const char *ws, const char *kts,
                                                      const ScanSeg sg)
@@ -1877,6 +1930,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
     __shared__ __align__(16) half_t sS[2][TR][D128];
     __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token]: D^T of chunk j in j & 1, Z^T in the other
     __shared__ __align__(16) half_t sDs[2][TR][CH];      // [hi, lo][row][token] (kd D)^T
+    __shared__ __align__(16) half_t sKr[CH][D128];       // chunk j's k rows [token][key]: P's left operand
     __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
     __shared__ float sTM[4][2];                           // per chain wave: max |S0| of its part, max |v|
 
@@ -2041,17 +2095,20 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             }
             f.gc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, RecT::SC + 2 * CH * 4, 0, 0));
         };
-        // D at (tokens 16 bt + 4 lq + i, state row 16 vb + lr) -> D^T and (kd D)^T
+        // D at (tokens 16 bt + 4 lq + i, state row 16 vb + lr) -> D^T and (kd D)^T.
+        // D^T takes the output waves' token order: within each 32-token step,
+        // position 8 lq + 4 h + i holds token 16 h + 4 lq + i (the order in
+        // which their P fragments come out of the matrix cores).
         auto put_d = [&](int bf, f4v dv, f4v kd, int bt, int vb) {
             f4v dsv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsv[i] = kd[i] * dv[i];
-            const int r = 16 * vb + lr, c = 16 * bt + 4 * lq;
+            const int r = 16 * vb + lr, c = 16 * bt + 4 * lq, cp = 32 * (bt >> 1) + 8 * lq + 4 * (bt & 1);
             h4 dh, dl, sh, sl;
             sw.note(dv);
             split4(dv, dh, dl);
-            *reinterpret_cast<h4 *>(&sDt[bf][0][r][sw_tok(lr, c)]) = dh;
-            *reinterpret_cast<h4 *>(&sDt[bf][1][r][sw_tok(lr, c)]) = dl;
+            *reinterpret_cast<h4 *>(&sDt[bf][0][r][sw_tok(lr, cp)]) = dh;
+            *reinterpret_cast<h4 *>(&sDt[bf][1][r][sw_tok(lr, cp)]) = dl;
             sw.note(dsv);
             split4(dsv, sh, sl);
             *reinterpret_cast<h4 *>(&sDs[0][r][sw_tok(lr, c)]) = sh;
@@ -2071,6 +2128,11 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                     *reinterpret_cast<h4 *>(&sS[0][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = hi;
                     *reinterpret_cast<h4 *>(&sS[1][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = lo;
                 }
+            // the chunk's k rows for the output waves' P
+            if (mode == SEG_REAL) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<h8 *>(&sKr[16 * tb + lr][sw_key(lr, 32 * kk + lk)]) = cur.k[kk];
+            }
             lds_barrier();  // 1
             if constexpr (RET) {
                 // ---- B1: Y = K S^T at (tokens 16 tb + 4 lq + i, rows 16 vb + lr), then
@@ -2135,6 +2197,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                     for (int i = 0; i < 4; ++i) dv[i] = um * (float)cur.v[vb][i];
                     put_d(bf, dv, cur.kd, tb, vb);
                 }
+                fetchK(jn, cur);
                 fetchV(jn, cur);
             }
             asm volatile("" ::: "memory");
@@ -2175,10 +2238,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         };
         Ops op;
         if (ce > cb) {
-            if constexpr (RET) {
-                fetchK(cb, op);
-                fetchT(cb, op);
-            }
+            fetchK(cb, op);
+            if constexpr (RET) fetchT(cb, op);
             fetchV(cb, op);
             fetchS(cb, op);
             fetchKt(cb, op);
@@ -2209,8 +2270,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         const float down = ldexpf(1.f, -scale_exp());
         struct Ops {
             h8 q[4];          // q row 16 tb + lr, keys 32 kk + 8 lq .. +7
-            h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
-            float gq;         // gq of this lane's token
+            float gq;         // gq of this lane's token t = 16 tb + lr
+            float pg, pgl, pq;        // G_t (hi, lo) and scale / |q_t|
+            f4v sg[4], sgl[4], sk[4];  // G_s (hi, lo) and 1 / |k_s| of tokens s = 16 sb + 4 lq + i
         };
         const uint32_t offQ = (uint32_t)((16 * tb + lr) * tok_k + 2 * lk);
         const int tok_bytes = HV * D128 * 2;
@@ -2221,9 +2283,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         const bool st_live = lane / LPT < TPS;
         const int st_tok = st_live ? lane / LPT : TPS - 1, st_q = lane % LPT;
         const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
-        const uint32_t offP = RecT::P + (uint32_t)tb * 4 * 1024 + l16;
-        const uint32_t offP1 = tb < 2 ? 0x7FFFF000u : offP + 2048;
         const uint32_t offG = RecT::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
+        const uint32_t offPt = RecT::SC + (uint32_t)(16 * tb + lr) * 4, offPs = RecT::SC + (uint32_t)(4 * lq) * 4;
         auto fetchQ = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = act_rsrc(p.q, p.H, qh, 0, tok_k, D128 * 2, jj);
             bool ok = true;
@@ -2233,13 +2294,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         auto fetchG = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
             f.gq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offG, 0, 0));
-        };
-        auto fetchP = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
+            f.pg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offPt + SCT_G * 4, 0, 0));
+            f.pgl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offPt + SCT_GL * 4, 0, 0));
+            f.pq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offPt + SCT_QS * 4, 0, 0));
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f.ph[ks] = ld_b128<h8>(r, ks ? offP1 : offP);
-                f.pl[ks] = ld_b128<h8>(r, (ks ? offP1 : offP) + 1024);
+            for (int sb = 0; sb < 4; ++sb) {
+                f.sg[sb] = ld_b128<f4v>(r, offPs + (SCT_G + 16 * sb) * 4);
+                f.sgl[sb] = ld_b128<f4v>(r, offPs + (SCT_GL + 16 * sb) * 4);
+                f.sk[sb] = ld_b128<f4v>(r, offPs + (SCT_IK + 16 * sb) * 4);
             }
         };
         auto store_out = [&](int jo) {
@@ -2253,6 +2315,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                 __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok + TPS * ps][8 * st_q]), ro,
                                                        offO + (uint32_t)(TPS * ps * tok_bytes), 0, 0);
         };
+        SplitWatch pw;
         auto step = [&](int j, Ops &cur) {
             const int bf = j & 1;
             const int jn = j + 1 < ce ? j + 1 : j;
@@ -2271,10 +2334,45 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                     acc[vb] = mfma16(shi, cur.q[kk], acc[vb]);
                     acl[vb] = mfma16(slo, cur.q[kk], acl[vb]);
                 }
+            // P while the chain forms D (between barriers 1.5 and 2: the k rows
+            // stay in LDS until the chain's next stage A, after barrier 2)
+            if constexpr (RET) lds_barrier();  // 1.5
+            // ---- P_ts = scale / |q_t| / |k_s| exp(G_t - G_s) q_t . k_s (s <= t) from
+            // the k rows the chain parked and this wave's q rows: K Q^T at
+            // [s = 16 sb + 4 lq + i][t = 16 tb + lr] (fp16 products, exact in
+            // fp32), then (hi, lo) fragments whose element 4 h + i of token step
+            // ks is token 32 ks + 16 h + 4 lq + i (the order of D^T in LDS)
+            h8 ph[2], pl[2];
+            {
+                const int t = 16 * tb + lr;
+                h4 hh[4], hl[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    f4v c4 = {0.f, 0.f, 0.f, 0.f};
+                    if (sb <= tb) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            c4 = mfma16(ld_h8(&sKr[16 * sb + lr][sw_key(lr, 32 * kk + lk)]), cur.q[kk], c4);
+                    }
+                    f4v pv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int sx = 16 * sb + 4 * lq + i;
+                        const float d2 = (cur.pg - cur.sg[sb][i]) + (cur.pgl - cur.sgl[sb][i]);
+                        pv[i] = sx <= t ? cur.pq * cur.sk[sb][i] * ex2(d2) * c4[i] : 0.f;
+                    }
+                    pw.note(pv);
+                    split4(pv, hh[sb], hl[sb]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    ph[ks] = __builtin_shufflevector(hh[2 * ks], hh[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    pl[ks] = __builtin_shufflevector(hl[2 * ks], hl[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
             fetchQ(jn, cur);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (RET) lds_barrier();  // 1.5
             lds_barrier();  // 2
             // ---- O2: O^T = gq O^T + D^T P^T
 #pragma unroll
@@ -2283,19 +2381,20 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             {
                 f4v p3[NVB] = {};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks == 1 && tb < 2) break;  // P is zero there (tokens 32 .. 63 follow t)
 #pragma unroll
                     for (int vb = 0; vb < NVB; ++vb) {
                         const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
                         const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
-                        acc[vb] = mfma16(dhi, cur.ph[ks], acc[vb]);
-                        p3[vb] = mfma16(dlo, cur.ph[ks], p3[vb]);
-                        p3[vb] = mfma16(dhi, cur.pl[ks], p3[vb]);
+                        acc[vb] = mfma16(dhi, ph[ks], acc[vb]);
+                        p3[vb] = mfma16(dlo, ph[ks], p3[vb]);
+                        p3[vb] = mfma16(dhi, pl[ks], p3[vb]);
                     }
+                }
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
             }
-            fetchP(jn, cur);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -2310,7 +2409,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         if (ce > cb) {
             fetchQ(cb, op);
             fetchG(cb, op);
-            fetchP(cb, op);
         }
         {
             const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(o, 0, 0, 0x00020000);
@@ -2321,6 +2419,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             __builtin_amdgcn_s_waitcnt(0xc07f);
             store_out(ce - 1);
         }
+        if (pw.over()) off[p.B + 1 + bh] = 2;  // P past the split range: the recurrent kernel takes the pair
     }
 }
 
@@ -2389,9 +2488,10 @@ __global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int3
 
 // The per-head form has two variants.  With a single-pass scan over 128 or
 // more (request, head) pairs it takes the T form (k_chunk_prep<RULE, true>,
-// k_chunk_scan_t): records of 34 KB per (chunk, value head) instead of 81 KB
-// plus 32 KB of K^T and q per (chunk, q/k head), at the price of one more
-// product on the scan's serial chain per chunk.  Measured on MI355X in one
+// k_chunk_scan_t): records of 18 KB per (chunk, value head) instead of 81 KB
+// plus 16 KB of K^T instead of 32 KB of K^T and q per (chunk, q/k head), at
+// the price of one more product on the scan's serial chain per chunk and P
+// formed by the output waves.  Measured on MI355X in one
 // session: the varlen workload (8 requests, 32 heads) 0.974 -> 0.924 ms; the
 // 65,536-token sequence (16 heads, 5 scan segments) 1.53 -> 1.65 ms, so
 // segmented and few-pair scans keep W and U in the records.
