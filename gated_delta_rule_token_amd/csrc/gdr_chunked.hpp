@@ -266,6 +266,22 @@ struct SplitWatch {
     __device__ __forceinline__ bool over() const { return big >= __float_as_uint(SPLIT_LIMIT); }
 };
 
+// The scans' watch: a float maximum of |x| (v_max3_f32 with absolute-value
+// operands, half an instruction per value against one and a half for the
+// bits).  It does not see a NaN, and needs not: the prologues hand every
+// pair whose inputs hold one to the recurrent kernel (post_vmax and their
+// own watches), and a NaN that arises in the scan needs an infinite or
+// out-of-range operand first, which it sees.
+struct ScanWatch {
+    float big = 0.f;
+    __device__ __forceinline__ void note(f4v x)
+    {
+        big = fmaxf(fmaxf(big, fabsf(x[0])), fabsf(x[1]));
+        big = fmaxf(fmaxf(big, fabsf(x[2])), fabsf(x[3]));
+    }
+    __device__ __forceinline__ bool over() const { return !(big < SPLIT_LIMIT); }
+};
+
 // T = (I + A)^-1 of a chunk's strictly lower triangular 64 x 64 matrix A
 // (rows of LA floats) by forward substitution down the rows,
 //   T_tc = [t == c] - sum_{s<t} A_ts T_sc,
@@ -327,19 +343,23 @@ __device__ __forceinline__ int tile_exponent(float m)
 
 // Largest |v| of a prologue wave's chunk rows (4 vectors of 8 per thread),
 // stored as one float per wave at SC[252 + wave] of the chunk record, where
-// the scan reads it back.
+// the scan reads it back.  Returns false when the wave's rows hold an
+// infinite value or a NaN: the caller then hands the pair to the recurrent
+// kernel (in the chunk products a NaN would reach earlier tokens through the
+// zero entries of T above the diagonal).
 constexpr int SC_VMAX = 252;
 template <typename V8>
-__device__ __forceinline__ void post_vmax(const V8 (&x)[4], char *rec_sc)
+__device__ __forceinline__ bool post_vmax(const V8 (&x)[4], char *rec_sc)
 {
-    float m = 0.f;
+    uint32_t m = 0u;  // bits of |v|: NaN ranks above every finite value
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(to_f32(x[i][e])));
+        for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(to_f32(x[i][e])) & 0x7FFFFFFFu);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) reinterpret_cast<float *>(rec_sc)[SC_VMAX + (threadIdx.x >> 6)] = m;
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) reinterpret_cast<float *>(rec_sc)[SC_VMAX + (threadIdx.x >> 6)] = __uint_as_float(m);
+    return m < 0x7F800000u;
 }
 
 // Segments of the scan's chain (see k_chunk_scan).  pass 0: one pass over
@@ -573,7 +593,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         if (!TF && kq_writer)
             *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
-    post_vmax(ldv, rec + OSC);
+    if (!post_vmax(ldv, rec + OSC)) *flag = 2;
     if (!exact) *flag = 2;  // a bf16 value fp16 cannot hold: the recurrent kernel takes the pair
     lds_barrier();
 
@@ -1247,7 +1267,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
         const int idx = tid + 256 * i, r = idx >> 4, c8 = (idx & 15) * 8;
         *reinterpret_cast<a8 *>(&sK[r][c8]) = ldv[i];
     }
-    post_vmax(ldv, rec + RC::SC);
+    if (!post_vmax(ldv, rec + RC::SC)) *flag = 2;
     // W's right-hand-side fragments wait in LDS (in fragment order: one
     // 16-byte read each later), so no register holds them across the solve
     h8 *sBw = reinterpret_cast<h8 *>(sm + 2 * SLOT);  // [plane][wave][c][ks][lane]
@@ -1577,7 +1597,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 #pragma unroll
             for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= up;
         const float um = mode == SEG_TRANS ? 0.f : up;  // a transition tile leaves U out
-        SplitWatch sw;
+        ScanWatch sw;
         struct Ops {
             h8 wh[4], wl[4];    // W (hi, lo) of token block tb, four k-steps of 32
             h8 kt[2][2][NPL];   // K^T (per key: Kd^T hi, lo) fragments: key tiles 2 wave + a, token steps ks
@@ -2041,7 +2061,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
 #pragma unroll
             for (int rt = 0; rt < NVB; ++rt) Sc[a][rt] *= up;
         const float um = mode == SEG_TRANS ? 0.f : up;  // a transition tile leaves V out
-        SplitWatch sw;
+        ScanWatch sw;
         struct Ops {
             h8 k[4];        // k row 16 tb + lr, keys 32 kk + 8 lq .. +7
             h4 v[NVB];      // v at (tokens 16 tb + 4 lq + i, row 16 vb + lr)
@@ -2315,7 +2335,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                 __builtin_amdgcn_raw_buffer_store_b128(ld_b128_lds(&sO[tb][st_tok + TPS * ps][8 * st_q]), ro,
                                                        offO + (uint32_t)(TPS * ps * tok_bytes), 0, 0);
         };
-        SplitWatch pw;
+        ScanWatch pw;
         auto step = [&](int j, Ops &cur) {
             const int bf = j & 1;
             const int jn = j + 1 < ce ? j + 1 : j;

@@ -205,6 +205,32 @@ def test_chunked_state_precision(form, lengths, H, HV, per_key):
     assert_close(st, rs, 1e-4, "%s state" % form)
 
 
+# ------------------------------------------------------------------ NaN in v
+@pytest.mark.parametrize("form,H,HV", [("t_form", 16, 64), ("wu_form", 2, 4)], ids=["t_form", "wu_form"])
+def test_chunked_nan_value_hand_over(form, H, HV):
+    """A NaN in one value channel c of token t: token by token (the README
+    recurrence) it reaches only row c of the state, so only channel c of o
+    from t on.  The chunk products would spread it to the earlier tokens of
+    the chunk (zero entries of T times NaN), so the prologue hands the pair
+    to the recurrent kernel: every other output and state entry stays finite
+    and matches the oracle."""
+    case = _case(88, [300, 200], H=H, HV=HV)
+    t, h, c = 150, 1, 5
+    case["v"] = case["v"].copy()
+    case["v"][t, h, c] = np.float16(np.nan)
+    say("case NaN value %s" % form)
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    ro, rs = oracle_forward(case)
+    bad_o = np.zeros(o.shape, bool)
+    bad_o[t:300, h, c] = True
+    bad_s = np.zeros(st.shape, bool)
+    bad_s[0, h, c, :] = True
+    assert np.all(np.isnan(o[bad_o])) and np.all(np.isnan(st[bad_s])), "the NaN reaches what the recurrence sends it to"
+    assert np.all(np.isfinite(o[~bad_o])) and np.all(np.isfinite(st[~bad_s])), "and nothing else"
+    assert rel_err(np.where(bad_o, 0.0, o), np.where(bad_o, 0.0, ro)) <= TOL_CHUNKED
+    assert rel_err(np.where(bad_s, 0.0, st), np.where(bad_s, 0.0, rs)) <= TOL_CHUNKED
+
+
 # ------------------------------------------------------------------ state magnitude
 @pytest.mark.parametrize("magnitude", [1e4, 1e-5])
 @pytest.mark.parametrize("rule", ["gated_delta", "gated"])
