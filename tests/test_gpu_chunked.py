@@ -177,7 +177,8 @@ def test_chunked_wide_tiles(rule, per_key):
 # ------------------------------------------------------------------ state precision
 # (form, lengths, q/k heads, value heads, per-key decay)
 PRECISION_FORMS = [("t_form", [700, 300, 1000, 64], 16, 64, False), ("wu_form", [1500, 700], 2, 4, False),
-                   ("per_key_form", [900, 500], 2, 4, True), ("wu_form_one_chunk", [64], 16, 64, False)]
+                   ("per_key_form", [900, 500], 2, 4, True), ("wu_form_one_chunk", [64], 16, 64, False),
+                   ("per_key_raw_gate", [700, 64, 300], 4, 16, True)]
 
 
 @pytest.mark.parametrize("form,lengths,H,HV,per_key", PRECISION_FORMS, ids=[f[0] for f in PRECISION_FORMS])
@@ -192,7 +193,10 @@ def test_chunked_state_precision(form, lengths, H, HV, per_key):
     fp16 and keeps the 2e-3 bar."""
     kw = dict(update_rule="gated_delta_v2", per_key=True, gate_activation="none",
               beta_activation="none") if per_key else {}
-    case = _case(67 if form != "per_key_form" else 73, lengths, H=H, HV=HV, **kw)
+    if form == "per_key_raw_gate":
+        # the raw-gate arm per key channel: some channels decay by tens of nats per token
+        kw = dict(update_rule="gated_delta_v2", per_key=True, gate_activation="qwen", beta_activation="none")
+    case = _case(67 if not per_key else 73, lengths, H=H, HV=HV, **kw)
     if form == "wu_form_one_chunk":
         # request 3 of the T-form case on its own: 64 pairs take W and U in the records
         case = _case(67, [700, 300, 1000, 64], H=H, HV=HV)
