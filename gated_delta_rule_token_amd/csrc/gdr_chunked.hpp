@@ -374,6 +374,19 @@ struct ScanSeg {
     float *stage;  // in-place state (slab, or final == initial): final states go here first, else nullptr
 };
 enum SegMode : int { SEG_REAL = 0, SEG_CARRY = 1, SEG_TRANS = 2 };
+
+// Value heads of one q/k head that a single-pass scan places on one XCD
+// (consecutive groups), so that the k, q and K^T rows they share are fetched
+// into its L2 once: the largest power of two up to 8 dividing HV / H (1
+// without grouped heads, and for the passes of a segmented scan).
+__host__ __device__ inline int xcd_heads(int H, int HV, int pass)
+{
+    if (pass != 0 || H <= 0 || HV % H != 0) return 1;
+    const int r = HV / H;
+    int g = 1;
+    while (g < 8 && r % (2 * g) == 0) g *= 2;
+    return g;
+}
 __host__ __device__ constexpr int seg_slots(int nseg) { return 3 * nseg; }
 __host__ __device__ constexpr int seg_start(int p) { return p; }
 __host__ __device__ constexpr int seg_carry(int nseg, int p) { return nseg + p; }
@@ -1485,11 +1498,14 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
     // A group is one (request, head) -- with segments one (request, head,
     // segment) -- and its units are its row tiles (pass 1: carry tiles, then
     // transition tiles).  XCD-aware order: blocks i, i + 8, ... (one XCD) are
-    // the units of one group, which read the same chunk records.
+    // the units of one group, which read the same chunk records, and with
+    // grouped heads the next groups there are the other value heads of the
+    // same q/k head (xcd_heads).
     const int NU = (sg.pass == 1 ? 2 : 1) * NTILE;
     const int nsg = sg.pass == 0 ? 1 : sg.nseg - 1;  // groups per (request, head)
-    const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
-    const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
+    const int gs = xcd_heads(p.H, HV, sg.pass);      // groups in a row on one XCD
+    const int xl = blockIdx.x & 7, q8 = blockIdx.x >> 3, unit = q8 % NU, rest = q8 / NU;
+    const int64_t gi = ((int64_t)(rest / gs) * 8 + xl) * gs + rest % gs;
     if (gi >= (int64_t)p.B * HV * nsg) return;
     // group -> (request, head): requests longest first (k_chunk_table's order)
     const int pr = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
@@ -1957,8 +1973,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
     const int HV = p.HV;
     const int NU = (sg.pass == 1 ? 2 : 1) * NTILE;
     const int nsg = sg.pass == 0 ? 1 : sg.nseg - 1;
-    const int xl = blockIdx.x & 7, unit = (blockIdx.x >> 3) % NU;
-    const int64_t gi = (int64_t)(blockIdx.x / (8 * NU)) * 8 + xl;
+    const int gs = xcd_heads(p.H, HV, sg.pass);
+    const int xl = blockIdx.x & 7, q8 = blockIdx.x >> 3, unit = q8 % NU, rest = q8 / NU;
+    const int64_t gi = ((int64_t)(rest / gs) * 8 + xl) * gs + rest % gs;
     if (gi >= (int64_t)p.B * HV * nsg) return;
     // group -> (request, head): requests longest first (k_chunk_table's order)
     const int pr = (int)(gi / nsg), seg = (int)(gi % nsg) + (sg.pass == 2 ? 1 : 0);
@@ -2557,7 +2574,8 @@ static void launch_scan(const Params &p, int32_t *off, const char *rec, const ch
 {
     constexpr int NTILE = D128 / (16 * NVB);
     const int64_t groups = (int64_t)p.B * p.HV * (sg.pass == 0 ? 1 : sg.nseg - 1);
-    const int64_t blocks = (groups + 7) / 8 * 8 * NTILE * (sg.pass == 1 ? 2 : 1);
+    const int64_t per = 8 * xcd_heads(p.H, p.HV, sg.pass);  // groups per round of the eight XCDs
+    const int64_t blocks = (groups + per - 1) / per * per * NTILE * (sg.pass == 1 ? 2 : 1);
     if (blocks <= 0) return;
     if constexpr (TF)
         hipLaunchKernelGGL((k_chunk_scan_t<TA, RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
