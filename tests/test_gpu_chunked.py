@@ -159,6 +159,20 @@ def test_chunked_resume_split(split):
     assert_close(sb, rs, TOL_CHUNKED, "resumed at %d: state" % split)
 
 
+@pytest.mark.parametrize("H,HV", [(8, 64), (4, 24), (16, 48)], ids=["ratio8", "ratio6", "ratio3"])
+def test_chunked_grouped_heads_on_one_xcd(H, HV):
+    """Single-pass scans place the value heads of one q/k head in a row on one
+    XCD (2, 4 or 8 of them, the largest power of two dividing HV / H): ragged
+    requests over 128 pairs or more (the T form) with 8, 6 and 3 value heads
+    per q/k head, so the grid's last round is partly empty."""
+    case = _case(90 + HV, [150, 333, 0, 64, 97], H=H, HV=HV)
+    say("case grouped heads H=%d HV=%d" % (H, HV))
+    o, st = gpu_forward(case, "chunked", scan_segments=1)
+    ro, rs = oracle_forward(case)
+    assert_close(o, ro, TOL_CHUNKED, "H=%d HV=%d o" % (H, HV))
+    assert_close(st, rs, 1e-4, "H=%d HV=%d state" % (H, HV))
+
+
 @pytest.mark.parametrize("rule,per_key", [("gated_delta", False), ("gated_delta_v2", True)],
                          ids=["per_head", "per_key_form"])
 def test_chunked_wide_tiles(rule, per_key):
