@@ -2371,32 +2371,42 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                     acc[vb] = mfma16(shi, cur.q[kk], acc[vb]);
                     acl[vb] = mfma16(slo, cur.q[kk], acl[vb]);
                 }
-            // P while the chain forms D (between barriers 1.5 and 2: the k rows
-            // stay in LDS until the chain's next stage A, after barrier 2)
-            if constexpr (RET) lds_barrier();  // 1.5
             // ---- P_ts = scale / |q_t| / |k_s| exp(G_t - G_s) q_t . k_s (s <= t) from
-            // the k rows the chain parked and this wave's q rows: K Q^T at
-            // [s = 16 sb + 4 lq + i][t = 16 tb + lr] (fp16 products, exact in
-            // fp32), then (hi, lo) fragments whose element 4 h + i of token step
-            // ks is token 32 ks + 16 h + 4 lq + i (the order of D^T in LDS)
+            // the k rows the chain parked with the state tile and this wave's q
+            // rows.  K Q^T at [s = 16 sb + 4 lq + i][t = 16 tb + lr] (fp16
+            // products, exact in fp32) right after O1, where these waves would
+            // wait for the chain at barrier 1.5; then, while the chain forms D,
+            // the per-element factors and the (hi, lo) fragments whose element
+            // 4 h + i of token step ks is token 32 ks + 16 h + 4 lq + i (the
+            // order of D^T in LDS).  The k rows stay in LDS until the chain's
+            // next stage A, after barrier 2.
+            f4v c4[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                c4[sb] = f4v{0.f, 0.f, 0.f, 0.f};
+                if (sb <= tb) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        c4[sb] = mfma16(ld_h8(&sKr[16 * sb + lr][sw_key(lr, 32 * kk + lk)]), cur.q[kk], c4[sb]);
+                }
+            }
+            if constexpr (RET) lds_barrier();  // 1.5
+            // the factors' exponentials stay below the barrier: their inputs pass
+            // through an asm the compiler keeps after it (hoisted above it, they
+            // made these waves late for it)
+            asm volatile("" : "+v"(cur.pg), "+v"(cur.pgl));
             h8 ph[2], pl[2];
             {
                 const int t = 16 * tb + lr;
                 h4 hh[4], hl[4];
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) {
-                    f4v c4 = {0.f, 0.f, 0.f, 0.f};
-                    if (sb <= tb) {
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk)
-                            c4 = mfma16(ld_h8(&sKr[16 * sb + lr][sw_key(lr, 32 * kk + lk)]), cur.q[kk], c4);
-                    }
                     f4v pv;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int sx = 16 * sb + 4 * lq + i;
                         const float d2 = (cur.pg - cur.sg[sb][i]) + (cur.pgl - cur.sgl[sb][i]);
-                        pv[i] = sx <= t ? cur.pq * cur.sk[sb][i] * ex2(d2) * c4[i] : 0.f;
+                        pv[i] = sx <= t ? cur.pq * cur.sk[sb][i] * ex2(d2) * c4[sb][i] : 0.f;
                     }
                     pw.note(pv);
                     split4(pv, hh[sb], hl[sb]);
