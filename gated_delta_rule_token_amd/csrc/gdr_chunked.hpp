@@ -82,7 +82,8 @@ constexpr int D128 = 128;       // dk = dv
 // and, once per (chunk, q/k head) -- the same for every value head of the
 // group, written by its first value head (struct KQ):
 //   KT  K^T fp16,        block mt * 2 + ks:              key 16 mt + lr, tokens 32 ks + 8 lq .. +7
-//   Q   q fp16,          block tb * 4 + kk:              token 16 tb + lr, keys 32 kk + 8 lq .. +7
+// (the scan's output waves read the q rows from the activations themselves:
+// a row of 8 keys per lane is already their fragment layout)
 // Decay per key channel (PK = true): the per-token weights kd and gq become
 // per-element factors, so two operands carry fp32 values and get two planes:
 //   KT  Kd^T (hi, lo),   block (mt * 2 + ks) * 2 + plane,  Kd = kn o exp(G_C - G)
@@ -123,7 +124,7 @@ struct RecT {
 };
 constexpr int SCT_BETA = 256, SCT_RW = 320, SCT_G = 384, SCT_IK = 448, SCT_QS = 512, SCT_GL = 576;
 struct KQ {
-    static constexpr uint32_t KT = 0, Q = 16 * 1024, SIZE = 32 * 1024;
+    static constexpr uint32_t KT = 0, SIZE = 16 * 1024;
 };
 
 __device__ __forceinline__ f4v mfma16(h8 a, h8 b, f4v c)
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(256) void k_chunk_table(const Params p, int32_t *of
 // 256 threads.  LDS: K, V and Q rows of the chunk; A (fp32) replaces Q once
 // K Q^T and K K^T are formed; after the solve W (hi, lo) rows replace K and V.
 // TF: the T form (RecT: T and the scalars; no W, U, P or q), else Rec<false>
-// plus the K^T and q area.
+// plus the K^T area.
 // TI: the activations' dtype (bf16 rows are converted to fp16 as they load;
 // a pair with a value fp16 cannot hold exactly goes to the recurrent kernel).
 template <typename TI, int RULE, bool TF>
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     const int lr = lane & 15, lq = lane >> 4, lk = lq * 8;
     constexpr uint32_t OSC = TF ? RecT::SC : R_SC;
     char *rec = ws + ((size_t)ci * HV + h) * (TF ? RecT::SIZE : WS_REC);
-    // K^T and q once per (chunk, q/k head): the group's first value head writes them
+    // K^T once per (chunk, q/k head): the group's first value head writes it
     char *kq = kqs + ((size_t)ci * H + qh) * (TF ? RecT::KT_SIZE : KQ::SIZE);
     const bool kq_writer = h % (HV / H) == 0;
     // A split operand past the fp16 range hands the pair to the recurrent
@@ -602,9 +603,6 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         *reinterpret_cast<h8 *>(&sK[r][c8]) = ldk[i];
         *reinterpret_cast<h8 *>(&sQ[r][c8]) = ldq[i];
         if constexpr (!TF) *reinterpret_cast<h8 *>(&sV[r][c8]) = ldv[i];
-        // q in fragment order for the scan's output waves (rows past the end are zero)
-        if (!TF && kq_writer)
-            *reinterpret_cast<h8 *>(kq + KQ::Q + ((((r >> 4) * 4 + (c8 >> 5)) * 64) + ((c8 & 31) >> 3) * 16 + (r & 15)) * 16) = ldq[i];
     }
     if (!post_vmax(ldv, rec + OSC)) *flag = 2;
     if (!exact) *flag = 2;  // a bf16 value fp16 cannot hold: the recurrent kernel takes the pair
@@ -1555,7 +1553,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
         const float mv = fmaxf(fmaxf(sTM[0][1], sTM[1][1]), fmaxf(sTM[2][1], sTM[3][1]));
         return ce > cb ? tile_exponent(fmaxf(mode == SEG_TRANS ? 0.f : mv, ms)) : 0;
     };
-    // per head: K^T and q of chunk jj come from the (chunk, q/k head) area, else from the record
+    // per head: K^T of chunk jj comes from the (chunk, q/k head) area, else from the record
     auto kq_rsrc = [&](int jj) {
         if constexpr (PK) return make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
         else return make_rsrc(kqs + ((size_t)(c0 + jj) * p.H + qh) * KQ::SIZE, KQ::SIZE);
@@ -1802,7 +1800,12 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
             h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
             float gq;         // per head: gq of this lane's token
         };
-        const uint32_t offQ = (PK ? RC::Q : KQ::Q) + (uint32_t)tb * 4 * NPL * 1024 + l16;
+        // per key: Qg (hi, lo) from the record; per head: q rows from the
+        // activations (row 16 tb + lr, keys 32 kk + 8 lq .. +7), converted to fp16
+        // as they load (the prologue has handed pairs with values fp16 cannot
+        // hold to the recurrent kernel); rows past the request's end read zero
+        const uint32_t offQ = PK ? RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16
+                                 : (uint32_t)((16 * tb + lr) * p.H * D128 * 2 + 2 * lk);
         // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
         const int tok_bytes = HV * D128 * 2;
         // after the LDS transpose each lane stores 16 bytes (8 rows of a token):
@@ -1824,11 +1827,22 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         // one operand set, each part reloaded for chunk jj right after its last use
         auto fetchQ = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = kq_rsrc(jj);
+            if constexpr (PK) {
+                const __amdgpu_buffer_rsrc_t r = kq_rsrc(jj);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+                for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
+                    for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
+            } else {
+                const int64_t t0 = rs + (int64_t)jj * CH;
+                const int n = (int)((re - t0) < CH ? (re - t0) : CH);
+                const TA *base = static_cast<const TA *>(p.q) + ((size_t)t0 * p.H + qh) * D128;
+                const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<TA *>(base), 0, (n - 1) * p.H * D128 * 2 + D128 * 2, 0x00020000);
+                bool ok = true;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) f.q[kk][0] = to_h8(ld_b128<typename ActVec<TA>::v8>(r, offQ + 64 * kk), ok);
+            }
         };
         auto fetchG = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)(c0 + jj) * HV + h) * RC::SIZE, RC::SIZE);
@@ -2536,18 +2550,19 @@ __global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int3
 // The per-head form has two variants.  With a single-pass scan over 128 or
 // more (request, head) pairs it takes the T form (k_chunk_prep<RULE, true>,
 // k_chunk_scan_t): records of 18 KB per (chunk, value head) instead of 81 KB
-// plus 16 KB of K^T instead of 32 KB of K^T and q per (chunk, q/k head), at
+// plus 16 KB of K^T per (chunk, q/k head), at
 // the price of one more product on the scan's serial chain per chunk and P
 // formed by the output waves.  Measured on MI355X in one
 // session: the varlen workload (8 requests, 32 heads) 0.974 -> 0.924 ms; the
-// 65,536-token sequence (16 heads, 5 scan segments) 1.53 -> 1.65 ms, so
-// segmented and few-pair scans keep W and U in the records.
+// 65,536-token sequence (16 heads, 5 scan segments) 1.53 -> 1.65 ms (and
+// 1.42 -> 1.56 ms once the T form formed P in its scan), so segmented and
+// few-pair scans keep W and U in the records.
 static bool t_form(bool per_key, int B, int HV, int nseg) { return !per_key && nseg <= 1 && (int64_t)B * HV >= 128; }
 
 // Workspace: chunk table (off[B + 1], the (B * HV) hand-over flags, the scan
 // order of the B requests) |
 // records of every (chunk, value head) (Rec<true>, Rec<false> or RecT) |
-// per-head form: K^T and q (T form: K^T only) of every (chunk, q/k head) |
+// per-head form: K^T of every (chunk, q/k head) |
 // segment states | staging for in-place final states (one 128 x 128 fp32
 // state per pair).  The chunk budget of gdr_chunk_plan.hpp sizes the
 // records; the table never assigns a chunk index at or past it.
