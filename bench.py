@@ -160,11 +160,28 @@ def bench_decode(args, L=1):
     digest = source_digest(DECODE_SOURCES)
     traffic = committed_traffic(digest)
     achieved = total_b / (kms * 1e-3) / 1e9
-    return case, {
+    out = {
         "wall_s": wall, "kernel_ms": kms, "bytes_per_step": total_b, "state_bytes": state_b,
         "gbs_wall": total_b * steps / wall / 1e9, "gbs_kernel": achieved,
         "algo": calls[0].algo, "tokens": B * L, "traffic": traffic, "digest": digest,
     }
+    if L == 1:
+        # the same steps' state bytes moved by a plain in-place copy (no compute),
+        # alternating the two slot sets as the decode steps do: the ceiling of
+        # this access pattern (random 2 MiB slots), measured after the timed region
+        class Floor:
+            def __init__(self, ids):
+                self.ids = ids
+
+            def run(self):
+                api.slab_stream(slab, self.ids, 1.0)
+        floors = [Floor(_t(ids)) for ids in (ids_a, ids_b)]
+        for i in range(args.warmup):
+            floors[i % 2].run()
+        fms = time_events(floors, steps)
+        out["slab_stream_ms"] = fms
+        out["slab_stream_gbs"] = state_b / (fms * 1e-3) / 1e9
+    return case, out
 
 
 PREFILL_CASES = {
@@ -380,6 +397,11 @@ def main():
         best = max(x["GB/s"] for x in ceil.values())
         result["decode"]["stream_ceiling_gbs"] = best
         result["decode"]["frac_of_stream_ceiling"] = d["gbs_kernel"] / best
+        # the same slots' state bytes with no compute (gdr_slab_stream): a plain
+        # copy over the step's own access pattern
+        result["decode"]["slab_stream_gbs"] = d["slab_stream_gbs"]
+        result["decode"]["slab_stream_ms"] = d["slab_stream_ms"]
+        result["decode"]["kernel_ms_over_slab_stream_ms"] = d["kernel_ms"] / d["slab_stream_ms"]
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, d["bytes_per_step"])
         del case

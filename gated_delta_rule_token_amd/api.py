@@ -70,7 +70,8 @@ class Tensors(ctypes.Structure):
 
 
 EXPORTS = ("gdr_abi_version", "gdr_status_str", "gdr_last_error", "gdr_validate",
-           "gdr_workspace_size", "gdr_select_algo", "gdr_forward", "gdr_forward_noalloc", "gdr_gate")
+           "gdr_workspace_size", "gdr_select_algo", "gdr_forward", "gdr_forward_noalloc", "gdr_gate",
+           "gdr_slab_stream")
 NOALLOC_SCRATCH_BYTES = 256 << 20  # GDR_NOALLOC_SCRATCH_BYTES of include/gdr.h
 
 
@@ -109,6 +110,9 @@ def load_library():
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p]
         lib.gdr_gate.restype = ctypes.c_int
+        lib.gdr_slab_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+        lib.gdr_slab_stream.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -371,6 +375,22 @@ def gate(a, dt_bias, decay_scale, b=None, want_beta=False, out_decay=None, out_b
     check(lib.gdr_gate(a.numel(), heads, _dtype_code(a.dtype), _ptr(a), _ptr(dt_bias),
                        _ptr(decay_scale), _ptr(b), _ptr(decay), _ptr(beta), stream))
     return decay, beta
+
+
+def slab_stream(slab, slot_ids, factor=1.0):
+    """Multiply in place by ``factor`` the state matrices ``slab[slot_ids[b]]``
+    (every head) and nothing else: the state traffic of a decode step over the
+    same slot ids, with no compute (a measurement aid).  ``slab`` is fp32
+    (num_slots, HV, dv, dk) on the GPU, ``slot_ids`` int32 (B,)."""
+    lib = load_library()
+    dev = slab.device
+    _need(slab, "slab", torch.float32, dev)
+    _need(slot_ids, "slot_ids", torch.int32, dev)
+    if slab.dim() != 4:
+        raise ValueError("slab must be (num_slots, HV, dv, dk)")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    check(lib.gdr_slab_stream(_ptr(slab), _ptr(slot_ids), slot_ids.numel(), slab.shape[1],
+                              slab.shape[2] * slab.shape[3], slab.shape[0], float(factor), stream))
 
 
 class Prepared:

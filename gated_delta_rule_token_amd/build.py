@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgdr.so")
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_recurrent.hip", "gdr_chunked.hip", "gdr_chunked_bf16.hip",
-           "gdr_gate.hip"]
+           "gdr_gate.hip", "gdr_stream.hip"]
 
 # Packed fp32 VALU forms are switched off for the device code; every kernel
 # is ordinary fp32 arithmetic.

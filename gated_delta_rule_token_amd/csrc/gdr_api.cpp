@@ -419,4 +419,21 @@ gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a, 
     return GDR_OK;
 }
 
+gdr_status gdr_slab_stream(float *slab, const int32_t *slot_ids, int32_t batch, int32_t heads, int64_t matrix,
+                           int32_t num_slots, float factor, void *stream)
+{
+    g_last_error.clear();
+    if (batch < 0 || heads < 1 || num_slots < 1) return fail(GDR_E_INVALID, "batch must be >= 0, heads and num_slots >= 1");
+    if (matrix < 4 || matrix % 4 != 0) return fail(GDR_E_INVALID, "matrix must be a positive multiple of 4 floats");
+    if (batch == 0) return GDR_OK;
+    if (!slab || !slot_ids) return fail(GDR_E_INVALID, "slab and slot_ids are required");
+    if (!aligned16(slab)) return fail(GDR_E_INVALID, "slab must be 16-byte aligned");
+    if (gdr::slab_stream_blocks(batch, heads, matrix) > INT32_MAX)
+        return fail(GDR_E_INVALID, "batch * heads * matrix is too large for one launch");
+    hipError_t err = gdr::launch_slab_stream(slab, slot_ids, batch, heads, matrix, num_slots, factor,
+                                             static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDR_E_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 }  // extern "C"

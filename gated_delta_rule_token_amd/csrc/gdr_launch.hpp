@@ -28,5 +28,9 @@ hipError_t launch_chunked_bf16(const Params &p, int rule, bool per_key, int nseg
 // Standalone gate fusion.
 hipError_t launch_gate(int64_t count, int heads, int dtype, const void *a, const float *dt_bias,
                        const float *decay_scale, const void *b, void *decay, void *beta, hipStream_t s);
+// gdr_stream.hip: read and rewrite, scaled, the state matrices slab[slot_ids[b], h]
+int64_t slab_stream_blocks(int batch, int heads, int64_t matrix);
+hipError_t launch_slab_stream(float *slab, const int32_t *slot_ids, int batch, int heads, int64_t matrix,
+                              int num_slots, float factor, hipStream_t s);
 
 }  // namespace gdr

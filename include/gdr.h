@@ -254,6 +254,20 @@ gdr_status gdr_gate(int64_t count, int32_t heads, int32_t dtype, const void *a,
                     const float *dt_bias, const float *decay_scale, const void *b,
                     void *decay, void *beta, void *stream);
 
+/* Memory-traffic floor of a decode step over a state slab: a measurement
+ * aid beside the operation, which computes nothing of it.  Multiplies in place
+ * by `factor` each fp32 matrix slab[slot_ids[b], h] (b < batch, h < heads,
+ * `matrix` floats each, a positive multiple of 4; slab laid out (num_slots,
+ * heads, matrix) as gdr_forward's slab) and touches nothing else, so it moves
+ * exactly the state bytes a decode step over the same slot ids reads and
+ * writes, in the same order of requests.  factor = 1 leaves the values
+ * unchanged.  A slot id outside [0, num_slots) skips its request, as in
+ * gdr_forward.  slab (16-byte aligned) and slot_ids are device memory owned
+ * by the caller; enqueued on `stream`.  GDR_E_INVALID for bad sizes, NULL or
+ * misaligned pointers, or a grid past one launch's limit. */
+gdr_status gdr_slab_stream(float *slab, const int32_t *slot_ids, int32_t batch, int32_t heads, int64_t matrix,
+                           int32_t num_slots, float factor, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -277,6 +277,19 @@ def test_gate_argument_checks(lib):
         == api.GDR_E_INVALID  # bad dtype
 
 
+def test_slab_stream_argument_checks(lib):
+    f = ctypes.c_float(1.0)
+    assert lib.gdr_slab_stream(_fake(1), _fake(2), 4, 0, 16, 8, f, None) == api.GDR_E_INVALID  # no heads
+    assert lib.gdr_slab_stream(_fake(1), _fake(2), 4, 2, 18, 8, f, None) == api.GDR_E_INVALID  # not 4k floats
+    assert lib.gdr_slab_stream(_fake(1), _fake(2), 4, 2, 16, 0, f, None) == api.GDR_E_INVALID  # no slots
+    assert lib.gdr_slab_stream(None, _fake(2), 4, 2, 16, 8, f, None) == api.GDR_E_INVALID
+    assert lib.gdr_slab_stream(_fake(1) + 4, _fake(2), 4, 2, 16, 8, f, None) == api.GDR_E_INVALID  # misaligned
+    # 2^20 requests x 2^10 heads x 4 pieces of 64 KB: 2^32 workgroups, past one launch
+    assert lib.gdr_slab_stream(_fake(1), _fake(2), 1 << 20, 1 << 10, 1 << 16, 8, f, None) \
+        == api.GDR_E_INVALID
+    assert lib.gdr_slab_stream(None, None, 0, 2, 16, 8, f, None) == api.GDR_OK  # nothing to do
+
+
 def test_forward_rejects_a_short_workspace(lib):
     """gdr_forward compares the workspace size it is given with what the
     problem needs and returns GDR_E_WORKSPACE before anything is enqueued."""

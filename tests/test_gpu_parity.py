@@ -351,6 +351,32 @@ def test_gate_kernel(dtype):
         assert worst <= 1.0, "%s off the oracle by more than one store rounding" % what
 
 
+# ------------------------------------------------------------------ slab stream
+@pytest.mark.parametrize("shape", [(12, 3, 16, 20), (6, 2, 128, 128)], ids=["ragged", "d128"])
+def test_slab_stream_touches_only_addressed_rows(shape):
+    """gdr_slab_stream scales exactly the addressed state matrices (every head
+    of slab[slot_ids[b]]) by the factor -- one fp32 multiply per element, so
+    bit for bit what torch's fp32 multiply gives -- and leaves every other
+    slot, and requests with a slot id outside [0, num_slots), untouched.
+    Covers a matrix that is not a whole number of 16 KB pieces (320 floats)
+    and one of four pieces (128 x 128)."""
+    from gated_delta_rule_token_amd import api
+    g = torch.Generator().manual_seed(5)
+    slab = torch.randn(shape, generator=g).cuda()
+    before = slab.clone()
+    n = shape[0]
+    ids = torch.tensor([n - 1, -1, 2, 0, n, 2 * n], dtype=torch.int32).cuda()
+    api.slab_stream(slab, ids, 1.5)
+    torch.cuda.synchronize()
+    want = before.clone()
+    for s in (n - 1, 2, 0):
+        want[s] = before[s] * 1.5
+    assert torch.equal(slab, want)
+    api.slab_stream(slab, ids, 1.0)  # factor 1 leaves the values as they are
+    torch.cuda.synchronize()
+    assert torch.equal(slab, want)
+
+
 # ------------------------------------------------------------------ chunked prefill
 CHUNK_RULES = ["linear", "gated", "delta", "gated_delta"]
 
