@@ -113,14 +113,12 @@ constexpr uint32_t R_W = Rec<false>::W, R_U = Rec<false>::U, R_P = Rec<false>::P
 //       P's per-token factors: G[64] at SCT_G (cumulative log decay in log2
 //       units) with its rounding error at SCT_GL, 1 / |k| [64] at SCT_IK,
 //       scale / |q| [64] at SCT_QS
-// plus, once per (chunk, q/k head), K^T in fragment order as KQ::KT below
-// (16 KB: the state update's left operand, which the k rows give only
-// through a transpose).
+// (the state update's left operand K^T the scan gathers from the k rows it
+// parks in LDS).
 struct RecT {
     static constexpr uint32_t T = 0;
     static constexpr uint32_t SC = 16 * 1024;
     static constexpr uint32_t SIZE = SC + 2560;
-    static constexpr uint32_t KT_SIZE = 16 * 1024;
 };
 constexpr int SCT_BETA = 256, SCT_RW = 320, SCT_G = 384, SCT_IK = 448, SCT_QS = 512, SCT_GL = 576;
 struct KQ {
@@ -539,8 +537,9 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     constexpr uint32_t OSC = TF ? RecT::SC : R_SC;
     char *rec = ws + ((size_t)ci * HV + h) * (TF ? RecT::SIZE : WS_REC);
     // K^T once per (chunk, q/k head): the group's first value head writes it
-    char *kq = kqs + ((size_t)ci * H + qh) * (TF ? RecT::KT_SIZE : KQ::SIZE);
-    const bool kq_writer = h % (HV / H) == 0;
+    // (W/U form only; the T form's scan gathers it from the k rows itself)
+    char *kq = TF ? nullptr : kqs + ((size_t)ci * H + qh) * KQ::SIZE;
+    const bool kq_writer = !TF && h % (HV / H) == 0;
     // A split operand past the fp16 range hands the pair to the recurrent
     // kernel.  Each phase watches its own operands and posts at its end, so no
     // register stays live across the phases.
@@ -1962,14 +1961,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 // since U = T diag(beta) V and W = T diag(w) K (w = beta gamma / |k|).  The
 // output waves form P from the q rows and the k rows that the chain waves
 // park in LDS with the state tile (fp16 products, exact in fp32, scaled per
-// element as the prologue of the W/U form scales them).  The record holds T
-// and the per-token scalars, the (chunk, q/k head) area K^T; k, v and q are
-// read from the activations.  A chunk step has three barriers: the state
-// tile and the k rows are in LDS (1), Z is (1.5, retrieving rules only), D is
-// (2).  Workgroup layout, segments, tile scaling and the output path follow
+// element as the prologue of the W/U form scales them), and the chain waves
+// gather the state update's K^T fragments from the same k rows (eight 16-bit
+// LDS reads per fragment, issued after barrier 1 and consumed at stage E).
+// The record holds T and the per-token scalars; k, v and q are read from the
+// activations.  A chunk step has three barriers: the state tile and the k
+// rows are in LDS (1), Z is (1.5, retrieving rules only), D is (2).  Workgroup layout, segments, tile scaling and the output path follow
 // k_chunk_scan.
 template <typename TA, int RULE, int NVB>
-__global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *off, const char *ws, const char *kts,
+__global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *off, const char *ws,
                                                      const ScanSeg sg)
 {
     constexpr bool RET = rule_retrieves(RULE);
@@ -1980,7 +1980,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
     __shared__ __align__(16) half_t sS[2][TR][D128];
     __shared__ __align__(16) half_t sDt[2][2][TR][CH];   // [buffer][hi, lo][row][token]: D^T of chunk j in j & 1, Z^T in the other
     __shared__ __align__(16) half_t sDs[2][TR][CH];      // [hi, lo][row][token] (kd D)^T
-    __shared__ __align__(16) half_t sKr[CH][D128];       // chunk j's k rows [token][key]: P's left operand
+    __shared__ __align__(16) half_t sKr[CH][D128];       // chunk j's k rows [token][key]: P's and (gathered) K^T's source
     __shared__ __align__(16) TA sO[4][16][TR + 8];       // per output wave: [token][row] staging for the store
     __shared__ float sTM[4][2];                           // per chain wave: max |S0| of its part, max |v|
 
@@ -2096,7 +2096,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
         struct Ops {
             h8 k[4];        // k row 16 tb + lr, keys 32 kk + 8 lq .. +7
             h4 v[NVB];      // v at (tokens 16 tb + 4 lq + i, row 16 vb + lr)
-            h8 kt[2][2];    // K^T fragments: key tiles 2 wave + a, token steps ks
+            h8 kt[2][2];    // K^T fragments: key tiles 2 wave + a, token steps ks (from sKr)
             h8 th[2], tl[2];  // T (hi, lo): token 16 tb + lr, tokens 32 ks + 8 lq .. +7
             f4v kd, bt, rw;   // kd, beta and w of this lane's four D tokens 16 tb + 4 lq + i
             float gc;         // gamma_C
@@ -2118,14 +2118,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                 for (int i = 0; i < 4; ++i)
                     f.v[vb][i] = (half_t)to_f32(__builtin_bit_cast(TA, __builtin_amdgcn_raw_buffer_load_b16(
                                      r, (uint32_t)((16 * tb + 4 * lq + i) * tok_v + 2 * (16 * vb + lr)), 0, 0)));
-        };
-        const uint32_t offKt = (uint32_t)(2 * wave) * 2 * 1024 + l16;
-        auto fetchKt = [&](int jj, Ops &f) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(kts + ((size_t)(c0 + jj) * p.H + qh) * RecT::KT_SIZE, RecT::KT_SIZE);
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = ld_b128<h8>(r, offKt + (2 * a + ks) * 1024);
         };
         auto fetchT = [&](int jj, Ops &f) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(jj), RecT::SIZE);
@@ -2179,12 +2171,21 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                     *reinterpret_cast<h4 *>(&sS[0][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = hi;
                     *reinterpret_cast<h4 *>(&sS[1][16 * rt + lr][sw_key(lr, 16 * (2 * wave + a) + 4 * lq)]) = lo;
                 }
-            // the chunk's k rows for the output waves' P
-            if (mode == SEG_REAL) {
+            // the chunk's k rows: the output waves' P, and K^T for stage E
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<h8 *>(&sKr[16 * tb + lr][sw_key(lr, 32 * kk + lk)]) = cur.k[kk];
-            }
+            for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<h8 *>(&sKr[16 * tb + lr][sw_key(lr, 32 * kk + lk)]) = cur.k[kk];
             lds_barrier();  // 1
+            // K^T fragments (key 16 (2 wave + a) + lr, tokens 32 ks + 8 lq .. +7),
+            // gathered from the k rows now, consumed at stage E
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const int t = 32 * ks + 8 * lq + x;
+                        cur.kt[a][ks][x] = sKr[t][sw_key(t, 16 * (2 * wave + a) + lr)];
+                    }
             if constexpr (RET) {
                 // ---- B1: Y = K S^T at (tokens 16 tb + 4 lq + i, rows 16 vb + lr), then
                 // Z = um beta V - w Y as Z^T into the free D buffer
@@ -2283,7 +2284,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                         if constexpr (SEPL) Sc[a][rt] += lo4[a][rt];
             }
             fetchS(jn, cur);
-            fetchKt(jn, cur);
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -2293,7 +2293,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             if constexpr (RET) fetchT(cb, op);
             fetchV(cb, op);
             fetchS(cb, op);
-            fetchKt(cb, op);
         }
         for (int j = cb; j < ce; ++j) step(j, op);
         if (to) {
@@ -2549,8 +2548,8 @@ __global__ __launch_bounds__(256) void k_chunk_commit(const Params p, const int3
 
 // The per-head form has two variants.  With a single-pass scan over 128 or
 // more (request, head) pairs it takes the T form (k_chunk_prep<RULE, true>,
-// k_chunk_scan_t): records of 18 KB per (chunk, value head) instead of 81 KB
-// plus 16 KB of K^T per (chunk, q/k head), at
+// k_chunk_scan_t): records of 18 KB per (chunk, value head) and no K^T area,
+// instead of 81 KB plus 16 KB of K^T per (chunk, q/k head), at
 // the price of one more product on the scan's serial chain per chunk and P
 // formed by the output waves.  Measured on MI355X in one
 // session: the varlen workload (8 requests, 32 heads) 0.974 -> 0.924 ms; the
@@ -2562,7 +2561,7 @@ static bool t_form(bool per_key, int B, int HV, int nseg) { return !per_key && n
 // Workspace: chunk table (off[B + 1], the (B * HV) hand-over flags, the scan
 // order of the B requests) |
 // records of every (chunk, value head) (Rec<true>, Rec<false> or RecT) |
-// per-head form: K^T of every (chunk, q/k head) |
+// per-head W/U form: K^T of every (chunk, q/k head) |
 // segment states | staging for in-place final states (one 128 x 128 fp32
 // state per pair).  The chunk budget of gdr_chunk_plan.hpp sizes the
 // records; the table never assigns a chunk index at or past it.
@@ -2577,7 +2576,7 @@ static Layout layout(int64_t T, int B, int H, int HV, bool per_key, int nseg)
     const int64_t maxch = chunk_budget(T, B);
     const bool tf = t_form(per_key, B, HV, nseg);
     const size_t rec = per_key ? Rec<true>::SIZE : tf ? RecT::SIZE : Rec<false>::SIZE;
-    const size_t kq = per_key ? 0 : tf ? RecT::KT_SIZE : KQ::SIZE;
+    const size_t kq = per_key || tf ? 0 : KQ::SIZE;
     Layout l;
     l.kq = table_bytes(B, HV) + round256((size_t)maxch * HV * rec);
     l.seg = l.kq + round256((size_t)maxch * H * kq);
@@ -2603,7 +2602,7 @@ static void launch_scan(const Params &p, int32_t *off, const char *rec, const ch
     const int64_t blocks = (groups + per - 1) / per * per * NTILE * (sg.pass == 1 ? 2 : 1);
     if (blocks <= 0) return;
     if constexpr (TF)
-        hipLaunchKernelGGL((k_chunk_scan_t<TA, RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq, sg);
+        hipLaunchKernelGGL((k_chunk_scan_t<TA, RULE, NVB>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, sg);
     else
         hipLaunchKernelGGL((k_chunk_scan<TA, RULE, NVB, PK>), dim3((unsigned)blocks), dim3(512), 0, s, p, off, rec, kq,
                            sg);
