@@ -350,7 +350,7 @@ def main():
                          "known-size reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the engine has no multi-GPU path in this build "
+        print("bench.py measures one GPU: the engine has no multi-GPU path "
               "(requests and heads shard with no communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

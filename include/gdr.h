@@ -90,7 +90,7 @@ extern "C" {
 typedef enum {
     GDR_OK = 0,
     GDR_E_INVALID = 1,      /* bad shape, missing or unexpected tensor, bad enum */
-    GDR_E_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    GDR_E_UNSUPPORTED = 2,  /* valid request the library does not implement */
     GDR_E_ALIAS = 3,        /* overlapping input/output buffers */
     GDR_E_WORKSPACE = 4,    /* workspace missing or smaller than gdr_workspace_size */
     GDR_E_HIP = 5           /* a HIP runtime call failed (message in gdr_last_error) */
