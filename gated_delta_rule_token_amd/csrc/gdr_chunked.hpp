@@ -331,6 +331,90 @@ __device__ __forceinline__ void solve_unit_lower(float (*sA)[LA], int tid, float
     for (int i = 0; i < CH / 4; ++i) sA[4 * i + q][c] = x[i];
 }
 
+// The same T by blocks of 16 (row block i, column block j): wave i inverts
+// its unit lower diagonal block I + A_ii by forward substitution (four lanes
+// per column, as above, 16 rows), then the blocks below the diagonal follow
+// by their distance d = i - j from it, one level per barrier,
+//   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
+// on the fp32 matrix cores (16x16x4: fp32 products and sums; lane (g, r) of
+// an operand holds row r, k-index g of the left one and k-index g, column r
+// of the right one, and result rows 4 g .. 4 g + 3 of column r).  A is read
+// as the caller stores it (row t, column s at a_pos(s); only s < t is read);
+// wave i keeps its row block's A blocks in registers before it writes T over
+// them, and reads other row blocks only as T.  T ends up over A in natural
+// order with zeros above the diagonal, without a trailing barrier.  wgt[c] is
+// column c's weight: each lane watches its T entries and the entries times
+// their column's weight, the products the caller forms from them.
+template <int LA>
+__device__ __forceinline__ void solve_blocked(float (*sA)[LA], int tid, const float *wgt, SplitWatch &wt)
+{
+    const int i = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g4 = lane >> 4;  // operand lane (row / column r16, k-index g4)
+    const int c = lane >> 2, q = lane & 3;      // forward substitution: column c, terms s = q (mod 4)
+    // this row block's A_ik (k < i) in the left-operand layout
+    float ab[3][4];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ab[k][ks] = k < i ? sA[16 * i + r16][a_pos(16 * k + 4 * ks + g4)] : 0.f;
+    // T_ii: x[m] = T_ii[4 m + q][c]; row t's terms A_ii[t][4 m + q] lie at a_pos = 16 q + 4 i + m
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const f4v a = *reinterpret_cast<const f4v *>(&sA[16 * i + t][16 * q + 4 * i]);
+        float r = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) r = fmaf(a[m], x[m], r);  // zero past the diagonal (A) or not yet formed (x)
+        r += dpp_mov<0xB1>(r);  // the quad's four partial sums
+        r += dpp_mov<0x4E>(r);
+        const float xt = (t == c ? 1.f : 0.f) - r;
+        if ((t & 3) == q) x[t >> 2] = xt;
+    }
+    const float wd = wgt[16 * i + c];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        wt.note(x[m]);
+        wt.note(x[m] * wd);
+        sA[16 * i + 4 * m + q][16 * i + c] = x[m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j > i) sA[16 * i + 4 * m + q][16 * j + c] = 0.f;
+    }
+    lds_barrier();  // every T_ii is in place
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+        if (i >= d) {
+            const int j = i - d;
+            f4v acc = {0.f, 0.f, 0.f, 0.f};
+            // X = sum_k A_ik T_kj
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (k >= j && k < i) {  // (static k: the register array is not indexed at run time)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[k][ks], sA[16 * k + 4 * ks + g4][16 * j + r16], acc, 0, 0, 0);
+                }
+            }
+            // X through block (i, j), then T_ij = -T_ii X there
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sA[16 * i + 4 * g4 + r][16 * j + r16] = acc[r];
+            f4v tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                tij = __builtin_amdgcn_mfma_f32_16x16x4f32(-sA[16 * i + r16][16 * i + 4 * ks + g4],
+                                                           sA[16 * i + 4 * ks + g4][16 * j + r16], tij, 0, 0, 0);
+            const float wj = wgt[16 * j + r16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wt.note(tij[r]);
+                wt.note(tij[r] * wj);
+                sA[16 * i + 4 * g4 + r][16 * j + r16] = tij[r];
+            }
+        }
+        if (d < 3) lds_barrier();  // level d is in place
+    }
+}
+
 __device__ __forceinline__ int tile_exponent(float m)
 {
     if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;  // zero, or not finite
@@ -748,7 +832,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
         // exports it).
         {
             SplitWatch wt;
-            solve_unit_lower(sA, tid, sBeta[16 * wave + (lane >> 2)], wt);
+            solve_blocked(sA, tid, sBeta, wt);
             if constexpr (!TF) post(wt);
         }
         lds_barrier();  // T is complete
@@ -1366,7 +1450,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
             // the column times its weight (split beside T below) peaks where
             // |T| does: rounding is monotone
             SplitWatch wt;
-            solve_unit_lower(sA, tid, sWt[16 * wave + (lane >> 2)], wt);
+            solve_blocked(sA, tid, sWt, wt);
             post(wt);
         }
         lds_barrier();  // T is complete
