@@ -281,59 +281,19 @@ struct ScanWatch {
     __device__ __forceinline__ bool over() const { return !(big < SPLIT_LIMIT); }
 };
 
-// T = (I + A)^-1 of a chunk's strictly lower triangular 64 x 64 matrix A
-// (rows of LA floats) by forward substitution down the rows,
-//   T_tc = [t == c] - sum_{s<t} A_ts T_sc,
-// on the four waves of a 256-thread workgroup: wave w takes the columns
-// 16 w .. 16 w + 15 with four lanes each, lane q of a column the terms
-// s = q (mod 4) of every row, and a quad reduction completes the row.  The
-// caller stores A with each row permuted, entry s at a_pos(s) = 16 (s mod 4)
-// + s / 4, so that a lane reads its terms as 16-byte vectors; it must store
-// the diagonal 4 x 4 groups of A in full (zeros on and above the diagonal),
-// the only entries at or above the diagonal that the substitution reads.
-// T is written over A in natural order after a barrier (zeros above the
-// diagonal); each lane watches its column's entries and, scaled by the
-// column's weight `wc`, the products the caller forms from them.
+// The caller of solve_blocked stores A with each row permuted, entry s at
+// a_pos(s) = 16 (s mod 4) + s / 4, so that the diagonal blocks' forward
+// substitution reads its terms as 16-byte vectors; it must store the
+// diagonal 16 x 16 blocks in full (zeros on and above the diagonal).
 __device__ __forceinline__ int a_pos(int s) { return 16 * (s & 3) + (s >> 2); }
 
-template <int LA>
-__device__ __forceinline__ void solve_unit_lower(float (*sA)[LA], int tid, float wc, SplitWatch &wt)
-{
-    const int lane = tid & 63, c = 16 * (tid >> 6) + (lane >> 2), q = lane & 3;
-    float x[CH / 4];  // x[i] = T_{4 i + q, c}
-#pragma unroll
-    for (int i = 0; i < CH / 4; ++i) x[i] = 0.f;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-        // terms i < ceil(t / 4): s = 4 i + q < t, or s in t's group (A_ts = 0, x = 0 yet)
-        const int nt = (t + 3) >> 2;
-        float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < nt; j += 4) {
-            const f4v a = *reinterpret_cast<const f4v *>(&sA[t][16 * q + j]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (j + u < nt) {
-                    if (u & 1) r1 = fmaf(a[u], x[j + u], r1);
-                    else r0 = fmaf(a[u], x[j + u], r0);
-                }
-        }
-        float r = r0 + r1;
-        r += dpp_mov<0xB1>(r);  // the quad's four partial sums
-        r += dpp_mov<0x4E>(r);
-        const float xt = (t == c ? 1.f : 0.f) - r;
-        if ((t & 3) == q) x[t >> 2] = xt;
-        wt.note(xt);
-    }
-    wt.note(__uint_as_float(wt.big) * wc);
-    lds_barrier();  // every wave has read A
-#pragma unroll
-    for (int i = 0; i < CH / 4; ++i) sA[4 * i + q][c] = x[i];
-}
-
-// The same T by blocks of 16 (row block i, column block j): wave i inverts
-// its unit lower diagonal block I + A_ii by forward substitution (four lanes
-// per column, as above, 16 rows), then the blocks below the diagonal follow
+// T = (I + A)^-1 of a chunk's strictly lower triangular 64 x 64 matrix A
+// (rows of LA floats), by blocks of 16 (row block i, column block j), on the
+// four waves of a 256-thread workgroup.  Wave i inverts its unit lower
+// diagonal block I + A_ii by forward substitution down its 16 rows,
+//   T_tc = [t == c] - sum_{s<t} A_ts T_sc,
+// four lanes per column (lane q of column c the terms s = q (mod 4), a quad
+// reduction completing the row), then the blocks below the diagonal follow
 // by their distance d = i - j from it, one level per barrier,
 //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
 // on the fp32 matrix cores (16x16x4: fp32 products and sums; lane (g, r) of
