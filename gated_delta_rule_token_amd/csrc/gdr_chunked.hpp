@@ -2541,7 +2541,11 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
 // ------------------------------------------------------------------ segment starts
 // start_{p+1} = start_p M_p + c_p for the middle segments p = 1 .. nseg - 2,
 // in order; rows are independent, so one workgroup takes 16 rows of one
-// (request, head) and keeps them in LDS from one segment to the next.
+// (request, head) and keeps them in LDS from one segment to the next.  The
+// products run on the fp32 matrix cores (16x16x4: fp32 products and sums),
+// wave w forming the output column blocks 2 w and 2 w + 1: lane (g, r) gives
+// row r, k-index 4 ks + g of the rows and k-index 4 ks + g, column r of M at
+// step ks, and holds result rows 4 g .. 4 g + 3 of column r.
 __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const int32_t *off, const ScanSeg sg)
 {
     const int64_t bh = blockIdx.x >> 3;
@@ -2551,8 +2555,9 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const int32
     const float *src;
     float *dst;
     if (!state_ptrs(p, (int)(bh / p.HV), (int)(bh % p.HV), src, dst)) return;
-    __shared__ float sR[16][D128];
-    const int tid = threadIdx.x, c = tid & 127, r0 = (tid >> 7) * 8;
+    __shared__ float sR[16][D128 + 4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g4 = lane >> 4;
     constexpr size_t HEAD = (size_t)D128 * D128;
     float *xs = sg.xs + (size_t)bh * seg_slots(sg.nseg) * HEAD;
     const size_t rows = (size_t)(16 * rb) * D128;
@@ -2561,23 +2566,28 @@ __global__ __launch_bounds__(256) void k_seg_combine(const Params p, const int32
     for (int sp = 1; sp + 1 < sg.nseg; ++sp) {
         const float *M = xs + (size_t)seg_trans(sg.nseg, sp) * HEAD;
         const float *C = xs + (size_t)seg_carry(sg.nseg, sp) * HEAD + rows;
-        float acc[8];
+        f4v acc[2];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] = C[(size_t)(r0 + r) * D128 + c];
-        // unrolled so that many loads of M's rows (from L2) are in flight at once
-#pragma unroll 16
-        for (int j = 0; j < D128; ++j) {
-            const float m = M[(size_t)j * D128 + c];
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int r = 0; r < 8; ++r) acc[r] = fmaf(sR[r0 + r][j], m, acc[r]);
+            for (int r = 0; r < 4; ++r) acc[cb][r] = C[(size_t)(4 * g4 + r) * D128 + 16 * (2 * wave + cb) + r16];
+#pragma unroll 8
+        for (int ks = 0; ks < D128 / 4; ++ks) {
+            const float a = sR[r16][4 * ks + g4];
+            const float *mrow = M + (size_t)(4 * ks + g4) * D128 + 32 * wave + r16;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mrow[16 * cb], acc[cb], 0, 0, 0);
         }
-        __syncthreads();  // every thread has read the old rows
+        __syncthreads();  // every wave has read the old rows
         float *S = xs + (size_t)seg_start(sp + 1) * HEAD + rows;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            sR[r0 + r][c] = acc[r];
-            S[(size_t)(r0 + r) * D128 + c] = acc[r];
-        }
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g4 + r, col = 16 * (2 * wave + cb) + r16;
+                sR[row][col] = acc[cb][r];
+                S[(size_t)row * D128 + col] = acc[cb][r];
+            }
         __syncthreads();
     }
 }
