@@ -626,10 +626,11 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     // update rate.  The sums run in fp64: in a strongly decaying chunk two
     // prefix sums of hundreds of nats differ by a few late in the chunk, and
     // their fp32 roundings alone would put relative errors of 1e-5 .. 1e-4
-    // into the decay factors between them (kd, A, P).  G_t is kept as fp32
-    // (hi, lo), so that (hi_t - hi_s) + (lo_t - lo_s) -- the first difference
-    // exact whenever it is small against the sums -- recovers G_t - G_s.
-    float gend = 0.f;  // G_end - G_t of this thread's token t = tid < CH (kd below)
+    // into the decay factors between them (kd, A, P).  G_t is kept in log2
+    // units (scaled in fp64) as fp32 (hi, lo), so that (hi_t - hi_s) +
+    // (lo_t - lo_s) -- the first difference exact whenever it is small against
+    // the sums -- recovers G_t - G_s, and every factor is one v_exp_f32.
+    float gend = 0.f;  // G_end - G_t (log2 units) of this thread's token t = tid < CH (kd below)
     if (tid < CH) {
         const int t = tid;
         float gt = 0.f, bt = 0.f;
@@ -644,9 +645,10 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
             const double y = __shfl_up(g, o, CH);
             if (t >= o) g += y;
         }
+        g *= LOG2E_D;
         const double ge = __shfl(g, n - 1, CH);
         const float gh = (float)g;
-        sG[t] = gh;  // inclusive cumulative log decay inside the chunk
+        sG[t] = gh;  // inclusive cumulative log2 decay inside the chunk
         sGl[t] = (float)(g - (double)gh);
         gend = (float)(ge - g);
         sBeta[t] = bt;
@@ -703,15 +705,15 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
     if (tid < CH) {
         const int t = tid;
         const float gl = sG[n - 1];
-        sRw[t] = sBeta[t] * expf(sG[t]) * sIk[t];  // row scale of K in W's right-hand side
+        sRw[t] = sBeta[t] * ex2(sG[t]) * sIk[t];  // row scale of K in W's right-hand side
         float *sc = reinterpret_cast<float *>(rec + OSC);
-        sc[t] = t < n ? expf(gend) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
-        sc[CH + t] = scale * sIq[t] * expf(sG[t]);        // gq: read-out weight of the incoming state
-        if (t == 0) sc[2 * CH] = DEC ? expf(gl) : 1.f;    // gamma_C
+        sc[t] = t < n ? ex2(gend) * sIk[t] : 0.f;  // kd: key weight of token t in the state update
+        sc[CH + t] = scale * sIq[t] * ex2(sG[t]);        // gq: read-out weight of the incoming state
+        if (t == 0) sc[2 * CH] = DEC ? ex2(gl) : 1.f;    // gamma_C
         if constexpr (TF) {
             sc[SCT_BETA + t] = sBeta[t];  // zero past the request's end, like w
             sc[SCT_RW + t] = sRw[t];
-            const double g2 = ((double)sG[t] + (double)sGl[t]) * LOG2E_D;
+            const double g2 = (double)sG[t] + (double)sGl[t];
             sc[SCT_G + t] = (float)g2;
             sc[SCT_GL + t] = (float)(g2 - (double)(float)g2);
             sc[SCT_IK + t] = sIk[t];
@@ -747,7 +749,7 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + i;
-                const float dg = (s <= t) ? expf((sG[t] - sG[s]) + (sGl[t] - sGl[s])) : 0.f;
+                const float dg = (s <= t) ? ex2((sG[t] - sG[s]) + (sGl[t] - sGl[s])) : 0.f;
                 pv[i] = scale * sIq[t] * sIk[s] * dg * accq[sb][i];
                 av[i] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
             }
