@@ -308,7 +308,7 @@ __device__ __forceinline__ int a_pos(int s) { return 16 * (s & 3) + (s >> 2); }
 template <int LA>
 __device__ __forceinline__ void solve_blocked(float (*sA)[LA], int tid, const float *wgt, SplitWatch &wt)
 {
-    const int i = tid >> 6, lane = tid & 63;
+    const int i = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // (a scalar: branches on i stay scalar)
     const int r16 = lane & 15, g4 = lane >> 4;  // operand lane (row / column r16, k-index g4)
     const int c = lane >> 2, q = lane & 3;      // forward substitution: column c, terms s = q (mod 4)
     // this row block's A_ik (k < i) in the left-operand layout
@@ -749,7 +749,8 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + i;
-                const float dg = (s <= t) ? ex2((sG[t] - sG[s]) + (sGl[t] - sGl[s])) : 0.f;
+                const float e2 = ex2((sG[t] - sG[s]) + (sGl[t] - sGl[s]));  // (select, not branch, past the diagonal)
+                const float dg = s <= t ? e2 : 0.f;
                 pv[i] = scale * sIq[t] * sIk[s] * dg * accq[sb][i];
                 av[i] = (s < t) ? sBeta[t] * sIk[t] * sIk[s] * dg * acck[sb][i] : 0.f;
             }
