@@ -85,17 +85,20 @@ constexpr int D128 = 128;       // dk = dv
 // (the scan's output waves read the q rows from the activations themselves:
 // a row of 8 keys per lane is already their fragment layout)
 // Decay per key channel (PK = true): the per-token weights kd and gq become
-// per-element factors, so two operands carry fp32 values and get two planes:
+// per-element factors, so two operands carry fp32 values:
 //   KT  Kd^T (hi, lo),   block (mt * 2 + ks) * 2 + plane,  Kd = kn o exp(G_C - G)
-//   Q   Qg (hi, lo),     block (tb * 4 + kk) * 2 + plane,  Qg = scale qn o exp(G)
+//   Q   Qg fp16,         block tb * 4 + kk,                Qg = scale qn o exp(G)
 //   SC  fp32 gamma_C of each of the 128 key channels
+// Kd^T enters the state update and keeps (hi, lo) planes; Qg enters only the
+// outputs, which are stored in 16 bits, so one fp16 plane (round to nearest,
+// 2^-11 relative) adds an error of the order of that store's own rounding.
 template <bool PK>
 struct Rec {
     static constexpr uint32_t W = 0;
     static constexpr uint32_t KT = W + 32 * 1024;
     static constexpr uint32_t U = KT + (PK ? 32 : 0) * 1024;
     static constexpr uint32_t Q = U + 32 * 1024;
-    static constexpr uint32_t P = Q + (PK ? 32 : 0) * 1024;
+    static constexpr uint32_t P = Q + (PK ? 16 : 0) * 1024;
     static constexpr uint32_t SC = P + 16 * 1024;
     static constexpr uint32_t SIZE = SC + 1024;
 };
@@ -1188,10 +1191,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
         for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * (PKG ? ex2(sG[t][key + x]) : sFq[t]);
         h8 hi, lo;
         wg.note(x8);
-        split8(x8, hi, lo);
-        char *dst = rec + RC::Q + ((uint32_t)(blk * 2) * 64 + fl) * 16;
-        *reinterpret_cast<h8 *>(dst) = hi;
-        *reinterpret_cast<h8 *>(dst + 1024) = lo;
+        split8(x8, hi, lo);  // hi: x8 rounded to nearest fp16
+        *reinterpret_cast<h8 *>(rec + RC::Q + ((uint32_t)blk * 64 + fl) * 16) = hi;
     }
     post(wg);
     if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
@@ -1853,15 +1854,15 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
         lds_barrier();  // 0: the chain waves have posted the tile's max |S0|
         const float down = ldexpf(1.f, -scale_exp());  // o = (scaled o) / 2^e
         struct Ops {
-            h8 q[4][NPL];     // q rows (per key: Qg hi, lo) of token block tb, four k-steps of 32
+            h8 q[4][1];       // q rows (per key: Qg, one fp16 plane) of token block tb, four k-steps of 32
             h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
             float gq;         // per head: gq of this lane's token
         };
-        // per key: Qg (hi, lo) from the record; per head: q rows from the
+        // per key: Qg from the record; per head: q rows from the
         // activations (row 16 tb + lr, keys 32 kk + 8 lq .. +7), converted to fp16
         // as they load (the prologue has handed pairs with values fp16 cannot
         // hold to the recurrent kernel); rows past the request's end read zero
-        const uint32_t offQ = PK ? RC::Q + (uint32_t)tb * 4 * NPL * 1024 + l16
+        const uint32_t offQ = PK ? RC::Q + (uint32_t)tb * 4 * 1024 + l16
                                  : (uint32_t)((16 * tb + lr) * p.H * D128 * 2 + 2 * lk);
         // o byte offset of this lane's token (16 tb + lr) and rows 4 lq .. +3 inside a chunk
         const int tok_bytes = HV * D128 * 2;
@@ -1887,9 +1888,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
             if constexpr (PK) {
                 const __amdgpu_buffer_rsrc_t r = kq_rsrc(jj);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl) f.q[kk][pl] = ld_b128<h8>(r, offQ + (kk * NPL + pl) * 1024);
+                for (int kk = 0; kk < 4; ++kk) f.q[kk][0] = ld_b128<h8>(r, offQ + kk * 1024);
             } else {
                 const int64_t t0 = rs + (int64_t)jj * CH;
                 const int n = (int)((re - t0) < CH ? (re - t0) : CH);
@@ -1946,7 +1945,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
                     const h8 slo = ld_h8(&sS[bf][1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
                     acc[vb] = mfma16(shi, cur.q[kk][0], acc[vb]);
                     acl[vb] = mfma16(slo, cur.q[kk][0], acl[vb]);
-                    if constexpr (PK) acl[vb] = mfma16(shi, cur.q[kk][NPL - 1], acl[vb]);
                 }
             fetchQ(jn, cur);  // pinned like the chain's loads
             asm volatile("" ::: "memory");
