@@ -77,7 +77,8 @@ constexpr int D128 = 128;       // dk = dv
 // bytes (eight whole cache lines).  Per-head decay (PK = false):
 //   W   W (hi, lo) fp16, block (tb * 4 + kk) * 2 + plane: token 16 tb + lr, keys 32 kk + 8 lq .. +7
 //   U   U fp32,          block tb * 8 + rt:              tokens 16 tb + 4 lq .. +3, row 16 rt + lr
-//   P   P (hi, lo) fp16, block (tb * 2 + ks) * 2 + plane: token 16 tb + lr, tokens 32 ks + 8 lq .. +7
+//   P   P fp16,          block tb * 2 + ks:              token 16 tb + lr, tokens 32 ks + 8 lq .. +7
+//       (P enters only the 16-bit outputs: one plane, rounded to nearest)
 //   SC  fp32 scalars: kd[64], gq[64], gamma_C
 // and, once per (chunk, q/k head) -- the same for every value head of the
 // group, written by its first value head (struct KQ):
@@ -99,7 +100,7 @@ struct Rec {
     static constexpr uint32_t U = KT + (PK ? 32 : 0) * 1024;
     static constexpr uint32_t Q = U + 32 * 1024;
     static constexpr uint32_t P = Q + (PK ? 16 : 0) * 1024;
-    static constexpr uint32_t SC = P + 16 * 1024;
+    static constexpr uint32_t SC = P + 8 * 1024;
     static constexpr uint32_t SIZE = SC + 1024;
 };
 constexpr uint32_t R_W = Rec<false>::W, R_U = Rec<false>::U, R_P = Rec<false>::P, R_SC = Rec<false>::SC,
@@ -221,6 +222,14 @@ __device__ __forceinline__ void split4(f4v x, h4 &hi, h4 &lo)
     split2(x[2], x[3], h1, l1);
     hi = __builtin_bit_cast(h4, u2v{h0, h1});
     lo = __builtin_bit_cast(h4, u2v{l0, l1});
+}
+
+// One fp16 plane: each value rounded to nearest (the hi part of a split),
+// for operands that enter only the 16-bit outputs.
+__device__ __forceinline__ h4 round_h4(f4v x) { return __builtin_convertvector(x, h4); }
+__device__ __forceinline__ h8 round_h8(const float (&x)[8])
+{
+    return h8{(half_t)x[0], (half_t)x[1], (half_t)x[2], (half_t)x[3], (half_t)x[4], (half_t)x[5], (half_t)x[6], (half_t)x[7]};
 }
 
 // Column index of a swizzled LDS row of fp16: the 16-byte chunk (8 values)
@@ -761,12 +770,9 @@ __global__ __launch_bounds__(256, TF ? 4 : 3) void k_chunk_prep(const Params p, 
             // fragments of token blocks 0, 1 against tokens 32 .. 63 are all zero
             // and are not stored (the scan reads zero past the record instead)
             if (!TF && (tb >= 2 || sb < 2)) {
-                h4 hi, lo;
                 wp.note(pv);
-                split4(pv, hi, lo);
-                const uint32_t po = R_P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
-                *reinterpret_cast<h4 *>(rec + po) = hi;
-                *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+                const uint32_t po = R_P + ((uint32_t)(tb * 2 + (s0 >> 5)) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+                *reinterpret_cast<h4 *>(rec + po) = round_h4(pv);  // P enters only the outputs
             }
             if constexpr (RET) {
 #pragma unroll
@@ -1189,10 +1195,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
         float x8[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) x8[x] = scale * sIq[t] * (float)qq[x] * (PKG ? ex2(sG[t][key + x]) : sFq[t]);
-        h8 hi, lo;
         wg.note(x8);
-        split8(x8, hi, lo);  // hi: x8 rounded to nearest fp16
-        *reinterpret_cast<h8 *>(rec + RC::Q + ((uint32_t)blk * 64 + fl) * 16) = hi;
+        *reinterpret_cast<h8 *>(rec + RC::Q + ((uint32_t)blk * 64 + fl) * 16) = round_h8(x8);
     }
     post(wg);
     if (tid < D128) reinterpret_cast<float *>(rec + RC::SC)[tid] = ex2(sG[CH - 1][tid]);
@@ -1365,12 +1369,9 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
                 pv[i] = s <= t ? pt * sIk[s] * resP[slot][i] : 0.f;
                 av[i] = s < t ? at * sIk[s] * resA[slot][i] : 0.f;
             }
-            h4 hi, lo;
             wp.note(pv);
-            split4(pv, hi, lo);
-            const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
-            *reinterpret_cast<h4 *>(rec + po) = hi;
-            *reinterpret_cast<h4 *>(rec + po + 1024) = lo;
+            const uint32_t po = RC::P + ((uint32_t)(tb * 2 + (s0 >> 5)) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+            *reinterpret_cast<h4 *>(rec + po) = round_h4(pv);  // P enters only the outputs
             if constexpr (RET) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sA[t][a_pos(s0 + i)] = av[i];
@@ -1385,9 +1386,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep_pk(const Params p, int32_
         // all-zero fragments of token blocks 0, 1 against tokens 32 .. 63 are
         // read as zero past the record's end
         const int tb = 2 * wave, sb = 2 * wave + 1, s0 = 16 * sb + 4 * lq;
-        const uint32_t po = RC::P + ((uint32_t)((tb * 2 + (s0 >> 5)) * 2) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
+        const uint32_t po = RC::P + ((uint32_t)(tb * 2 + (s0 >> 5)) * 64 + ((s0 & 31) >> 3) * 16 + lr) * 16 + ((s0 & 7) >> 2) * 8;
         *reinterpret_cast<h4 *>(rec + po) = h4{};
-        *reinterpret_cast<h4 *>(rec + po + 1024) = h4{};
     }
     lds_barrier();
 
@@ -1855,7 +1855,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
         const float down = ldexpf(1.f, -scale_exp());  // o = (scaled o) / 2^e
         struct Ops {
             h8 q[4][1];       // q rows (per key: Qg, one fp16 plane) of token block tb, four k-steps of 32
-            h8 ph[2], pl[2];  // P (hi, lo) rows of token block tb, two token steps of 32
+            h8 ph[2];         // P rows (one fp16 plane) of token block tb, two token steps of 32
             float gq;         // per head: gq of this lane's token
         };
         // per key: Qg from the record; per head: q rows from the
@@ -1878,10 +1878,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
         const bool st_live = lane / LPT < TPS;
         const int st_tok = st_live ? lane / LPT : TPS - 1, st_q = lane % LPT;
         const uint32_t offO = st_live ? (uint32_t)((16 * tb + st_tok) * tok_bytes + 16 * st_q) : 0x7FFFFFF0u;
-        const uint32_t offP = RC::P + (uint32_t)tb * 4 * 1024 + l16;
+        const uint32_t offP = RC::P + (uint32_t)tb * 2 * 1024 + l16;
         // token blocks 0, 1 against tokens 32 .. 63: all zero, not stored; an offset
         // past the record makes the buffer load return zero
-        const uint32_t offP1 = tb < 2 ? 0x7FFFF000u : offP + 2048;
+        const uint32_t offP1 = tb < 2 ? 0x7FFFF000u : offP + 1024;
         const uint32_t offG = RC::SC + (uint32_t)(CH + 16 * tb + lr) * 4;
         // one operand set, each part reloaded for chunk jj right after its last use
         auto fetchQ = [&](int jj, Ops &f) {
@@ -1909,7 +1909,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 f.ph[ks] = ld_b128<h8>(r, ks ? offP1 : offP);
-                f.pl[ks] = ld_b128<h8>(r, (ks ? offP1 : offP) + 1024);
             }
         };
         // Store the output tile of chunk jo, staged in sO, as one 16-byte write per
@@ -1959,7 +1958,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
             }
             fetchG(jn, cur);
             {
-                f4v p3[NVB] = {};  // the two lo products in their own chain
+                f4v p3[NVB] = {};  // the lo product in its own chain
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1968,7 +1967,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const Params p, int32_t *off
                         const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
                         acc[vb] = mfma16(dhi, cur.ph[ks], acc[vb]);
                         p3[vb] = mfma16(dlo, cur.ph[ks], p3[vb]);
-                        p3[vb] = mfma16(dhi, cur.pl[ks], p3[vb]);
                     }
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
@@ -2464,10 +2462,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             // through an asm the compiler keeps after it (hoisted above it, they
             // made these waves late for it)
             asm volatile("" : "+v"(cur.pg), "+v"(cur.pgl));
-            h8 ph[2], pl[2];
+            h8 ph[2];  // P enters only the 16-bit outputs: one fp16 plane
             {
                 const int t = 16 * tb + lr;
-                h4 hh[4], hl[4];
+                h4 hh[4];
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb) {
                     f4v pv;
@@ -2478,13 +2476,10 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                         pv[i] = sx <= t ? cur.pq * cur.sk[sb][i] * ex2(d2) * c4[sb][i] : 0.f;
                     }
                     pw.note(pv);
-                    split4(pv, hh[sb], hl[sb]);
+                    hh[sb] = round_h4(pv);
                 }
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    ph[ks] = __builtin_shufflevector(hh[2 * ks], hh[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    pl[ks] = __builtin_shufflevector(hl[2 * ks], hl[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-                }
+                for (int ks = 0; ks < 2; ++ks) ph[ks] = __builtin_shufflevector(hh[2 * ks], hh[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
             }
             fetchQ(jn, cur);
             asm volatile("" ::: "memory");
@@ -2505,7 +2500,6 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
                         const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
                         acc[vb] = mfma16(dhi, ph[ks], acc[vb]);
                         p3[vb] = mfma16(dlo, ph[ks], p3[vb]);
-                        p3[vb] = mfma16(dhi, pl[ks], p3[vb]);
                     }
                 }
 #pragma unroll
