@@ -2426,17 +2426,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             lds_barrier();  // 1
             store_out(j - 1);
             // ---- O1: O^T = S Q^T at (rows 16 vb + 4 lq + i, token 16 tb + lr)
-            f4v acc[NVB], acl[NVB];
+            // (the state's hi plane only: O1 enters only the 16-bit outputs; the
+            // W/U scan keeps both planes, where dropping the lo product measured
+            // slower)
+            f4v acc[NVB];
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) acc[vb] = acl[vb] = f4v{0.f, 0.f, 0.f, 0.f};
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int vb = 0; vb < NVB; ++vb) {
                     const h8 shi = ld_h8(&sS[0][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
-                    const h8 slo = ld_h8(&sS[1][16 * vb + lr][sw_key(lr, 32 * kk + lk)]);
                     acc[vb] = mfma16(shi, cur.q[kk], acc[vb]);
-                    acl[vb] = mfma16(slo, cur.q[kk], acl[vb]);
                 }
             // ---- P_ts = scale / |q_t| / |k_s| exp(G_t - G_s) q_t . k_s (s <= t) from
             // the k rows the chain parked with the state tile and this wave's q
@@ -2487,7 +2488,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
             lds_barrier();  // 2
             // ---- O2: O^T = gq O^T + D^T P^T
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) acc[vb] = cur.gq * (acc[vb] + acl[vb]);
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = cur.gq * acc[vb];
             fetchG(jn, cur);
             {
                 f4v p3[NVB] = {};
