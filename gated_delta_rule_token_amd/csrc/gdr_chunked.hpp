@@ -2490,21 +2490,16 @@ __global__ __launch_bounds__(512) void k_chunk_scan_t(const Params p, int32_t *o
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) acc[vb] = cur.gq * acc[vb];
             fetchG(jn, cur);
-            {
-                f4v p3[NVB] = {};
+            // (the delta's hi plane only: this product enters only the 16-bit
+            // outputs; the chain's state update keeps both planes)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks == 1 && tb < 2) break;  // P is zero there (tokens 32 .. 63 follow t)
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 1 && tb < 2) break;  // P is zero there (tokens 32 .. 63 follow t)
 #pragma unroll
-                    for (int vb = 0; vb < NVB; ++vb) {
-                        const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
-                        const h8 dlo = ld_h8(&sDt[bf][1][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
-                        acc[vb] = mfma16(dhi, ph[ks], acc[vb]);
-                        p3[vb] = mfma16(dlo, ph[ks], p3[vb]);
-                    }
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const h8 dhi = ld_h8(&sDt[bf][0][16 * vb + lr][sw_tok(lr, 32 * ks + lk)]);
+                    acc[vb] = mfma16(dhi, ph[ks], acc[vb]);
                 }
-#pragma unroll
-                for (int vb = 0; vb < NVB; ++vb) acc[vb] += p3[vb];
             }
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
